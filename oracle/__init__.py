@@ -1,0 +1,216 @@
+"""CPU oracle for the INT4 weight-only decode GEMV (test infrastructure only).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  It loads ``liboracle_w4.so``, built from
+``w4_oracle.c`` with gcc, and shares no code with the HIP library.
+
+Definitions (restated from the pages: "How To Build Your Own LLM Runtime From
+Scratch", aitrending.vip, "Technical Details" bullet 1 -- INT4 weights
+dequantized at run time; noticiai.com.br, "As tres licoes", lesson 3 -- the
+activations stay floating point; zero point 8 and one fp16 scale per group of G
+inputs per row are the workload definition's format, the pages being silent):
+
+    w[n, k] = (q[n, k] - 8) * s[n, k // G]
+    y[n]    = sum_k w[n, k] * x[k]          (fp64, exact products)
+    A[n]    = sum_k |w[n, k] * x[k]|
+    h[j]    = silu(y[j]) * y[I + j],  silu(t) = t / (1 + exp(-t))
+    argmax  = lowest index of max y
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "w4_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle_w4.so")
+
+
+def build(src: str = _SRC, out: str = _LIB) -> str:
+    """Compile the oracle with gcc (plain -O2, no fast-math)."""
+    tmp = out + ".tmp"
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-Wall", "-Wextra",
+                           "-o", tmp, src, "-lm"])
+    os.replace(tmp, out)
+    return out
+
+
+class Oracle:
+    """ctypes view of one build of the oracle library (the default build, or a
+    mutated copy compiled by the self-tests)."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        p = ctypes.c_void_p
+        i64 = ctypes.c_int64
+        i32 = ctypes.c_int32
+        lib.oracle_half_to_double.restype = ctypes.c_double
+        lib.oracle_half_to_double.argtypes = [ctypes.c_uint16]
+        lib.oracle_packed_weight_bytes.restype = i64
+        lib.oracle_packed_weight_bytes.argtypes = [i64, i64, i32]
+        lib.oracle_packed_scale_bytes.restype = i64
+        lib.oracle_packed_scale_bytes.argtypes = [i64, i64, i32, i32]
+        lib.oracle_pack.restype = ctypes.c_int
+        lib.oracle_pack.argtypes = [p, p, i64, i64, i32, i32, p, p]
+        lib.oracle_unpack.restype = ctypes.c_int
+        lib.oracle_unpack.argtypes = [p, p, i64, i64, i32, i32, p, p]
+        lib.oracle_gemv_rows.restype = None
+        lib.oracle_gemv_rows.argtypes = [p, p, p, i64, i64, i32, p, i64, p, p]
+        lib.oracle_gemv.restype = None
+        lib.oracle_gemv.argtypes = [p, p, p, i64, i64, i32, p, p]
+        lib.oracle_gemv_packed_rows.restype = None
+        lib.oracle_gemv_packed_rows.argtypes = [p, p, p, i64, i64, i32, i32, p, i64, p, p]
+        lib.oracle_silu.restype = ctypes.c_double
+        lib.oracle_silu.argtypes = [ctypes.c_double]
+        lib.oracle_silu_gate.restype = None
+        lib.oracle_silu_gate.argtypes = [p, i64, p]
+        lib.oracle_argmax.restype = i64
+        lib.oracle_argmax.argtypes = [p, i64]
+        self.lib = lib
+        self.path = path
+
+    def half_to_double(self, bits: int) -> float:
+        return self.lib.oracle_half_to_double(int(bits) & 0xFFFF)
+
+    def packed_sizes(self, n: int, k: int, group: int, gateup: bool = False) -> tuple[int, int]:
+        return (int(self.lib.oracle_packed_weight_bytes(n, k, int(gateup))),
+                int(self.lib.oracle_packed_scale_bytes(n, k, group, int(gateup))))
+
+    def pack(self, q: np.ndarray, s_bits: np.ndarray, group: int, gateup: bool = False):
+        """Logical q uint8 [n, k], s fp16 bits uint16 [n, k/group] -> (pw, ps) uint8."""
+        q = np.ascontiguousarray(q, dtype=np.uint8)
+        s_bits = np.ascontiguousarray(s_bits, dtype=np.uint16)
+        n, k = q.shape
+        assert s_bits.shape == (n, k // group)
+        wb, sb = self.packed_sizes(n, k, group, gateup)
+        pw = np.empty(wb, np.uint8)
+        ps = np.empty(sb, np.uint8)
+        rc = self.lib.oracle_pack(_ptr(q), _ptr(s_bits), n, k, group, int(gateup), _ptr(pw), _ptr(ps))
+        if rc != 0:
+            raise ValueError("oracle_pack: shape not representable")
+        return pw, ps
+
+    def unpack(self, pw: np.ndarray, ps: np.ndarray, n: int, k: int, group: int,
+               gateup: bool = False):
+        """Packed buffers -> logical (q uint8 [n, k], s bits uint16 [n, k/group])."""
+        pw = np.ascontiguousarray(pw, dtype=np.uint8)
+        ps = np.ascontiguousarray(ps, dtype=np.uint8)
+        wb, sb = self.packed_sizes(n, k, group, gateup)
+        if pw.size < wb or ps.size < sb:
+            raise ValueError("oracle.unpack: packed buffers too small")
+        q = np.empty((n, k), np.uint8)
+        s = np.empty((n, k // group), np.uint16)
+        rc = self.lib.oracle_unpack(_ptr(pw), _ptr(ps), n, k, group, int(gateup), _ptr(q), _ptr(s))
+        if rc != 0:
+            raise ValueError("oracle_unpack: shape not representable")
+        return q, s
+
+    def gemv(self, q: np.ndarray, s_bits: np.ndarray, x_bits: np.ndarray, group: int, rows=None):
+        """(y, A) in float64 for all rows, or for the listed rows."""
+        q = np.ascontiguousarray(q, dtype=np.uint8)
+        s_bits = np.ascontiguousarray(s_bits, dtype=np.uint16)
+        x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+        n, k = q.shape
+        assert s_bits.shape == (n, k // group) and x_bits.shape == (k,)
+        if rows is None:
+            y = np.empty(n, np.float64)
+            a = np.empty(n, np.float64)
+            self.lib.oracle_gemv(_ptr(q), _ptr(s_bits), _ptr(x_bits), n, k, group, _ptr(y), _ptr(a))
+        else:
+            rows = np.ascontiguousarray(rows, dtype=np.int64)
+            assert rows.size == 0 or (rows.min() >= 0 and rows.max() < n)
+            y = np.empty(rows.size, np.float64)
+            a = np.empty(rows.size, np.float64)
+            self.lib.oracle_gemv_rows(_ptr(q), _ptr(s_bits), _ptr(x_bits), n, k, group,
+                                      _ptr(rows), rows.size, _ptr(y), _ptr(a))
+        return y, a
+
+    def gemv_packed(self, pw: np.ndarray, ps: np.ndarray, x_bits: np.ndarray, n: int, k: int,
+                    group: int, gateup: bool = False, rows=None):
+        """(y, A) for the listed rows (default: all), reading the packed buffers."""
+        pw = np.ascontiguousarray(pw, dtype=np.uint8)
+        ps = np.ascontiguousarray(ps, dtype=np.uint8)
+        x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+        wb, sb = self.packed_sizes(n, k, group, gateup)
+        assert pw.size >= wb and ps.size >= sb and x_bits.shape == (k,)
+        if rows is None:
+            rows = np.arange(n, dtype=np.int64)
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        assert rows.size == 0 or (rows.min() >= 0 and rows.max() < n)
+        y = np.empty(rows.size, np.float64)
+        a = np.empty(rows.size, np.float64)
+        self.lib.oracle_gemv_packed_rows(_ptr(pw), _ptr(ps), _ptr(x_bits), n, k, group,
+                                         int(gateup), _ptr(rows), rows.size, _ptr(y), _ptr(a))
+        return y, a
+
+    def silu(self, t: float) -> float:
+        return self.lib.oracle_silu(float(t))
+
+    def silu_gate(self, y: np.ndarray) -> np.ndarray:
+        y = np.ascontiguousarray(y, dtype=np.float64)
+        assert y.size % 2 == 0
+        half = y.size // 2
+        h = np.empty(half, np.float64)
+        self.lib.oracle_silu_gate(_ptr(y), half, _ptr(h))
+        return h
+
+    def argmax(self, y: np.ndarray) -> int:
+        y = np.ascontiguousarray(y, dtype=np.float64)
+        return int(self.lib.oracle_argmax(_ptr(y), y.size))
+
+
+def _ptr(a: np.ndarray) -> int:
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data
+
+
+_default: Oracle | None = None
+
+
+def default() -> Oracle:
+    """The oracle built from w4_oracle.c (compiled on first use if absent)."""
+    global _default
+    if _default is None:
+        if not os.path.exists(_LIB):
+            build()
+        _default = Oracle(_LIB)
+    return _default
+
+
+def half_to_double(bits):
+    return default().half_to_double(bits)
+
+
+def packed_sizes(n, k, group, gateup=False):
+    return default().packed_sizes(n, k, group, gateup)
+
+
+def pack(q, s_bits, group, gateup=False):
+    return default().pack(q, s_bits, group, gateup)
+
+
+def unpack(pw, ps, n, k, group, gateup=False):
+    return default().unpack(pw, ps, n, k, group, gateup)
+
+
+def gemv(q, s_bits, x_bits, group, rows=None):
+    return default().gemv(q, s_bits, x_bits, group, rows)
+
+
+def gemv_packed(pw, ps, x_bits, n, k, group, gateup=False, rows=None):
+    return default().gemv_packed(pw, ps, x_bits, n, k, group, gateup, rows)
+
+
+def silu(t):
+    return default().silu(t)
+
+
+def silu_gate(y):
+    return default().silu_gate(y)
+
+
+def argmax(y):
+    return default().argmax(y)

@@ -1,0 +1,109 @@
+"""Seeded synthetic inputs for the INT4 weight-only GEMV (shared by tests,
+the oracle checks and the benchmark).
+
+This module only draws random numbers; it holds none of the method's
+arithmetic.  Every draw comes from numpy's Philox counter-based generator keyed
+by the seed, in a fixed order: nibbles, then scales, then activations.
+
+Recipe (the pages give the model dimensions -- "How To Build Your Own LLM
+Runtime From Scratch", aitrending.vip, section 技术解析, first bullet: 28 layers,
+hidden 3584, MLP width 18944, vocabulary 152064 -- but no weights and no value
+distributions; the distributions below are the workload definition's):
+
+  * q  ~ uniform on {0..15}, i.i.d. per weight (zero point 8 is applied by the
+    method, not here);
+  * s  ~ uniform on [s_lo, s_hi] drawn in float32, rounded to fp16;
+  * x  ~ N(0, 1) drawn in float32, rounded to fp16.
+
+Trained Qwen2.5-Coder-7B weights are not available and are not needed: the
+GEMV has no data-dependent control flow, so uniform nibbles time the same as
+real ones and exercise every nibble value.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+HIDDEN = 3584
+MLP = 18944
+VOCAB = 152064
+LAYERS = 28
+QKV = 4608
+GROUP = 128
+
+
+def _rng(seed: int) -> np.random.Generator:
+    return np.random.Generator(np.random.Philox(key=int(seed)))
+
+
+def _nibbles(rng: np.random.Generator, count: int) -> np.ndarray:
+    """`count` i.i.d. uniform values in {0..15} (one per byte)."""
+    words = (count + 7) // 8
+    b = rng.bit_generator.random_raw(words).view(np.uint8)[:count]
+    np.bitwise_and(b, 15, out=b)
+    return b
+
+
+def _scales(rng: np.random.Generator, count: int, lo: float, hi: float) -> np.ndarray:
+    u = rng.random(count, dtype=np.float32)
+    return (u * np.float32(hi - lo) + np.float32(lo)).astype(np.float16).view(np.uint16)
+
+
+def _acts(rng: np.random.Generator, count: int) -> np.ndarray:
+    return rng.standard_normal(count, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def logical(seed: int, n: int, k: int, group: int, s_lo: float = 0.001, s_hi: float = 0.02):
+    """Logical inputs: q uint8 [n, k], s fp16 bits uint16 [n, k/group], x fp16 bits [k]."""
+    rng = _rng(seed)
+    q = _nibbles(rng, n * k).reshape(n, k)
+    s = _scales(rng, n * (k // group), s_lo, s_hi).reshape(n, k // group)
+    x = _acts(rng, k)
+    return q, s, x
+
+
+def packed_random(seed: int, weight_bytes: int, scale_count: int, k: int,
+                  s_lo: float = 0.001, s_hi: float = 0.02):
+    """Inputs drawn directly in packed form, for shapes without padding slots:
+    uniform random weight bytes (two i.i.d. uniform nibbles each), scale_count
+    fp16 scales, and x.  Returns (pw uint8 [weight_bytes], ps uint8
+    [2*scale_count], x fp16 bits [k])."""
+    rng = _rng(seed)
+    pw = rng.bit_generator.random_raw((weight_bytes + 7) // 8).view(np.uint8)[:weight_bytes]
+    ps = _scales(rng, scale_count, s_lo, s_hi).view(np.uint8)
+    x = _acts(rng, k)
+    return np.ascontiguousarray(pw), ps, x
+
+
+@dataclass(frozen=True)
+class Proj:
+    """One projection of the decode-step linear sweep."""
+    name: str
+    kind: str          # "plain" | "gateup" | "lmhead"
+    n: int             # output rows (gate/up: 2 * MLP width)
+    k: int
+    group: int
+    seed: int
+
+
+# Per-projection seeds: layer l, projection p in {0 qkv, 1 o, 2 gate/up, 3 down}
+# uses 1000 + 10*l + p; lm_head uses 1280.
+CONFIG_TINY = dict(name="tiny", kind="plain", n=512, k=256, group=64, seed=0, s_lo=0.005, s_hi=0.02)
+CONFIG_DOWN = dict(name="down", kind="plain", n=HIDDEN, k=MLP, group=GROUP, seed=1, s_lo=0.001, s_hi=0.02)
+CONFIG_GATEUP = dict(name="gateup", kind="gateup", n=2 * MLP, k=HIDDEN, group=GROUP, seed=2,
+                     s_lo=0.001, s_hi=0.02)
+CONFIG_LMHEAD = dict(name="lmhead", kind="lmhead", n=VOCAB, k=HIDDEN, group=GROUP, seed=3,
+                     s_lo=0.001, s_hi=0.02)
+
+
+def sweep_projections(layers: int = LAYERS) -> list[Proj]:
+    """The 28-layer decode-step sweep in decode order, then lm_head."""
+    out = []
+    for l in range(layers):
+        out.append(Proj(f"L{l}.qkv", "plain", QKV, HIDDEN, GROUP, 1000 + 10 * l + 0))
+        out.append(Proj(f"L{l}.o", "plain", HIDDEN, HIDDEN, GROUP, 1000 + 10 * l + 1))
+        out.append(Proj(f"L{l}.gateup", "gateup", 2 * MLP, HIDDEN, GROUP, 1000 + 10 * l + 2))
+        out.append(Proj(f"L{l}.down", "plain", HIDDEN, MLP, GROUP, 1000 + 10 * l + 3))
+    out.append(Proj("lm_head", "lmhead", VOCAB, HIDDEN, GROUP, 1280))
+    return out

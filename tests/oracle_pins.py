@@ -1,0 +1,256 @@
+"""Pins that tie the CPU oracle to facts outside itself.
+
+Each pin takes an ``oracle.Oracle`` and raises AssertionError when the oracle
+disagrees with something the pages, the mathematics or an independent library
+routine fixes:
+
+  * the hand-derived packing and GEMV example in tests/golden/ (bytes and
+    products worked out by hand from the layout rules);
+  * IEEE binary16 decoding checked against numpy's float16 for every pattern;
+  * the plain GEMV checked against numpy's float64 matrix product of the
+    dequantized matrix (a library routine, independent of the C loops);
+  * closed forms (zero point, constant nibbles, one-hot activations);
+  * exact invariants (power-of-two scaling, A >= |y|);
+  * silu against scipy's logistic function, argmax against numpy.argmax.
+
+The same pins run against deliberately mutated copies of the oracle
+(test_oracle_mutants.py) to show that each plausible mistake trips one.
+"""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+import scipy.special
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "pack_2x64_g32.txt")
+
+
+def load_golden(path: str = GOLDEN) -> dict:
+    out: dict = {}
+    with open(path) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, *vals = line.split()
+            if key in ("n", "k", "group"):
+                out[key] = int(vals[0])
+            elif key.endswith("_pw") or key.endswith("_ps"):
+                out.setdefault(key, []).extend(int(v, 16) for v in vals)
+            else:
+                out[key] = [float(v) for v in vals]
+    for key in list(out):
+        if key.endswith("_pw") or key.endswith("_ps"):
+            out[key] = np.array(out[key], np.uint8)
+    return out
+
+
+def golden_logical():
+    """The golden matrix as described in words in the fixture header."""
+    k = 64
+    kk = np.arange(k)
+    q = np.stack([kk % 16, 15 - (kk % 16)]).astype(np.uint8)
+    s = np.array([[0x3C00, 0x4000], [0x3800, 0xBC00]], np.uint16)
+    return q, s
+
+
+def _h(v) -> np.ndarray:
+    """float values -> fp16 bit patterns (numpy's conversion)."""
+    return np.asarray(v, np.float16).view(np.uint16)
+
+
+def _dequant_numpy(q, s_bits, group):
+    s = s_bits.view(np.float16).astype(np.float64)
+    return (q.astype(np.float64) - 8.0) * np.repeat(s, group, axis=1)
+
+
+# --------------------------------------------------------------------------- pins
+
+
+def pin_half_decode_all(orc):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = np.array([orc.half_to_double(int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+def pin_golden_pack(orc):
+    g = load_golden()
+    q, s = golden_logical()
+    pw, ps = orc.pack(q, s, g["group"], gateup=False)
+    assert np.array_equal(pw, g["plain_pw"]), "plain weight bytes differ from the hand-derived ones"
+    assert np.array_equal(ps, g["plain_ps"]), "plain scale bytes differ from the hand-derived ones"
+    pw, ps = orc.pack(q, s, g["group"], gateup=True)
+    assert np.array_equal(pw, g["gateup_pw"]), "gate/up weight bytes differ"
+    assert np.array_equal(ps, g["gateup_ps"]), "gate/up scale bytes differ"
+
+
+def pin_golden_unpack(orc):
+    g = load_golden()
+    q, s = golden_logical()
+    for layout in ("plain", "gateup"):
+        uq, us = orc.unpack(g[layout + "_pw"], g[layout + "_ps"], g["n"], g["k"], g["group"],
+                            gateup=(layout == "gateup"))
+        assert np.array_equal(uq, q), layout
+        assert np.array_equal(us, s), layout
+
+
+def pin_golden_gemv(orc):
+    g = load_golden()
+    q, s = golden_logical()
+    ones = _h(np.ones(g["k"]))
+    onehot = _h(np.eye(g["k"])[33])
+    for x, yk, ak in ((ones, "y_ones", "a_ones"), (onehot, "y_onehot33", "a_onehot33")):
+        y, a = orc.gemv(q, s, x, g["group"])
+        assert np.array_equal(y, g[yk]), (yk, y)
+        assert np.array_equal(a, g[ak]), (ak, a)
+        for layout in ("plain", "gateup"):
+            y2, a2 = orc.gemv_packed(g[layout + "_pw"], g[layout + "_ps"], x, g["n"], g["k"],
+                                     g["group"], gateup=(layout == "gateup"))
+            assert np.array_equal(y2, g[yk]), (layout, yk, y2)
+            assert np.array_equal(a2, g[ak]), (layout, ak, a2)
+
+
+def pin_pack_roundtrip(orc):
+    rng = np.random.default_rng(7)
+    for n, k, group, gateup in ((1, 32, 32, False), (3, 64, 32, False), (5, 96, 32, False),
+                                (7, 128, 64, False), (9, 256, 128, False), (2, 64, 32, True),
+                                (6, 128, 64, True), (10, 256, 128, True), (16, 64, 64, True)):
+        q = rng.integers(0, 16, (n, k), dtype=np.uint8)
+        s = _h(rng.uniform(-2, 2, (n, k // group)))
+        pw, ps = orc.pack(q, s, group, gateup)
+        wb, sb = orc.packed_sizes(n, k, group, gateup)
+        assert pw.size == wb and ps.size == sb
+        uq, us = orc.unpack(pw, ps, n, k, group, gateup)
+        assert np.array_equal(uq, q), (n, k, group, gateup)
+        assert np.array_equal(us, s), (n, k, group, gateup)
+
+
+def pin_packed_sizes(orc):
+    # closed forms: ceil(n/4) tiles of k/2 * 4 bytes, and (k/G) * 8 scale bytes
+    assert orc.packed_sizes(512, 256, 64) == (128 * 512, 128 * 4 * 8)
+    assert orc.packed_sizes(3584, 18944, 128) == (3584 * 18944 // 2, 896 * 148 * 8)
+    assert orc.packed_sizes(5, 32, 32) == (2 * 64, 2 * 8)
+    assert orc.packed_sizes(6, 32, 32, True) == (2 * 64, 2 * 8)    # halves of 3 rows, 1 tile each
+    assert orc.packed_sizes(10, 32, 32, True) == (4 * 64, 4 * 8)   # halves of 5 rows, 2 tiles each
+
+
+def pin_gemv_vs_numpy(orc):
+    rng = np.random.default_rng(11)
+    for n, k, group in ((512, 256, 64), (37, 384, 128), (6, 96, 32)):
+        q = rng.integers(0, 16, (n, k), dtype=np.uint8)
+        s = _h(rng.uniform(0.001, 0.02, (n, k // group)))
+        x = _h(rng.standard_normal(k))
+        w = _dequant_numpy(q, s, group)
+        xf = x.view(np.float16).astype(np.float64)
+        ref = w @ xf
+        refa = np.abs(w) @ np.abs(xf)
+        y, a = orc.gemv(q, s, x, group)
+        assert np.all(np.abs(y - ref) <= 1e-12 * refa + 1e-300), (n, k, group)
+        assert np.allclose(a, refa, rtol=1e-12, atol=0), (n, k, group)
+
+
+def pin_closed_forms(orc):
+    n, k, group = 5, 256, 64
+    ones = _h(np.ones(k))
+    one_s = _h(np.ones((n, k // group)))
+    rng = np.random.default_rng(3)
+    xr = _h(rng.integers(-4, 5, k))          # small integers: every sum exact
+    s_r = _h(rng.uniform(0.001, 0.02, (n, k // group)))
+    # zero point: q == 8 gives a zero matrix
+    y, a = orc.gemv(np.full((n, k), 8, np.uint8), s_r, xr, group)
+    assert np.all(y == 0) and np.all(a == 0)
+    # q == 15, s == 1, x == 1  ->  7K
+    y, _ = orc.gemv(np.full((n, k), 15, np.uint8), one_s, ones, group)
+    assert np.all(y == 7 * k)
+    # q == 0, s == 1  ->  -8 * sum(x)
+    y, _ = orc.gemv(np.zeros((n, k), np.uint8), one_s, xr, group)
+    assert np.all(y == -8 * xr.view(np.float16).astype(np.float64).sum())
+    # q == 9, s == 0.5, x == 1  ->  K/2
+    y, _ = orc.gemv(np.full((n, k), 9, np.uint8), _h(np.full((n, k // group), 0.5)), ones, group)
+    assert np.all(y == k / 2)
+
+
+def pin_onehot(orc):
+    rng = np.random.default_rng(5)
+    n, k, group = 9, 256, 64
+    q = rng.integers(0, 16, (n, k), dtype=np.uint8)
+    s = _h(rng.uniform(-0.02, 0.02, (n, k // group)))
+    sv = s.view(np.float16).astype(np.float64)
+    for kk in (0, 1, 7, 8, group - 1, group, 2 * group + 3, k - 1):
+        x = _h(np.eye(k)[kk])
+        y, a = orc.gemv(q, s, x, group)
+        expect = (q[:, kk].astype(np.float64) - 8.0) * sv[:, kk // group]
+        assert np.array_equal(y, expect), kk
+        assert np.array_equal(a, np.abs(expect)), kk
+
+
+def pin_scaling(orc):
+    rng = np.random.default_rng(9)
+    n, k, group = 13, 384, 128
+    q = rng.integers(0, 16, (n, k), dtype=np.uint8)
+    s = _h(rng.uniform(0.001, 0.02, (n, k // group)))
+    x = _h(rng.standard_normal(k))
+    x2 = _h(2.0 * x.view(np.float16).astype(np.float64))
+    y, a = orc.gemv(q, s, x, group)
+    y2, a2 = orc.gemv(q, s, x2, group)
+    assert np.array_equal(y2, 2 * y) and np.array_equal(a2, 2 * a)
+    assert np.all(a >= np.abs(y))
+    # all terms non-negative -> A == y
+    qp = rng.integers(8, 16, (n, k), dtype=np.uint8)
+    xp = _h(np.abs(x.view(np.float16)))
+    yp, ap = orc.gemv(qp, s, xp, group)
+    assert np.array_equal(yp, ap)
+
+
+def pin_rows_subset(orc):
+    rng = np.random.default_rng(13)
+    n, k, group = 21, 128, 32
+    q = rng.integers(0, 16, (n, k), dtype=np.uint8)
+    s = _h(rng.uniform(0.001, 0.02, (n, k // group)))
+    x = _h(rng.standard_normal(k))
+    y, a = orc.gemv(q, s, x, group)
+    rows = np.array([20, 0, 7, 7, 13], np.int64)
+    yr, ar = orc.gemv(q, s, x, group, rows=rows)
+    assert np.array_equal(yr, y[rows]) and np.array_equal(ar, a[rows])
+    for gateup in (False, True):
+        pw, ps = orc.pack(q[:20], s[:20], group, gateup)
+        yp, ap = orc.gemv_packed(pw, ps, x, 20, k, group, gateup, rows=rows[rows < 20])
+        assert np.array_equal(yp, y[rows[rows < 20]]) and np.array_equal(ap, a[rows[rows < 20]])
+
+
+def pin_silu(orc):
+    t = np.linspace(-20, 20, 4001)
+    ref = t * scipy.special.expit(t)
+    got = np.array([orc.silu(v) for v in t])
+    assert np.allclose(got, ref, rtol=1e-14, atol=1e-300)
+    assert orc.silu(0.0) == 0.0
+    # silu(-t) = silu(t) - t
+    for v in (0.5, 2.399, 7.0, 19.0):
+        assert abs(orc.silu(-v) - (orc.silu(v) - v)) <= 1e-14 * max(1.0, v)
+
+
+def pin_silu_gate(orc):
+    g = np.array([-3.0, 0.0, 1.5, 4.0])
+    u = np.array([2.0, 5.0, -1.0, 0.25])
+    h = orc.silu_gate(np.concatenate([g, u]))
+    assert np.allclose(h, g * scipy.special.expit(g) * u, rtol=1e-14, atol=0)
+    # gate rows come first: a zero up half gives zero regardless of the gate
+    assert np.all(orc.silu_gate(np.concatenate([g, np.zeros(4)])) == 0)
+
+
+def pin_argmax(orc):
+    rng = np.random.default_rng(17)
+    for _ in range(20):
+        y = rng.standard_normal(1000)
+        assert orc.argmax(y) == int(np.argmax(y))
+    y = np.array([1.0, 3.0, 2.0, 3.0, 3.0])
+    assert orc.argmax(y) == int(np.argmax(y)) == 1
+    y = np.array([np.nan, -1.0, 5.0, np.nan, 5.0])
+    assert orc.argmax(y) == 2
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

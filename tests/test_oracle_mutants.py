@@ -1,0 +1,75 @@
+"""Plant plausible mistakes in copies of the oracle (on the CPU) and check
+that at least one pin fails for each: the pins are strong enough to catch a
+dropped term, a wrong sign or index, a transposed operand, a wrong layout
+rule or a wrong tie-break."""
+import os
+import tempfile
+
+import pytest
+
+import oracle
+import oracle_pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "w4_oracle.c")
+
+# (name, text to find, replacement, which occurrence (0-based) or None for all)
+MUTANTS = [
+    ("zero_point_7", "(double)q[row * k + kk] - 8.0", "(double)q[row * k + kk] - 7.0", None),
+    ("packed_zero_point_7", "(double)qv - 8.0", "(double)qv - 7.0", None),
+    ("slot_map_swapped", "(e % 2 == 0) ? e / 2 : 4 + e / 2", "(e % 2 == 0) ? 4 + e / 2 : e / 2", None),
+    ("tile_row_reversed", "*r = (int)(row % 4);\n    }\n}", "*r = (int)(3 - row % 4);\n    }\n}", None),
+    ("up_row_slot", "*r = (int)((row - half) % 4);", "*r = (int)(row % 4);", None),
+    ("up_tile_base", "*tile = per_half + (row - half) / 4;", "*tile = (row - half) / 4;", None),
+    ("group_index_dropped", "s[row * ngroups + kk / group]", "s[row * ngroups]", None),
+    ("group_index_off_by_one", "s[row * ngroups + kk / group]", "s[row * ngroups + (kk + 1) % k / group]", None),
+    ("q_transposed", "q[row * k + kk]", "q[kk * n + row]", None),
+    ("x_reversed", "oracle_half_to_double(x[kk])", "oracle_half_to_double(x[k - 1 - kk])", None),
+    ("x_dropped", "double p = w * oracle_half_to_double(x[kk]);", "double p = w;", None),
+    ("abs_dropped", "mag += fabs(p);", "mag += p;", None),
+    ("half_exponent_bias", "expo - 25", "expo - 24", None),
+    ("half_subnormal", "ldexp((double)frac, -24)", "ldexp((double)frac, -25)", None),
+    ("half_sign_dropped", "return sign ? -v : v;", "return v;", None),
+    ("half_implicit_bit", "(double)(1024 + frac)", "(double)(frac)", None),
+    ("silu_sign", "t / (1.0 + exp(-t))", "t / (1.0 + exp(t))", None),
+    ("silu_gate_order", "oracle_silu(y[j]) * y[half + j]", "oracle_silu(y[half + j]) * y[j]", None),
+    ("argmax_last_tie", "y[i] > y[best]", "y[i] >= y[best]", None),
+    ("pack_pad_zero", "memset(pw, 0x88", "memset(pw, 0x00", None),
+    ("pack_word_slot", "(t * nblocks + j) * 16 + 4 * r;\n            dst[0]",
+     "(t * nblocks + j) * 16 + 4 * (3 - r);\n            dst[0]", None),
+    ("pack_scale_slot", "(t * ngroups + g) * 8 + 2 * r;\n            dst[0]",
+     "(t * ngroups + g) * 8 + 2 * (3 - r);\n            dst[0]", None),
+    ("pack_byte_order", "dst[0] = (uint8_t)(word & 0xff);", "dst[0] = (uint8_t)((word >> 24) & 0xff);", None),
+    ("unpack_nibble_shift", "q[row * k + 8 * j + e] = (uint8_t)((word >> (4 * slot_of_offset(e))) & 0xfu);",
+     "q[row * k + 8 * j + e] = (uint8_t)((word >> (4 * e)) & 0xfu);", None),
+    ("sizes_scale_bytes", "(k / group) * 8;", "(k / group) * 16;", None),
+]
+
+
+def _mutate(text, find, repl, occ):
+    assert find in text, f"mutation anchor not found: {find!r}"
+    if occ is None:
+        return text.replace(find, repl)
+    idx = -1
+    for _ in range(occ + 1):
+        idx = text.index(find, idx + 1)
+    return text[:idx] + repl + text[idx + len(find):]
+
+
+@pytest.mark.parametrize("name,find,repl,occ", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(name, find, repl, occ, tmp_path):
+    text = open(SRC).read()
+    mutated = _mutate(text, find, repl, occ)
+    assert mutated != text
+    src = tmp_path / f"{name}.c"
+    src.write_text(mutated)
+    lib = oracle.build(str(src), str(tmp_path / f"lib{name}.so"))
+    orc = oracle.Oracle(lib)
+    failed = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(orc)
+        except AssertionError:
+            failed.append(pin.__name__)
+        except ValueError:
+            failed.append(pin.__name__)
+    assert failed, f"mutant {name} passed every pin"
