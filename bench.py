@@ -1,0 +1,279 @@
+"""Benchmark: the per-token INT4 linear sweep of a 28-layer decode step.
+
+One step = one replay of the captured HIP graph that runs, in decode order,
+28 x (QKV 3584->4608, o_proj 3584->3584, gate/up 3584->2x18944 + SiLU,
+down 18944->3584) and lm_head 3584->152064 + argmax: 113 GEMVs over
+3,650,274,304 algorithmic bytes (packed nibbles + fp16 scales + fp16 x +
+outputs), all resident in HBM before timing starts.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 5]
+
+prints one JSON line: achieved GB/s over the whole sweep (value), ms per
+sweep, the eager-launch sweep for comparison, the dominant kernel's roofline
+(gate/up + SiLU, timed per launch with HIP events on the launch stream) and
+the CPU oracle timed on a bounded sample on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import synthetic  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "achieved HBM GB/s (% of peak) and ms per 28-layer+lm_head INT4 linear sweep"
+KERNEL_SRC = os.path.join(ROOT, "int4_weight_only_04_amd", "csrc", "w4_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gateup_silu_37888x3584.json")
+
+
+def algorithmic_bytes(kind: str, n: int, k: int, group: int) -> int:
+    """Bytes a GEMV must move at least once: nibbles, scales, x, outputs."""
+    b = n * k // 2 + 2 * n * (k // group) + 2 * k
+    if kind == "gateup":
+        b += 2 * (n // 2)
+    else:
+        b += 4 * n
+    if kind == "lmhead":
+        b += 4
+    return b
+
+
+def sweep_bytes(projs) -> int:
+    return sum(algorithmic_bytes(p.kind, p.n, p.k, p.group) for p in projs)
+
+
+def build_sweep(layers: int = synthetic.LAYERS, device: str = "cuda"):
+    """Device buffers of the sweep: each projection's inputs are drawn already
+    packed (uniform random bytes = i.i.d. uniform nibbles; all row counts are
+    multiples of 4, so there are no padding slots) from its own seed."""
+    import torch
+    from int4_weight_only_04_amd import w4
+
+    specs = synthetic.sweep_projections(layers)
+    projs = []
+    for p in specs:
+        layout = "gateup" if p.kind == "gateup" else "plain"
+        wb, sb = w4.packed_size(p.n, p.k, p.group, layout)
+        pw, ps, x = synthetic.packed_random(p.seed, wb, sb // 2, p.k)
+        dpw = torch.from_numpy(pw).to(device)
+        dps = torch.from_numpy(ps).to(device)
+        dx = torch.from_numpy(x.view(np.int16)).to(device).view(torch.float16)
+        if p.kind == "gateup":
+            out = torch.empty(p.n // 2, dtype=torch.float16, device=device)
+            projs.append(w4.Proj(w4.PROJ_GATEUP_SILU, p.n, p.k, p.group, dpw, dps, dx, out))
+        elif p.kind == "lmhead":
+            out = torch.empty(p.n, dtype=torch.float32, device=device)
+            am = torch.full((1,), -1, dtype=torch.int32, device=device)
+            ws = torch.zeros(w4.gemv_workspace_size(p.n, p.k, p.group, True), dtype=torch.uint8,
+                             device=device)
+            projs.append(w4.Proj(w4.PROJ_LMHEAD_ARGMAX, p.n, p.k, p.group, dpw, dps, dx, out, am, ws))
+        else:
+            out = torch.empty(p.n, dtype=torch.float32, device=device)
+            projs.append(w4.Proj(w4.PROJ_PLAIN, p.n, p.k, p.group, dpw, dps, dx, out))
+    return specs, projs
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(launch_bytes_alg: int):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, or None if absent or taken on another kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def time_graph(sweep, stream, steps: int, warmup: int):
+    import torch
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            sweep.run(stream)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(steps):
+        sweep.run(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = start.elapsed_time(end) / steps
+    return ev_ms, wall * 1e3 / steps
+
+
+def time_dominant_kernel(projs, stream, rounds: int = 3):
+    """Average duration of one gate/up + SiLU launch (the kernel that moves
+    the most bytes in the sweep), from HIP events recorded around each launch
+    on the launch stream, cycling through the 28 layers' weights (1.96 GB, so
+    nothing is served from the 256 MB Infinity Cache)."""
+    import torch
+    from int4_weight_only_04_amd import w4
+    gu = [p for p in projs if p.kind == w4.PROJ_GATEUP_SILU]
+    evs = []
+    with torch.cuda.stream(stream):
+        for _ in range(rounds):
+            for p in gu:
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                w4.gemv_gateup_silu(p.packed_w, p.packed_s, p.x, p.out, p.n, p.k, p.group, stream)
+                b.record(stream)
+                evs.append((a, b))
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in evs[len(gu):]]  # first round warms up
+    return float(np.mean(ms)), float(np.median(ms)), len(ms)
+
+
+def cpu_baseline():
+    """The oracle as it stands (single thread, fp64) on a bounded sample: all
+    rows of layer 0's four projections, inputs drawn exactly as in the sweep."""
+    import oracle
+    from int4_weight_only_04_amd import w4
+    specs = synthetic.sweep_projections(1)
+    total_bytes = 0
+    t_total = 0.0
+    for p in specs:
+        layout = "gateup" if p.kind == "gateup" else "plain"
+        wb, sb = w4.packed_size(p.n, p.k, p.group, layout)
+        pw, ps, x = synthetic.packed_random(p.seed, wb, sb // 2, p.k)
+        t0 = time.perf_counter()
+        y, _ = oracle.gemv_packed(pw, ps, x, p.n, p.k, p.group, gateup=(layout == "gateup"))
+        if p.kind == "gateup":
+            oracle.silu_gate(y)
+        t_total += time.perf_counter() - t0
+        total_bytes += algorithmic_bytes(p.kind, p.n, p.k, p.group)
+    return {
+        "value": total_bytes / t_total / 1e9,
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": "layer 0 of the sweep (qkv, o_proj, gate/up+silu, down), all rows, "
+                  f"{total_bytes} algorithmic bytes in {t_total:.1f} s, single-threaded fp64 C",
+        "seconds": t_total,
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--layers", type=int, default=synthetic.LAYERS)
+    ap.add_argument("--eager-steps", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the INT4 decode GEMV sweep is a single-GPU path here; "
+              "run it with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+    from int4_weight_only_04_amd import w4
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    w4.lib()
+
+    if args.copy_probe:
+        nbytes = 1 << 30
+        src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(3)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": nbytes, "launches": 3}), flush=True)
+        return 0
+
+    print(f"[bench] building sweep ({args.layers} layers)", file=sys.stderr, flush=True)
+    specs, projs = build_sweep(args.layers)
+    alg_bytes = sweep_bytes(specs)
+    stream = torch.cuda.Stream()
+
+    print("[bench] graph sweep", file=sys.stderr, flush=True)
+    graph = w4.Sweep(projs, use_graph=True)
+    ev_ms, wall_ms = time_graph(graph, stream, args.steps, args.warmup)
+
+    print("[bench] eager sweep", file=sys.stderr, flush=True)
+    eager = w4.Sweep(projs, use_graph=False)
+    eager_ms, eager_wall_ms = time_graph(eager, stream, args.eager_steps, 2)
+    eager.close()
+
+    print("[bench] dominant kernel", file=sys.stderr, flush=True)
+    gu_mean_ms, gu_median_ms, gu_launches = time_dominant_kernel(projs, stream)
+    gp = next(p for p in specs if p.kind == "gateup")
+    gu_bytes = algorithmic_bytes("gateup", gp.n, gp.k, gp.group)
+    gu_gbs = gu_bytes / (gu_mean_ms * 1e-3) / 1e9
+    graph.close()
+
+    value = alg_bytes / (ev_ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ev_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"batch-1 decode-step INT4 linear sweep, hipGraph: {args.layers} x (qkv 3584->4608, "
+                         "o_proj 3584->3584, gate/up 3584->2x18944 + silu, down 18944->3584) + lm_head "
+                         "3584->152064 + argmax; int4 zero point 8, fp16 scales per 128 inputs, fp16 x, "
+                         "fp32 accumulation"),
+            "gemvs_per_step": len(specs),
+            "algorithmic_bytes_per_step": alg_bytes,
+            "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+            "wall_ms_per_step": round(wall_ms, 4),
+            "eager_ms_per_step": round(eager_ms, 4),
+            "graph_speedup_vs_eager": round(eager_ms / ev_ms, 3),
+        },
+        "roofline": {
+            "kernel": "gemv_w4_kernel<2, gate/up+silu> 37888x3584 g128",
+            "bound": "hbm",
+            "achieved": round(gu_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
+            "traffic": read_traffic(gu_bytes),
+            "algorithmic_bytes_per_launch": gu_bytes,
+            "avg_launch_us": round(gu_mean_ms * 1e3, 3),
+            "median_launch_us": round(gu_median_ms * 1e3, 3),
+            "launches_timed": gu_launches,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,191 @@
+/*
+ * w4.h -- C ABI of the MI355X (gfx950) INT4 weight-only decode GEMV library.
+ *
+ * The operation.  "How To Build Your Own LLM Runtime From Scratch"
+ * (aitrending.vip), section "Technical Details", first bullet: the runtime
+ * packs its weights, stores them as INT4 and dequantizes them at run time;
+ * the third page (noticiai.com.br, "As tres licoes", lesson 3) says the
+ * activations stay in floating point (the INT8-activation path was removed).
+ * The pages fix no quantization format; this library uses zero point 8 and one
+ * fp16 scale per row and per group of G consecutive inputs:
+ *
+ *     w[n][k] = (q[n][k] - 8) * s[n][k / G],   q in {0..15}
+ *     y[n]    = sum_k w[n][k] * x[k]            x fp16, products and sums fp32
+ *
+ * The decode step that runs these products once per token, for the fused QKV,
+ * o_proj, fused gate/up (with a SiLU-gated epilogue), down_proj and lm_head
+ * projections of each of 28 layers of a 3584-hidden / 18944-MLP / 152064-vocab
+ * model (same page, section 技术解析, first bullet), is replayed as one captured
+ * graph: the pages attribute a ~7x per-token gain to graph capture (section
+ * "CUDA Graph Optimization" / "Technical Details", third bullet).
+ *
+ * Conventions for every entry point.
+ *   - Every function returns a w4_status; W4_OK is 0.  On failure nothing has
+ *     been launched, and w4_last_error() returns a thread-local message.
+ *   - No C++ exception crosses this boundary.
+ *   - "device" pointers are HIP device allocations (e.g. torch CUDA tensors
+ *     on ROCm); "host" pointers are ordinary CPU memory.  The caller owns every
+ *     buffer; the library never frees caller memory.
+ *   - Device calls are asynchronous on the given stream (a hipStream_t passed
+ *     as void*, NULL = the legacy default stream).  A device fault surfaces at
+ *     the caller's next synchronization, not in the call.
+ *   - Calls on different streams may run concurrently from different threads;
+ *     one sweep handle must not be used by two threads at once.
+ *
+ * Packed layout "W4T4" (produced by w4_pack, consumed by the kernels).
+ *   - Rows are grouped in tiles of 4.  Plain layout: tile t holds rows
+ *     4t..4t+3 (ceil(n/4) tiles).  Gate/up layout (n = 2I): the gate half and
+ *     the up half are tiled separately, gate tiles first (2*ceil(I/4) tiles),
+ *     so that gate row j and up row j sit in the same slot of tiles j/4 and
+ *     ceil(I/4) + j/4.  Slots beyond the logical rows are padding (nibble 8,
+ *     scale +0.0, i.e. a zero weight).
+ *   - Weights: the 8 inputs 8j..8j+7 of tile t occupy 16 bytes at byte offset
+ *     (t * (k/8) + j) * 16; little-endian 32-bit word r of those 16 bytes holds
+ *     tile row r.  Nibble slot p of a word (bits 4p..4p+3) holds input offset
+ *     2p for p < 4 and 2(p-4)+1 for p >= 4, so the masks 0x000F000F and
+ *     0x00F000F0 (and the same after a shift by 8) pull out the input pairs
+ *     (0,1), (2,3), (4,5), (6,7) as two fp16 lanes each.
+ *   - Scales: tile t, group g occupies 8 bytes at byte offset
+ *     (t * (k/G) + g) * 8; the fp16 at bytes 2r..2r+1 is tile row r's scale.
+ *   - Size: weight bytes = tiles * k / 2 * 4, scale bytes = tiles * (k/G) * 8.
+ *
+ * Shape rules (W4_ESHAPE otherwise): n >= 1; k >= 8; G a power of two with
+ * 8 <= G <= k and k % G == 0; k <= 32768 (x is staged whole in LDS);
+ * gate/up: n even.  Device pointers must be 16-byte aligned (W4_EALIGN).
+ */
+#ifndef W4_H
+#define W4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t w4_status;
+
+#define W4_OK 0
+#define W4_EINVAL 1   /* null pointer, bad enum, nibble > 15, size mismatch */
+#define W4_ESHAPE 2   /* shape outside the rules above                     */
+#define W4_EALIGN 3   /* device pointer not 16-byte aligned                */
+#define W4_EHIP 4     /* a HIP runtime call failed (message names it)      */
+#define W4_ENOMEM 5   /* host allocation failed                            */
+#define W4_ECAPTURE 6 /* graph capture / instantiation failed              */
+
+#define W4_LAYOUT_PLAIN 0
+#define W4_LAYOUT_GATEUP 1
+
+/* Status code -> static string ("W4_OK", "W4_EINVAL", ...). */
+const char* w4_status_string(w4_status status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* w4_last_error(void);
+
+/* ABI version of this header: 1. */
+int32_t w4_abi_version(void);
+
+/*
+ * Packed sizes of an n x k matrix with group size `group` in `layout`
+ * (W4_LAYOUT_PLAIN or W4_LAYOUT_GATEUP), in bytes.  Host only, no device.
+ * Outputs must be non-null.
+ */
+w4_status w4_packed_size(int64_t n, int64_t k, int32_t group, int32_t layout,
+                         size_t* weight_bytes, size_t* scale_bytes);
+
+/*
+ * Pack logical INT4 weights into the W4T4 layout ("Technical Details",
+ * first bullet: weight packing).  Host only.
+ *   q        host, uint8 [n][k] row-major, every value in 0..15 (W4_EINVAL
+ *            names the first offending element otherwise; the outputs are
+ *            then partially written);
+ *   scales   host, fp16 bit patterns [n][k/group] row-major;
+ *   packed_w host, packed_w_bytes == the weight size from w4_packed_size;
+ *   packed_s host, packed_s_bytes == the scale size from w4_packed_size.
+ * Padding slots are written too, so the outputs are fully defined.
+ */
+w4_status w4_pack(const uint8_t* q, const uint16_t* scales, int64_t n, int64_t k, int32_t group,
+                  int32_t layout, void* packed_w, size_t packed_w_bytes, void* packed_s,
+                  size_t packed_s_bytes);
+
+/*
+ * Workspace bytes w4_gemv needs: 0 without argmax, a small fixed size with
+ * argmax.  Host only.
+ */
+w4_status w4_gemv_workspace_size(int64_t n, int64_t k, int32_t group, int32_t with_argmax,
+                                 size_t* bytes);
+
+/*
+ * y = W x for a plain-layout packed matrix, optionally with the lm_head argmax
+ * epilogue (lowest index of the largest y; NaN never wins; -1 if every y is
+ * NaN).  Device, asynchronous on `stream`.
+ *   packed_w, packed_s  device, from w4_pack(..., W4_LAYOUT_PLAIN, ...);
+ *   x        device, fp16 [k];
+ *   y        device, fp32 [n] (written for every row);
+ *   argmax   device int32 [1], or NULL for no argmax;
+ *   workspace device, >= w4_gemv_workspace_size bytes when argmax != NULL
+ *            (may be NULL otherwise).  It must be zero-filled once before its
+ *            first use; every completed call leaves it zero-filled again, so it
+ *            can be reused and replayed without clearing.  Calls that may run
+ *            at the same time need separate workspaces.
+ */
+w4_status w4_gemv(const void* packed_w, const void* packed_s, const uint16_t* x, float* y,
+                  int32_t* argmax, void* workspace, size_t workspace_bytes, int64_t n, int64_t k,
+                  int32_t group, void* stream);
+
+/*
+ * Fused gate/up + SiLU: with I = n_total / 2, g = rows [0, I) of W x and
+ * u = rows [I, 2I), h[j] = silu(g[j]) * u[j] rounded to fp16 (nearest even),
+ * silu(t) = t / (1 + e^-t).  Device, asynchronous on `stream`.
+ *   packed_w, packed_s  device, from w4_pack(..., W4_LAYOUT_GATEUP, ...);
+ *   x  device fp16 [k];  h  device fp16 [n_total / 2].
+ */
+w4_status w4_gemv_gateup_silu(const void* packed_w, const void* packed_s, const uint16_t* x,
+                              uint16_t* h, int64_t n_total, int64_t k, int32_t group, void* stream);
+
+/* One projection of the per-token linear sweep. */
+#define W4_PROJ_PLAIN 0         /* w4_gemv, out = float y[n]                  */
+#define W4_PROJ_GATEUP_SILU 1   /* w4_gemv_gateup_silu, out = fp16 h[n/2]     */
+#define W4_PROJ_LMHEAD_ARGMAX 2 /* w4_gemv with argmax, out = float y[n]      */
+
+typedef struct w4_proj_desc {
+    int32_t kind;          /* W4_PROJ_*                                      */
+    int32_t group;         /* G                                              */
+    int64_t n;             /* rows (gate/up: n_total = 2I)                   */
+    int64_t k;             /* inputs                                         */
+    const void* packed_w;  /* device                                         */
+    const void* packed_s;  /* device                                         */
+    const uint16_t* x;     /* device fp16 [k]                                */
+    void* out;             /* device float [n] or fp16 [n/2]                 */
+    int32_t* argmax;       /* device int32 [1] (LMHEAD_ARGMAX only)          */
+    void* workspace;       /* device (LMHEAD_ARGMAX only), zero-filled once  */
+    size_t workspace_bytes;
+} w4_proj_desc;
+
+typedef struct w4_sweep w4_sweep;
+
+/*
+ * Build the per-token sweep over `count` projections, run in array order
+ * (the decode order: per layer QKV, o_proj, gate/up, down; then lm_head).
+ * use_graph != 0 captures all launches into one HIP graph (one submission
+ * per token, as the pages' "CUDA Graph Optimization" bullet describes);
+ * use_graph == 0 keeps them as eager launches, for the eager-vs-graph
+ * comparison.  Every descriptor is validated first.  The handle keeps a copy
+ * of the descriptors and the graph, which bakes in every pointer: the buffers
+ * must stay alive and in place until w4_decode_linear_sweep_destroy.
+ * Capture uses a private stream of the library.
+ */
+w4_status w4_decode_linear_sweep_create(const w4_proj_desc* projs, int32_t count,
+                                        int32_t use_graph, w4_sweep** out);
+
+/* Run one token's sweep on `stream` (graph launch or eager launches). */
+w4_status w4_decode_linear_sweep(w4_sweep* sweep, void* stream);
+
+/* Release the handle (NULL is accepted). */
+w4_status w4_decode_linear_sweep_destroy(w4_sweep* sweep);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4_H */

@@ -1,0 +1,364 @@
+// extern "C" entry points of the INT4 weight-only GEMV library: argument
+// validation, error reporting, the host packer entry, single-GEMV launches
+// and the per-token sweep (eager launches or one captured HIP graph).
+#include <hip/hip_runtime_api.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <new>
+#include <string>
+#include <vector>
+
+#include "w4.h"
+#include "w4_internal.h"
+
+namespace w4i {
+int64_t pack_w4t4(const uint8_t* q, const uint16_t* s, int64_t n, int64_t k, int32_t group,
+                  bool gateup, uint8_t* pw, uint8_t* ps);
+}
+
+using namespace w4i;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+w4_status fail(w4_status code, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+w4_status ok()
+{
+    return W4_OK;
+}
+
+w4_status hip_fail(hipError_t err, const char* what)
+{
+    return fail(W4_EHIP, "%s failed: %s (%d)", what, hipGetErrorString(err), (int)err);
+}
+
+bool aligned16(const void* p)
+{
+    return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+w4_status check_shape(int64_t n, int64_t k, int32_t group, bool gateup, const char* who)
+{
+    if (n < 1) return fail(W4_ESHAPE, "%s: n=%lld must be >= 1", who, (long long)n);
+    if (k < 8) return fail(W4_ESHAPE, "%s: k=%lld must be >= 8", who, (long long)k);
+    if (k > kMaxK) return fail(W4_ESHAPE, "%s: k=%lld exceeds %lld", who, (long long)k, (long long)kMaxK);
+    if (group < 8 || (group & (group - 1)) != 0)
+        return fail(W4_ESHAPE, "%s: group=%d must be a power of two >= 8", who, group);
+    if (group > k || k % group != 0)
+        return fail(W4_ESHAPE, "%s: k=%lld must be a multiple of group=%d", who, (long long)k, group);
+    if (gateup && n % 2 != 0)
+        return fail(W4_ESHAPE, "%s: gate/up n_total=%lld must be even", who, (long long)n);
+    if (tiles_for(n, gateup) > ((int64_t)1 << 40))
+        return fail(W4_ESHAPE, "%s: n=%lld too large", who, (long long)n);
+    return W4_OK;
+}
+
+void sizes(int64_t n, int64_t k, int32_t group, bool gateup, size_t* wb, size_t* sb)
+{
+    const int64_t tiles = tiles_for(n, gateup);
+    *wb = (size_t)(tiles * (k / 8) * 16);
+    *sb = (size_t)(tiles * (k / group) * 8);
+}
+
+w4_status validate_gemv(const GemvCall& c, const char* who)
+{
+    const bool gateup = c.epi == kEpiGateUp;
+    w4_status st = check_shape(c.n, c.k, c.group, gateup, who);
+    if (st != W4_OK) return st;
+    if (!c.pw || !c.ps || !c.x || !c.out)
+        return fail(W4_EINVAL, "%s: null pointer (packed_w=%p packed_s=%p x=%p out=%p)", who, c.pw,
+                    c.ps, c.x, c.out);
+    if (!aligned16(c.pw) || !aligned16(c.ps) || !aligned16(c.x))
+        return fail(W4_EALIGN, "%s: packed_w, packed_s and x must be 16-byte aligned", who);
+    if (c.epi == kEpiArgmax) {
+        if (!c.argmax || !c.ws)
+            return fail(W4_EINVAL, "%s: argmax needs argmax and workspace pointers", who);
+        if (!aligned16(c.ws)) return fail(W4_EALIGN, "%s: workspace must be 16-byte aligned", who);
+        if (c.n > INT32_MAX - 1)
+            return fail(W4_ESHAPE, "%s: argmax needs n < 2^31-1 (int32 index)", who);
+    }
+    return W4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* w4_status_string(w4_status status)
+{
+    switch (status) {
+        case W4_OK: return "W4_OK";
+        case W4_EINVAL: return "W4_EINVAL";
+        case W4_ESHAPE: return "W4_ESHAPE";
+        case W4_EALIGN: return "W4_EALIGN";
+        case W4_EHIP: return "W4_EHIP";
+        case W4_ENOMEM: return "W4_ENOMEM";
+        case W4_ECAPTURE: return "W4_ECAPTURE";
+        default: return "W4_UNKNOWN";
+    }
+}
+
+const char* w4_last_error(void)
+{
+    return g_last_error.c_str();
+}
+
+int32_t w4_abi_version(void)
+{
+    return 1;
+}
+
+w4_status w4_packed_size(int64_t n, int64_t k, int32_t group, int32_t layout, size_t* weight_bytes,
+                         size_t* scale_bytes)
+{
+    try {
+        if (!weight_bytes || !scale_bytes) return fail(W4_EINVAL, "w4_packed_size: null output");
+        if (layout != W4_LAYOUT_PLAIN && layout != W4_LAYOUT_GATEUP)
+            return fail(W4_EINVAL, "w4_packed_size: unknown layout %d", layout);
+        const bool gateup = layout == W4_LAYOUT_GATEUP;
+        w4_status st = check_shape(n, k, group, gateup, "w4_packed_size");
+        if (st != W4_OK) return st;
+        sizes(n, k, group, gateup, weight_bytes, scale_bytes);
+        return ok();
+    } catch (...) {
+        return fail(W4_EINVAL, "w4_packed_size: internal exception");
+    }
+}
+
+w4_status w4_pack(const uint8_t* q, const uint16_t* scales, int64_t n, int64_t k, int32_t group,
+                  int32_t layout, void* packed_w, size_t packed_w_bytes, void* packed_s,
+                  size_t packed_s_bytes)
+{
+    try {
+        if (!q || !scales || !packed_w || !packed_s) return fail(W4_EINVAL, "w4_pack: null pointer");
+        if (layout != W4_LAYOUT_PLAIN && layout != W4_LAYOUT_GATEUP)
+            return fail(W4_EINVAL, "w4_pack: unknown layout %d", layout);
+        const bool gateup = layout == W4_LAYOUT_GATEUP;
+        w4_status st = check_shape(n, k, group, gateup, "w4_pack");
+        if (st != W4_OK) return st;
+        size_t wb, sb;
+        sizes(n, k, group, gateup, &wb, &sb);
+        if (packed_w_bytes != wb || packed_s_bytes != sb)
+            return fail(W4_EINVAL, "w4_pack: buffer sizes %zu/%zu, expected %zu/%zu", packed_w_bytes,
+                        packed_s_bytes, wb, sb);
+        const int64_t bad = pack_w4t4(q, scales, n, k, group, gateup, static_cast<uint8_t*>(packed_w),
+                                      static_cast<uint8_t*>(packed_s));
+        if (bad >= 0)
+            return fail(W4_EINVAL, "w4_pack: q[%lld][%lld] = %u is not a 4-bit value",
+                        (long long)(bad / k), (long long)(bad % k), (unsigned)q[bad]);
+        return ok();
+    } catch (const std::bad_alloc&) {
+        return fail(W4_ENOMEM, "w4_pack: out of host memory");
+    } catch (...) {
+        return fail(W4_EINVAL, "w4_pack: internal exception");
+    }
+}
+
+w4_status w4_gemv_workspace_size(int64_t n, int64_t k, int32_t group, int32_t with_argmax,
+                                 size_t* bytes)
+{
+    try {
+        if (!bytes) return fail(W4_EINVAL, "w4_gemv_workspace_size: null output");
+        w4_status st = check_shape(n, k, group, false, "w4_gemv_workspace_size");
+        if (st != W4_OK) return st;
+        *bytes = with_argmax ? kArgmaxWorkspaceBytes : 0;
+        return ok();
+    } catch (...) {
+        return fail(W4_EINVAL, "w4_gemv_workspace_size: internal exception");
+    }
+}
+
+w4_status w4_gemv(const void* packed_w, const void* packed_s, const uint16_t* x, float* y,
+                  int32_t* argmax, void* workspace, size_t workspace_bytes, int64_t n, int64_t k,
+                  int32_t group, void* stream)
+{
+    try {
+        GemvCall c{packed_w, packed_s, x, y, argmax, workspace, n, k, group,
+                   argmax ? kEpiArgmax : kEpiPlain};
+        w4_status st = validate_gemv(c, "w4_gemv");
+        if (st != W4_OK) return st;
+        if (argmax && workspace_bytes < kArgmaxWorkspaceBytes)
+            return fail(W4_EINVAL, "w4_gemv: workspace of %zu bytes, need %zu", workspace_bytes,
+                        kArgmaxWorkspaceBytes);
+        hipError_t err = launch_gemv(c, static_cast<hipStream_t>(stream));
+        if (err != hipSuccess) return hip_fail(err, "w4_gemv launch");
+        return ok();
+    } catch (...) {
+        return fail(W4_EINVAL, "w4_gemv: internal exception");
+    }
+}
+
+w4_status w4_gemv_gateup_silu(const void* packed_w, const void* packed_s, const uint16_t* x,
+                              uint16_t* h, int64_t n_total, int64_t k, int32_t group, void* stream)
+{
+    try {
+        GemvCall c{packed_w, packed_s, x, h, nullptr, nullptr, n_total, k, group, kEpiGateUp};
+        w4_status st = validate_gemv(c, "w4_gemv_gateup_silu");
+        if (st != W4_OK) return st;
+        hipError_t err = launch_gemv(c, static_cast<hipStream_t>(stream));
+        if (err != hipSuccess) return hip_fail(err, "w4_gemv_gateup_silu launch");
+        return ok();
+    } catch (...) {
+        return fail(W4_EINVAL, "w4_gemv_gateup_silu: internal exception");
+    }
+}
+
+}  // extern "C"
+
+struct w4_sweep {
+    std::vector<GemvCall> calls;
+    bool use_graph = false;
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+};
+
+namespace {
+
+w4_status desc_to_call(const w4_proj_desc& d, int32_t idx, GemvCall* out)
+{
+    int32_t epi;
+    switch (d.kind) {
+        case W4_PROJ_PLAIN: epi = kEpiPlain; break;
+        case W4_PROJ_GATEUP_SILU: epi = kEpiGateUp; break;
+        case W4_PROJ_LMHEAD_ARGMAX: epi = kEpiArgmax; break;
+        default: return fail(W4_EINVAL, "sweep projection %d: unknown kind %d", idx, d.kind);
+    }
+    *out = GemvCall{d.packed_w, d.packed_s, d.x, d.out, d.argmax, d.workspace, d.n, d.k, d.group, epi};
+    char who[64];
+    snprintf(who, sizeof who, "sweep projection %d", idx);
+    w4_status st = validate_gemv(*out, who);
+    if (st != W4_OK) return st;
+    if (epi == kEpiArgmax && d.workspace_bytes < kArgmaxWorkspaceBytes)
+        return fail(W4_EINVAL, "%s: workspace of %zu bytes, need %zu", who, d.workspace_bytes,
+                    kArgmaxWorkspaceBytes);
+    return W4_OK;
+}
+
+w4_status launch_all(const std::vector<GemvCall>& calls, hipStream_t stream)
+{
+    for (size_t i = 0; i < calls.size(); ++i) {
+        hipError_t err = launch_gemv(calls[i], stream);
+        if (err != hipSuccess) {
+            char what[64];
+            snprintf(what, sizeof what, "sweep launch %zu", i);
+            return hip_fail(err, what);
+        }
+    }
+    return W4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+w4_status w4_decode_linear_sweep_create(const w4_proj_desc* projs, int32_t count, int32_t use_graph,
+                                        w4_sweep** out)
+{
+    try {
+        if (!out) return fail(W4_EINVAL, "w4_decode_linear_sweep_create: null output");
+        *out = nullptr;
+        if (!projs || count < 1)
+            return fail(W4_EINVAL, "w4_decode_linear_sweep_create: need at least one projection");
+        w4_sweep* sw = new w4_sweep();
+        sw->use_graph = use_graph != 0;
+        sw->calls.resize((size_t)count);
+        for (int32_t i = 0; i < count; ++i) {
+            w4_status st = desc_to_call(projs[i], i, &sw->calls[(size_t)i]);
+            if (st != W4_OK) {
+                delete sw;
+                return st;
+            }
+        }
+        if (sw->use_graph) {
+            hipStream_t cap = nullptr;
+            hipError_t err = hipStreamCreateWithFlags(&cap, hipStreamNonBlocking);
+            if (err != hipSuccess) {
+                delete sw;
+                return hip_fail(err, "hipStreamCreateWithFlags");
+            }
+            // Resolve per-kernel residency (host queries) before capture.
+            for (size_t i = 0; i < sw->calls.size() && err == hipSuccess; ++i)
+                err = prepare_gemv(sw->calls[i]);
+            if (err != hipSuccess) {
+                hipStreamDestroy(cap);
+                delete sw;
+                return hip_fail(err, "device query before capture");
+            }
+            err = hipStreamBeginCapture(cap, hipStreamCaptureModeThreadLocal);
+            if (err != hipSuccess) {
+                hipStreamDestroy(cap);
+                delete sw;
+                return fail(W4_ECAPTURE, "hipStreamBeginCapture failed: %s", hipGetErrorString(err));
+            }
+            w4_status st = launch_all(sw->calls, cap);
+            hipGraph_t graph = nullptr;
+            hipError_t end_err = hipStreamEndCapture(cap, &graph);
+            hipStreamDestroy(cap);
+            if (st != W4_OK || end_err != hipSuccess) {
+                if (graph) hipGraphDestroy(graph);
+                delete sw;
+                if (st != W4_OK) return st;
+                return fail(W4_ECAPTURE, "hipStreamEndCapture failed: %s", hipGetErrorString(end_err));
+            }
+            hipGraphExec_t exec = nullptr;
+            err = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+            if (err != hipSuccess) {
+                hipGraphDestroy(graph);
+                delete sw;
+                return fail(W4_ECAPTURE, "hipGraphInstantiate failed: %s", hipGetErrorString(err));
+            }
+            sw->graph = graph;
+            sw->exec = exec;
+        }
+        *out = sw;
+        return ok();
+    } catch (const std::bad_alloc&) {
+        return fail(W4_ENOMEM, "w4_decode_linear_sweep_create: out of host memory");
+    } catch (...) {
+        return fail(W4_EINVAL, "w4_decode_linear_sweep_create: internal exception");
+    }
+}
+
+w4_status w4_decode_linear_sweep(w4_sweep* sweep, void* stream)
+{
+    try {
+        if (!sweep) return fail(W4_EINVAL, "w4_decode_linear_sweep: null handle");
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        if (sweep->use_graph) {
+            hipError_t err = hipGraphLaunch(sweep->exec, s);
+            if (err != hipSuccess) return hip_fail(err, "hipGraphLaunch");
+            return ok();
+        }
+        return launch_all(sweep->calls, s);
+    } catch (...) {
+        return fail(W4_EINVAL, "w4_decode_linear_sweep: internal exception");
+    }
+}
+
+w4_status w4_decode_linear_sweep_destroy(w4_sweep* sweep)
+{
+    try {
+        if (!sweep) return ok();
+        if (sweep->exec) hipGraphExecDestroy(sweep->exec);
+        if (sweep->graph) hipGraphDestroy(sweep->graph);
+        delete sweep;
+        return ok();
+    } catch (...) {
+        return fail(W4_EINVAL, "w4_decode_linear_sweep_destroy: internal exception");
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,258 @@
+"""Python binding of libw4.so (ctypes): argument marshalling only.
+
+Every step of the GEMV runs in the HIP kernels behind the C ABI declared in
+include/w4.h; PyTorch provides device memory and streams.  If the library is
+not built, every call raises -- there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libw4.so")
+
+OK, EINVAL, ESHAPE, EALIGN, EHIP, ENOMEM, ECAPTURE = range(7)
+LAYOUT_PLAIN, LAYOUT_GATEUP = 0, 1
+PROJ_PLAIN, PROJ_GATEUP_SILU, PROJ_LMHEAD_ARGMAX = 0, 1, 2
+
+EXPORTED = (
+    "w4_status_string", "w4_last_error", "w4_abi_version", "w4_packed_size", "w4_pack",
+    "w4_gemv_workspace_size", "w4_gemv", "w4_gemv_gateup_silu",
+    "w4_decode_linear_sweep_create", "w4_decode_linear_sweep", "w4_decode_linear_sweep_destroy",
+)
+
+
+class W4Error(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        super().__init__(f"{where}: status {status}: {detail}")
+
+
+class ProjDesc(ctypes.Structure):
+    _fields_ = [
+        ("kind", ctypes.c_int32),
+        ("group", ctypes.c_int32),
+        ("n", ctypes.c_int64),
+        ("k", ctypes.c_int64),
+        ("packed_w", ctypes.c_void_p),
+        ("packed_s", ctypes.c_void_p),
+        ("x", ctypes.c_void_p),
+        ("out", ctypes.c_void_p),
+        ("argmax", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """Load libw4.so (built in-tree by __graft_entry__.build())."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                           "(hipcc --offload-arch=gfx950) first")
+    L = ctypes.CDLL(LIB_PATH)
+    i32, i64, sz, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
+    L.w4_status_string.restype = ctypes.c_char_p
+    L.w4_status_string.argtypes = [i32]
+    L.w4_last_error.restype = ctypes.c_char_p
+    L.w4_last_error.argtypes = []
+    L.w4_abi_version.restype = i32
+    L.w4_abi_version.argtypes = []
+    L.w4_packed_size.restype = i32
+    L.w4_packed_size.argtypes = [i64, i64, i32, i32, ctypes.POINTER(sz), ctypes.POINTER(sz)]
+    L.w4_pack.restype = i32
+    L.w4_pack.argtypes = [vp, vp, i64, i64, i32, i32, vp, sz, vp, sz]
+    L.w4_gemv_workspace_size.restype = i32
+    L.w4_gemv_workspace_size.argtypes = [i64, i64, i32, i32, ctypes.POINTER(sz)]
+    L.w4_gemv.restype = i32
+    L.w4_gemv.argtypes = [vp, vp, vp, vp, vp, vp, sz, i64, i64, i32, vp]
+    L.w4_gemv_gateup_silu.restype = i32
+    L.w4_gemv_gateup_silu.argtypes = [vp, vp, vp, vp, i64, i64, i32, vp]
+    L.w4_decode_linear_sweep_create.restype = i32
+    L.w4_decode_linear_sweep_create.argtypes = [ctypes.POINTER(ProjDesc), i32, i32,
+                                                ctypes.POINTER(vp)]
+    L.w4_decode_linear_sweep.restype = i32
+    L.w4_decode_linear_sweep.argtypes = [vp, vp]
+    L.w4_decode_linear_sweep_destroy.restype = i32
+    L.w4_decode_linear_sweep_destroy.argtypes = [vp]
+    _lib = L
+    return L
+
+
+def _check(status: int, where: str):
+    if status != OK:
+        detail = lib().w4_last_error().decode(errors="replace")
+        raise W4Error(status, where, detail)
+
+
+def status_string(status: int) -> str:
+    return lib().w4_status_string(status).decode()
+
+
+def last_error() -> str:
+    return lib().w4_last_error().decode(errors="replace")
+
+
+def _layout(layout) -> int:
+    if layout in ("plain", LAYOUT_PLAIN):
+        return LAYOUT_PLAIN
+    if layout in ("gateup", LAYOUT_GATEUP):
+        return LAYOUT_GATEUP
+    return int(layout)
+
+
+def packed_size(n: int, k: int, group: int, layout="plain") -> tuple[int, int]:
+    wb, sb = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().w4_packed_size(n, k, group, _layout(layout), ctypes.byref(wb), ctypes.byref(sb)),
+           "w4_packed_size")
+    return wb.value, sb.value
+
+
+def pack(q: np.ndarray, scales_bits: np.ndarray, group: int, layout="plain"):
+    """Host packer: q uint8 [n, k] (values 0..15), scales fp16 bits uint16
+    [n, k/group] -> (packed_w, packed_s) as uint8 numpy arrays."""
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    scales_bits = np.ascontiguousarray(scales_bits, dtype=np.uint16)
+    if q.ndim != 2:
+        raise ValueError("q must be 2-D [n, k]")
+    n, k = q.shape
+    if scales_bits.shape != (n, k // group if group else 0):
+        raise ValueError(f"scales must be [{n}, {k}//{group}], got {scales_bits.shape}")
+    wb, sb = packed_size(n, k, group, layout)
+    pw = np.empty(wb, np.uint8)
+    ps = np.empty(sb, np.uint8)
+    _check(lib().w4_pack(q.ctypes.data, scales_bits.ctypes.data, n, k, group, _layout(layout),
+                         pw.ctypes.data, wb, ps.ctypes.data, sb), "w4_pack")
+    return pw, ps
+
+
+def gemv_workspace_size(n: int, k: int, group: int, with_argmax: bool) -> int:
+    out = ctypes.c_size_t()
+    _check(lib().w4_gemv_workspace_size(n, k, group, int(bool(with_argmax)), ctypes.byref(out)),
+           "w4_gemv_workspace_size")
+    return out.value
+
+
+def _dev_ptr(t, name: str, dtype=None, numel: Optional[int] = None) -> int:
+    if t is None:
+        return 0
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} has {t.numel()} elements, needs {numel}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def gemv(packed_w, packed_s, x, y, n: int, k: int, group: int, argmax=None, workspace=None,
+         stream=None):
+    """y[n] (fp32) = W x; with `argmax` (int32 [1]) and `workspace` (zero-filled
+    uint8, gemv_workspace_size bytes) also the lowest-index argmax of y."""
+    import torch
+    wb, sb = packed_size(n, k, group, "plain")
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if argmax is not None and ws_bytes < gemv_workspace_size(n, k, group, True):
+        raise ValueError("workspace too small for the argmax epilogue")
+    _check(lib().w4_gemv(_dev_ptr(packed_w, "packed_w", torch.uint8, wb),
+                         _dev_ptr(packed_s, "packed_s", torch.uint8, sb),
+                         _dev_ptr(x, "x", torch.float16, k),
+                         _dev_ptr(y, "y", torch.float32, n),
+                         _dev_ptr(argmax, "argmax", torch.int32, 1),
+                         _dev_ptr(workspace, "workspace"), ws_bytes, n, k, group,
+                         _stream(stream)), "w4_gemv")
+
+
+def gemv_gateup_silu(packed_w, packed_s, x, h, n_total: int, k: int, group: int, stream=None):
+    """h[n_total/2] (fp16) = silu(gate) * up for a gate/up-layout matrix."""
+    import torch
+    wb, sb = packed_size(n_total, k, group, "gateup")
+    _check(lib().w4_gemv_gateup_silu(_dev_ptr(packed_w, "packed_w", torch.uint8, wb),
+                                     _dev_ptr(packed_s, "packed_s", torch.uint8, sb),
+                                     _dev_ptr(x, "x", torch.float16, k),
+                                     _dev_ptr(h, "h", torch.float16, n_total // 2),
+                                     n_total, k, group, _stream(stream)), "w4_gemv_gateup_silu")
+
+
+@dataclass
+class Proj:
+    """One projection of a sweep (device tensors are kept alive by the Sweep)."""
+    kind: int
+    n: int
+    k: int
+    group: int
+    packed_w: object
+    packed_s: object
+    x: object
+    out: object
+    argmax: object = None
+    workspace: object = None
+
+
+class Sweep:
+    """Per-token linear sweep: eager launches or one captured HIP graph."""
+
+    def __init__(self, projs: Sequence[Proj], use_graph: bool = True):
+        import torch
+        self._projs = list(projs)  # keep device buffers alive while the graph exists
+        arr = (ProjDesc * len(self._projs))()
+        for i, p in enumerate(self._projs):
+            d = arr[i]
+            d.kind = p.kind
+            d.group = p.group
+            d.n = p.n
+            d.k = p.k
+            wb, sb = packed_size(p.n, p.k, p.group,
+                                 "gateup" if p.kind == PROJ_GATEUP_SILU else "plain")
+            d.packed_w = _dev_ptr(p.packed_w, "packed_w", torch.uint8, wb)
+            d.packed_s = _dev_ptr(p.packed_s, "packed_s", torch.uint8, sb)
+            d.x = _dev_ptr(p.x, "x", torch.float16, p.k)
+            if p.kind == PROJ_GATEUP_SILU:
+                d.out = _dev_ptr(p.out, "out", torch.float16, p.n // 2)
+            else:
+                d.out = _dev_ptr(p.out, "out", torch.float32, p.n)
+            d.argmax = _dev_ptr(p.argmax, "argmax", torch.int32, 1)
+            d.workspace = _dev_ptr(p.workspace, "workspace")
+            d.workspace_bytes = (p.workspace.numel() * p.workspace.element_size()
+                                 if p.workspace is not None else 0)
+        handle = ctypes.c_void_p()
+        _check(lib().w4_decode_linear_sweep_create(arr, len(self._projs), int(bool(use_graph)),
+                                                   ctypes.byref(handle)),
+               "w4_decode_linear_sweep_create")
+        self._handle = handle
+        self.use_graph = use_graph
+
+    def run(self, stream=None):
+        if not self._handle:
+            raise RuntimeError("sweep destroyed")
+        _check(lib().w4_decode_linear_sweep(self._handle, _stream(stream)), "w4_decode_linear_sweep")
+
+    def close(self):
+        if self._handle:
+            _check(lib().w4_decode_linear_sweep_destroy(self._handle), "w4_decode_linear_sweep_destroy")
+            self._handle = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -20,3 +20,13 @@ def pytest_collection_modifyitems(config, items):
     # GPU tests print the case they run before touching the device, so a
     # crash report names it; nothing to reorder here.
     pass
+
+
+@pytest.fixture(autouse=True)
+def _announce_gpu_case(request):
+    """Name each GPU case on the real stderr before it touches the device, so
+    that a run that ends abruptly still says which case was running."""
+    if request.node.get_closest_marker("gpu") is not None:
+        sys.__stderr__.write(f"\n[gpu-case] {request.node.nodeid}\n")
+        sys.__stderr__.flush()
+    yield

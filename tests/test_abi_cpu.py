@@ -1,0 +1,182 @@
+"""C-ABI checks that need no GPU: the library loads and exports every symbol
+include/w4.h declares, the host packer is bit-exact against the oracle's
+packer (integer/byte work: bit-exact is the bar), and argument validation
+rejects bad calls before anything is launched."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import synthetic
+from int4_weight_only_04_amd import w4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(w4_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_exactly_the_exports():
+    assert _declared_functions() == sorted(w4.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = w4.lib()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    assert lib.w4_abi_version() == 1
+
+
+def test_status_strings():
+    names = ["W4_OK", "W4_EINVAL", "W4_ESHAPE", "W4_EALIGN", "W4_EHIP", "W4_ENOMEM", "W4_ECAPTURE"]
+    for code, name in enumerate(names):
+        assert w4.status_string(code) == name
+    assert w4.status_string(99) == "W4_UNKNOWN"
+
+
+PACK_CASES = [
+    # (n, k, group, layout)
+    (1, 8, 8, "plain"), (3, 32, 32, "plain"), (5, 64, 32, "plain"), (7, 72, 8, "plain"),
+    (130, 1032, 8, "plain"), (512, 256, 64, "plain"), (65, 4104, 8, "plain"),
+    (2, 64, 32, "gateup"), (6, 128, 64, "gateup"), (10, 256, 128, "gateup"),
+    (14, 96, 32, "gateup"), (64, 384, 128, "gateup"),
+]
+
+
+@pytest.mark.parametrize("n,k,group,layout", PACK_CASES)
+def test_packer_bit_exact_vs_oracle(n, k, group, layout):
+    q, s, _ = synthetic.logical(100 + n + k, n, k, group)
+    pw, ps = w4.pack(q, s, group, layout)
+    opw, ops = oracle.pack(q, s, group, layout == "gateup")
+    assert np.array_equal(pw, opw)
+    assert np.array_equal(ps, ops)
+    assert w4.packed_size(n, k, group, layout) == oracle.packed_sizes(n, k, group, layout == "gateup")
+
+
+def test_packer_golden_bytes():
+    import oracle_pins
+    g = oracle_pins.load_golden()
+    q, s = oracle_pins.golden_logical()
+    pw, ps = w4.pack(q, s, g["group"], "plain")
+    assert np.array_equal(pw, g["plain_pw"]) and np.array_equal(ps, g["plain_ps"])
+    pw, ps = w4.pack(q, s, g["group"], "gateup")
+    assert np.array_equal(pw, g["gateup_pw"]) and np.array_equal(ps, g["gateup_ps"])
+
+
+@pytest.mark.parametrize("cfg", [synthetic.CONFIG_DOWN, synthetic.CONFIG_GATEUP],
+                         ids=["down", "gateup"])
+def test_packer_full_size_bit_exact(cfg):
+    q, s, _ = synthetic.logical(cfg["seed"], cfg["n"], cfg["k"], cfg["group"], cfg["s_lo"], cfg["s_hi"])
+    layout = "gateup" if cfg["kind"] == "gateup" else "plain"
+    pw, ps = w4.pack(q, s, cfg["group"], layout)
+    opw, ops = oracle.pack(q, s, cfg["group"], layout == "gateup")
+    assert np.array_equal(pw, opw) and np.array_equal(ps, ops)
+
+
+def test_pack_rejects_bad_nibble():
+    q = np.zeros((4, 32), np.uint8)
+    q[2, 17] = 16
+    s = np.zeros((4, 1), np.uint16)
+    with pytest.raises(w4.W4Error) as ei:
+        w4.pack(q, s, 32)
+    assert ei.value.status == w4.EINVAL
+    assert "q[2][17] = 16" in str(ei.value)
+
+
+@pytest.mark.parametrize("n,k,group,layout,status", [
+    (0, 64, 32, "plain", w4.ESHAPE),
+    (4, 4, 8, "plain", w4.ESHAPE),
+    (4, 64, 48, "plain", w4.ESHAPE),      # group not a power of two
+    (4, 64, 4, "plain", w4.ESHAPE),       # group < 8
+    (4, 96, 64, "plain", w4.ESHAPE),      # k % group != 0
+    (4, 64, 128, "plain", w4.ESHAPE),     # group > k
+    (4, 65536, 128, "plain", w4.ESHAPE),  # k above the LDS staging limit
+    (5, 64, 32, "gateup", w4.ESHAPE),     # odd n_total
+    (4, 64, 32, 7, w4.EINVAL),            # unknown layout
+])
+def test_packed_size_validation(n, k, group, layout, status):
+    with pytest.raises(w4.W4Error) as ei:
+        w4.packed_size(n, k, group, layout)
+    assert ei.value.status == status
+    assert w4.last_error()
+
+
+def test_pack_rejects_wrong_buffer_sizes():
+    L = w4.lib()
+    q = np.zeros((4, 32), np.uint8)
+    s = np.zeros((4, 1), np.uint16)
+    pw = np.zeros(64, np.uint8)
+    ps = np.zeros(8, np.uint8)
+    st = L.w4_pack(q.ctypes.data, s.ctypes.data, 4, 32, 32, 0, pw.ctypes.data, 63, ps.ctypes.data, 8)
+    assert st == w4.EINVAL and "buffer sizes" in w4.last_error()
+    st = L.w4_pack(None, s.ctypes.data, 4, 32, 32, 0, pw.ctypes.data, 64, ps.ctypes.data, 8)
+    assert st == w4.EINVAL
+
+
+def test_workspace_sizes():
+    assert w4.gemv_workspace_size(152064, 3584, 128, False) == 0
+    ws = w4.gemv_workspace_size(152064, 3584, 128, True)
+    assert 0 < ws <= 1 << 20
+
+
+def test_gemv_validation_before_launch():
+    """Calls that fail validation never reach the device (safe without a GPU)."""
+    L = w4.lib()
+    A = 1 << 20  # 16-byte aligned fake addresses: only used where validation must fail first
+    # null pointers
+    assert L.w4_gemv(None, A, A, A, None, None, 0, 4, 64, 32, None) == w4.EINVAL
+    assert L.w4_gemv(A, A, A, None, None, None, 0, 4, 64, 32, None) == w4.EINVAL
+    # misalignment
+    assert L.w4_gemv(A + 4, A, A, A, None, None, 0, 4, 64, 32, None) == w4.EALIGN
+    assert L.w4_gemv(A, A + 8, A, A, None, None, 0, 4, 64, 32, None) == w4.EALIGN
+    assert L.w4_gemv(A, A, A + 2, A, None, None, 0, 4, 64, 32, None) == w4.EALIGN
+    # shapes
+    assert L.w4_gemv(A, A, A, A, None, None, 0, 0, 64, 32, None) == w4.ESHAPE
+    assert L.w4_gemv(A, A, A, A, None, None, 0, 4, 96, 64, None) == w4.ESHAPE
+    # argmax without workspace / too small workspace
+    assert L.w4_gemv(A, A, A, A, A, None, 0, 4, 64, 32, None) == w4.EINVAL
+    assert L.w4_gemv(A, A, A, A, A, A, 16, 4, 64, 32, None) == w4.EINVAL
+    assert L.w4_gemv(A, A, A, A, A, A + 8, 1 << 20, 4, 64, 32, None) == w4.EALIGN
+    # gate/up: odd n_total
+    assert L.w4_gemv_gateup_silu(A, A, A, A, 5, 64, 32, None) == w4.ESHAPE
+    assert L.w4_gemv_gateup_silu(A, None, A, A, 6, 64, 32, None) == w4.EINVAL
+
+
+def test_sweep_create_validation():
+    L = w4.lib()
+    A = 1 << 20
+    handle = ctypes.c_void_p()
+    assert L.w4_decode_linear_sweep_create(None, 0, 1, ctypes.byref(handle)) == w4.EINVAL
+    descs = (w4.ProjDesc * 2)()
+    for d in descs:
+        d.kind, d.group, d.n, d.k = w4.PROJ_PLAIN, 32, 4, 64
+        d.packed_w = d.packed_s = d.x = d.out = A
+    descs[1].kind = 9
+    assert L.w4_decode_linear_sweep_create(descs, 2, 1, ctypes.byref(handle)) == w4.EINVAL
+    assert "projection 1" in w4.last_error()
+    descs[1].kind = w4.PROJ_LMHEAD_ARGMAX  # no workspace
+    assert L.w4_decode_linear_sweep_create(descs, 2, 0, ctypes.byref(handle)) == w4.EINVAL
+    descs[1].kind = w4.PROJ_GATEUP_SILU
+    descs[1].n = 7
+    assert L.w4_decode_linear_sweep_create(descs, 2, 0, ctypes.byref(handle)) == w4.ESHAPE
+    assert not handle.value
+    assert L.w4_decode_linear_sweep_destroy(None) == w4.OK
+    assert L.w4_decode_linear_sweep(None, None) == w4.EINVAL
+
+
+def test_launch_without_device_reports_hip_error():
+    """With no GPU present, a validated call fails with W4_EHIP (no launch)."""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present; this case only runs where no device exists")
+    L = w4.lib()
+    A = 1 << 20
+    st = L.w4_gemv(A, A, A, A, None, None, 0, 4, 64, 32, None)
+    assert st == w4.EHIP, w4.last_error()
