@@ -50,8 +50,8 @@
  *   - Size: weight bytes = tiles * k / 2 * 4, scale bytes = tiles * (k/G) * 8.
  *
  * Shape rules (W4_ESHAPE otherwise): n >= 1; k >= 8; G a power of two with
- * 8 <= G <= k and k % G == 0; k <= 32768 (x is staged whole in LDS);
- * gate/up: n even.  Device pointers must be 16-byte aligned (W4_EALIGN).
+ * 8 <= G <= k and k % G == 0; k <= 32768; gate/up: n even; argmax: n below
+ * 2^31 - 1.  Device pointers must be 16-byte aligned (W4_EALIGN).
  */
 #ifndef W4_H
 #define W4_H
@@ -109,8 +109,9 @@ w4_status w4_pack(const uint8_t* q, const uint16_t* scales, int64_t n, int64_t k
                   size_t packed_s_bytes);
 
 /*
- * Workspace bytes w4_gemv needs: 0 without argmax, a small fixed size with
- * argmax.  Host only.
+ * Workspace bytes w4_gemv needs: 0 without argmax; with argmax, 8 bytes per
+ * workgroup of the shape's launch (about 152 KiB for 152064 x 3584).  Host
+ * only.
  */
 w4_status w4_gemv_workspace_size(int64_t n, int64_t k, int32_t group, int32_t with_argmax,
                                  size_t* bytes);
@@ -118,16 +119,15 @@ w4_status w4_gemv_workspace_size(int64_t n, int64_t k, int32_t group, int32_t wi
 /*
  * y = W x for a plain-layout packed matrix, optionally with the lm_head argmax
  * epilogue (lowest index of the largest y; NaN never wins; -1 if every y is
- * NaN).  Device, asynchronous on `stream`.
+ * NaN).  Device, asynchronous on `stream`; with argmax a second, one-workgroup
+ * kernel on the same stream reduces the per-workgroup partials.
  *   packed_w, packed_s  device, from w4_pack(..., W4_LAYOUT_PLAIN, ...);
  *   x        device, fp16 [k];
  *   y        device, fp32 [n] (written for every row);
  *   argmax   device int32 [1], or NULL for no argmax;
  *   workspace device, >= w4_gemv_workspace_size bytes when argmax != NULL
- *            (may be NULL otherwise).  It must be zero-filled once before its
- *            first use; every completed call leaves it zero-filled again, so it
- *            can be reused and replayed without clearing.  Calls that may run
- *            at the same time need separate workspaces.
+ *            (may be NULL otherwise); no initial contents are needed.  Calls
+ *            that may run at the same time need separate workspaces.
  */
 w4_status w4_gemv(const void* packed_w, const void* packed_s, const uint16_t* x, float* y,
                   int32_t* argmax, void* workspace, size_t workspace_bytes, int64_t n, int64_t k,
@@ -158,7 +158,7 @@ typedef struct w4_proj_desc {
     const uint16_t* x;     /* device fp16 [k]                                */
     void* out;             /* device float [n] or fp16 [n/2]                 */
     int32_t* argmax;       /* device int32 [1] (LMHEAD_ARGMAX only)          */
-    void* workspace;       /* device (LMHEAD_ARGMAX only), zero-filled once  */
+    void* workspace;       /* device (LMHEAD_ARGMAX only)                    */
     size_t workspace_bytes;
 } w4_proj_desc;
 
@@ -178,7 +178,8 @@ typedef struct w4_sweep w4_sweep;
 w4_status w4_decode_linear_sweep_create(const w4_proj_desc* projs, int32_t count,
                                         int32_t use_graph, w4_sweep** out);
 
-/* Run one token's sweep on `stream` (graph launch or eager launches). */
+/* Run one token's sweep on `stream` (graph launch or eager launches).  The
+ * lm_head projection contributes two kernels (GEMV + argmax finalize). */
 w4_status w4_decode_linear_sweep(w4_sweep* sweep, void* stream);
 
 /* Release the handle (NULL is accepted). */

@@ -174,7 +174,12 @@ w4_status w4_gemv_workspace_size(int64_t n, int64_t k, int32_t group, int32_t wi
         if (!bytes) return fail(W4_EINVAL, "w4_gemv_workspace_size: null output");
         w4_status st = check_shape(n, k, group, false, "w4_gemv_workspace_size");
         if (st != W4_OK) return st;
-        *bytes = with_argmax ? kArgmaxWorkspaceBytes : 0;
+        GemvCall c{};
+        c.n = n;
+        c.k = k;
+        c.group = group;
+        c.epi = kEpiArgmax;
+        *bytes = with_argmax ? argmax_workspace_bytes(launch_grid(c)) : 0;
         return ok();
     } catch (...) {
         return fail(W4_EINVAL, "w4_gemv_workspace_size: internal exception");
@@ -190,9 +195,9 @@ w4_status w4_gemv(const void* packed_w, const void* packed_s, const uint16_t* x,
                    argmax ? kEpiArgmax : kEpiPlain};
         w4_status st = validate_gemv(c, "w4_gemv");
         if (st != W4_OK) return st;
-        if (argmax && workspace_bytes < kArgmaxWorkspaceBytes)
+        if (argmax && workspace_bytes < argmax_workspace_bytes(launch_grid(c)))
             return fail(W4_EINVAL, "w4_gemv: workspace of %zu bytes, need %zu", workspace_bytes,
-                        kArgmaxWorkspaceBytes);
+                        argmax_workspace_bytes(launch_grid(c)));
         hipError_t err = launch_gemv(c, static_cast<hipStream_t>(stream));
         if (err != hipSuccess) return hip_fail(err, "w4_gemv launch");
         return ok();
@@ -241,9 +246,9 @@ w4_status desc_to_call(const w4_proj_desc& d, int32_t idx, GemvCall* out)
     snprintf(who, sizeof who, "sweep projection %d", idx);
     w4_status st = validate_gemv(*out, who);
     if (st != W4_OK) return st;
-    if (epi == kEpiArgmax && d.workspace_bytes < kArgmaxWorkspaceBytes)
+    if (epi == kEpiArgmax && d.workspace_bytes < argmax_workspace_bytes(launch_grid(*out)))
         return fail(W4_EINVAL, "%s: workspace of %zu bytes, need %zu", who, d.workspace_bytes,
-                    kArgmaxWorkspaceBytes);
+                    argmax_workspace_bytes(launch_grid(*out)));
     return W4_OK;
 }
 
@@ -288,14 +293,6 @@ w4_status w4_decode_linear_sweep_create(const w4_proj_desc* projs, int32_t count
             if (err != hipSuccess) {
                 delete sw;
                 return hip_fail(err, "hipStreamCreateWithFlags");
-            }
-            // Resolve per-kernel residency (host queries) before capture.
-            for (size_t i = 0; i < sw->calls.size() && err == hipSuccess; ++i)
-                err = prepare_gemv(sw->calls[i]);
-            if (err != hipSuccess) {
-                hipStreamDestroy(cap);
-                delete sw;
-                return hip_fail(err, "device query before capture");
             }
             err = hipStreamBeginCapture(cap, hipStreamCaptureModeThreadLocal);
             if (err != hipSuccess) {

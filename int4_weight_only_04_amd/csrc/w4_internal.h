@@ -11,10 +11,7 @@ namespace w4i {
 constexpr int kTileRows = 4;          // rows per packed tile (W4T4 layout)
 constexpr int kBlockThreads = 256;    // 4 waves of 64 lanes
 constexpr int kWavesPerBlock = kBlockThreads / 64;
-constexpr int64_t kMaxK = 32768;      // x[k] is staged whole in LDS (64 KiB)
-constexpr int kArgmaxMaxBlocks = 4096;
-constexpr size_t kArgmaxHeaderBytes = 256;  // counter lives here
-constexpr size_t kArgmaxWorkspaceBytes = kArgmaxHeaderBytes + 8 * (size_t)kArgmaxMaxBlocks;
+constexpr int64_t kMaxK = 32768;      // bound on k (int32 block arithmetic)
 
 enum Epilogue : int32_t {
     kEpiPlain = 0,   // y fp32
@@ -35,11 +32,55 @@ struct GemvCall {
     int32_t epi;
 };
 
-// Launch one GEMV on `stream` (shape already validated by the caller).
+// Launch one GEMV on `stream` (shape already validated by the caller); the
+// argmax epilogue adds a one-workgroup finalize kernel on the same stream.
 hipError_t launch_gemv(const GemvCall& call, hipStream_t stream);
 
-// Resolve the launch's device queries (residency) ahead of a graph capture.
-hipError_t prepare_gemv(const GemvCall& call);
+// Workgroups of the main kernel for this call (only n, k, group, epi used).
+int64_t launch_grid(const GemvCall& call);
+
+// Launch shape: SPLIT waves share one unit (k split inside the workgroup),
+// each loading DEPTH k iterations per round before computing.  Chosen from
+// measurements on MI355X at the decode-step shapes: enough waves to cover
+// 256 CUs (split-k for the projections with few rows or long k) and, where
+// registers allow, a wave's whole k range in one round.
+struct LaunchConfig {
+    int split;
+    int depth;
+};
+
+inline LaunchConfig choose_config(int32_t epi, int64_t units, int32_t iters)
+{
+    int split;
+    if (epi == kEpiGateUp || units >= 8192)
+        split = 2;
+    else if (iters > 8)
+        split = 8;
+    else
+        split = 4;
+    while (split > 1 && split > iters) split >>= 1;
+    const int per_wave = (iters + split - 1) / split;
+    int depth;
+    if (per_wave <= 2)
+        depth = 2;
+    else if (split == 8)
+        depth = per_wave <= 5 ? 5 : 8;
+    else
+        depth = per_wave <= 4 ? 4 : 8;
+    return LaunchConfig{split, depth};
+}
+
+// Argmax workspace: per-workgroup best values (fp32), then, from a 256-byte
+// aligned offset, the matching rows (int32).
+inline size_t argmax_index_offset(int64_t grid)
+{
+    return ((size_t)grid * 4 + 255) & ~(size_t)255;
+}
+
+inline size_t argmax_workspace_bytes(int64_t grid)
+{
+    return argmax_index_offset(grid) + (size_t)grid * 4;
+}
 
 // Number of W4T4 tiles of an n-row matrix in the given epilogue's layout.
 inline int64_t tiles_for(int64_t n, bool gateup)

@@ -10,35 +10,40 @@
 // Design (one GEMV is a pure HBM stream: 0.52 bytes per weight against 2
 // flops, far below the chip's ridge point, so the kernel is shaped for
 // bandwidth, not for MFMA):
-//   * A wave owns one "unit" at a time: one W4T4 tile of 4 rows (plain,
-//     argmax) or the gate tile and the matching up tile (gate/up, 8 rows).
-//     Its 64 lanes stride along k in 8-input blocks, so every weight load is a
-//     16-byte global load and a wave instruction reads 1 KiB of contiguous
-//     packed weights per tile.
+//   * A "unit" is one W4T4 tile of 4 rows (plain, argmax) or a gate tile and
+//     the matching up tile (gate/up, 8 rows).  SPLIT waves of a workgroup
+//     share a unit, each taking a contiguous range of its k iterations; a
+//     k iteration is 64 lanes x one 8-input block, so every weight load is a
+//     16-byte load and a wave instruction reads 1 KiB of contiguous packed
+//     weights per tile.  The partial sums of the SPLIT waves meet in LDS and
+//     are added in wave order, so results do not depend on scheduling.
+//   * Each wave issues all its loads for a round (D iterations: weights,
+//     group scales and the 16 bytes of x its lane needs) before any math, so
+//     a unit's whole k range is in flight at once.  x is read through the
+//     L1/L2 caches (it is shared by every workgroup and small).
 //   * The 16 bytes a lane loads are the same 8 inputs of the tile's 4 rows,
-//     so one 16-byte LDS read of x serves 4 (or 8) rows.  x is staged once per
-//     workgroup in LDS; the grid is sized to the resident capacity and waves
-//     walk units with a grid stride, so the staging is amortised.
+//     so one 16-byte read of x serves 4 (or 8) rows.
 //   * Unpacking costs 5 integer ops per 8 nibbles (masks 0x000F000F /
 //     0x00F000F0 OR-ed into the fraction of fp16 1024.0, before and after a
 //     shift by 8), 4 packed-fp16 ops to remove the bias exactly (1024+q-1032
 //     and (1024+16q)/16-72 are both exactly q-8), and 4 v_dot2_f32_f16 whose
-//     products are exact in fp32.  One fma per row and block applies the
-//     group scale.  This is the gfx950 counterpart of the pages' lesson that
-//     a byte-permute unpack beat an integer dot product for these shapes
-//     ("Technical Details" bullet 4): keep the per-weight instruction count
-//     low, stay in floating point for the activations.
+//     products are exact in fp32; one mixed-precision fma per row and block
+//     applies the group scale.  This is the gfx950 counterpart of the pages'
+//     lesson that a byte-permute unpack beat an integer dot product for these
+//     shapes ("Technical Details" bullet 4): keep the per-weight instruction
+//     count low and stay in floating point for the activations.
 //   * Per-row sums are reduced across the wave with DPP row operations and
-//     four lane reads; no LDS is used for the reduction.
-//   * Tail rows are masked, never returned early: every wave reaches every
-//     barrier (the pages' warp-specialisation bug, "Technical Details"
-//     bullet 4, was a barrier inside a divergent branch).
+//     four lane reads.
+//   * Every wave of a workgroup reaches each barrier; tail units and lanes
+//     are masked, never returned early before one (the pages'
+//     warp-specialisation bug, "Technical Details" bullet 4, was a barrier
+//     inside a divergent branch).
+//   * lm_head argmax: each workgroup writes its best (value, row) to the
+//     workspace with plain stores and a one-workgroup second kernel reduces
+//     them in index order.  The kernel boundary orders the two, so there are
+//     no device-scope fences or atomics on the hot path.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
-
-#include <map>
-#include <mutex>
-#include <tuple>
 
 #include "w4_internal.h"
 
@@ -47,21 +52,20 @@ namespace {
 
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kDepth = 8;  // 16-byte weight loads in flight per lane and tile
-
 struct KernelArgs {
     const uint4* pw;
     const uint2* ps;
     const uint4* x;
     void* out;
-    int32_t* argmax;
-    uint8_t* ws;
+    float* part_v;       // argmax: per-workgroup best value
+    int32_t* part_i;     // argmax: per-workgroup best row
     int64_t n;           // logical rows (gate/up: 2I)
-    int64_t units;       // wave units
+    int64_t units;       // units (tiles, or gate/up tile pairs)
     int64_t tiles_half;  // gate/up: tiles per half
     int32_t kb;          // k / 8
     int32_t ng;          // k / G
     int32_t gshift;      // log2(G / 8)
+    int32_t iters;       // ceil(kb / 64)
 };
 
 __device__ __forceinline__ h2_t as_h2(uint32_t v) { return __builtin_bit_cast(h2_t, v); }
@@ -73,6 +77,16 @@ __device__ __forceinline__ uint32_t opaque_magic()
 {
     uint32_t r;
     asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(r));
+    return r;
+}
+
+// fp32 dot product of two fp16 pairs started from zero: one VOP3P
+// v_dot2_f32_f16 with an inline-constant accumulator (the builtin with a 0.0
+// accumulator compiles to a register move plus v_dot2c).
+__device__ __forceinline__ float dot2_first(h2_t a, h2_t b)
+{
+    float r;
+    asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
     return r;
 }
 
@@ -91,7 +105,7 @@ __device__ __forceinline__ float dot8(uint32_t d, const uint4& xv, uint32_t magi
     const h2_t vb = __builtin_elementwise_fma(as_h2(b), sixteenth, bias16);
     const h2_t vc = as_h2(c) + bias;
     const h2_t ve = __builtin_elementwise_fma(as_h2(e), sixteenth, bias16);
-    float p = __builtin_amdgcn_fdot2(va, as_h2(xv.x), 0.0f, false);
+    float p = dot2_first(va, as_h2(xv.x));
     p = __builtin_amdgcn_fdot2(vb, as_h2(xv.y), p, false);
     p = __builtin_amdgcn_fdot2(vc, as_h2(xv.z), p, false);
     p = __builtin_amdgcn_fdot2(ve, as_h2(xv.w), p, false);
@@ -130,24 +144,36 @@ __device__ __forceinline__ bool better(float v, int32_t i, float bv, int32_t bi)
     return v > bv || (v == bv && i < bi);
 }
 
-template <int U, int EPI>
-__global__ void __launch_bounds__(kBlockThreads) gemv_w4_kernel(KernelArgs a)
+constexpr int waves_for(int split) { return split < 4 ? 4 : split; }
+
+// U tiles per unit, epilogue EPI, SPLIT waves per unit, D iterations per load
+// round, FULL: k/8 is a multiple of 64 (no lane masking).
+template <int U, int EPI, int SPLIT, int D, bool FULL>
+__global__ void __launch_bounds__(waves_for(SPLIT) * 64) gemv_w4_kernel(KernelArgs a)
 {
-    extern __shared__ uint4 xs[];
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
+    constexpr int WAVES = waves_for(SPLIT);
+    constexpr int SLOTS = WAVES / SPLIT;
+    __shared__ float red[SLOTS][SPLIT][U * 4];
+    __shared__ float best_v_s[SLOTS];
+    __shared__ int32_t best_i_s[SLOTS];
 
-    for (int i = tid; i < a.kb; i += kBlockThreads) xs[i] = a.x[i];
-    __syncthreads();
-
-    const int iters = (a.kb + 63) >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int slot = wave / SPLIT;
+    const int sub = wave % SPLIT;
     const uint32_t magic = opaque_magic();
-    float best_v = -__builtin_inff();
-    int32_t best_i = INT32_MAX;
+    const int64_t unit = (int64_t)blockIdx.x * SLOTS + slot;
+    const bool live = unit < a.units;
+    const int it0 = sub * a.iters / SPLIT;
+    const int it1 = (sub + 1) * a.iters / SPLIT;
 
-    for (int64_t unit = (int64_t)blockIdx.x * kWavesPerBlock + wave; unit < a.units;
-         unit += (int64_t)gridDim.x * kWavesPerBlock) {
+    float acc[U][4];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[u][r] = 0.0f;
+
+    if (live) {
         const uint4* wp[U];
         const uint2* sp[U];
 #pragma unroll
@@ -156,228 +182,243 @@ __global__ void __launch_bounds__(kBlockThreads) gemv_w4_kernel(KernelArgs a)
             wp[u] = a.pw + tile * a.kb;
             sp[u] = a.ps + tile * a.ng;
         }
-        float acc[U][4];
+        for (int i0 = it0; i0 < it1; i0 += D) {
+            uint4 w[D][U];
+            uint2 s[D][U];
+            uint4 xr[D];
 #pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[u][r] = 0.0f;
-
-        for (int i0 = 0; i0 < iters; i0 += kDepth) {
-            uint4 w[kDepth][U];
-            uint2 s[kDepth][U];
-#pragma unroll
-            for (int d = 0; d < kDepth; ++d) {
+            for (int d = 0; d < D; ++d) {
                 const int j = (i0 + d) * 64 + lane;
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    if (j < a.kb) {
-                        w[d][u] = wp[u][j];
-                        s[d][u] = sp[u][j >> a.gshift];
-                    } else {
-                        w[d][u] = make_uint4(0, 0, 0, 0);
-                        s[d][u] = make_uint2(0, 0);
-                    }
-                }
-            }
-#pragma unroll
-            for (int d = 0; d < kDepth; ++d) {
-                const int j = (i0 + d) * 64 + lane;
-                if (j < a.kb) {
-                    const uint4 xv = xs[j];
+                if ((i0 + d < it1) && (FULL || j < a.kb)) {
 #pragma unroll
                     for (int u = 0; u < U; ++u) {
-                        acc[u][0] = __builtin_fmaf(dot8(w[d][u].x, xv, magic), half_lo(s[d][u].x), acc[u][0]);
-                        acc[u][1] = __builtin_fmaf(dot8(w[d][u].y, xv, magic), half_hi(s[d][u].x), acc[u][1]);
-                        acc[u][2] = __builtin_fmaf(dot8(w[d][u].z, xv, magic), half_lo(s[d][u].y), acc[u][2]);
-                        acc[u][3] = __builtin_fmaf(dot8(w[d][u].w, xv, magic), half_hi(s[d][u].y), acc[u][3]);
+                        w[d][u] = wp[u][j];
+                        s[d][u] = sp[u][j >> a.gshift];
+                    }
+                    xr[d] = a.x[j];
+                }
+            }
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                const int j = (i0 + d) * 64 + lane;
+                if ((i0 + d < it1) && (FULL || j < a.kb)) {
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        acc[u][0] = __builtin_fmaf(dot8(w[d][u].x, xr[d], magic), half_lo(s[d][u].x), acc[u][0]);
+                        acc[u][1] = __builtin_fmaf(dot8(w[d][u].y, xr[d], magic), half_hi(s[d][u].x), acc[u][1]);
+                        acc[u][2] = __builtin_fmaf(dot8(w[d][u].z, xr[d], magic), half_lo(s[d][u].y), acc[u][2]);
+                        acc[u][3] = __builtin_fmaf(dot8(w[d][u].w, xr[d], magic), half_hi(s[d][u].y), acc[u][3]);
                     }
                 }
             }
         }
+    }
 
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[u][r] = wave_sum(acc[u][r]);
+
+    if constexpr (SPLIT > 1) {
+        if (lane == 0) {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) red[slot][sub][u * 4 + r] = acc[u][r];
+        }
+        __syncthreads();
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[u][r] = wave_sum(acc[u][r]);
-
-        if constexpr (EPI == kEpiGateUp) {
-            const int64_t half = a.n >> 1;
-            uint16_t* h = reinterpret_cast<uint16_t*>(a.out);
-#pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int64_t j = unit * 4 + r;
-                if (j < half && lane == r) {
-                    const float g = acc[0][r];
-                    const float up = acc[1][r];
-                    const float silu = g / (1.0f + __expf(-g));
-                    const _Float16 hv = (_Float16)(silu * up);
-                    h[j] = __builtin_bit_cast(uint16_t, hv);
-                }
+                float t = red[slot][0][u * 4 + r];
+#pragma unroll
+                for (int q = 1; q < SPLIT; ++q) t += red[slot][q][u * 4 + r];
+                acc[u][r] = t;
             }
-        } else {
-            float* y = reinterpret_cast<float*>(a.out);
+    }
+    const bool owner = live && sub == 0;  // the wave that writes this unit's outputs
+
+    if constexpr (EPI == kEpiGateUp) {
+        const int64_t half = a.n >> 1;
+        uint16_t* h = reinterpret_cast<uint16_t*>(a.out);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t j = unit * 4 + r;
+            if (owner && j < half && lane == r) {
+                const float g = acc[0][r];
+                const float silu = g / (1.0f + __expf(-g));
+                const _Float16 hv = (_Float16)(silu * acc[1][r]);
+                h[j] = __builtin_bit_cast(uint16_t, hv);
+            }
+        }
+    } else {
+        float* y = reinterpret_cast<float*>(a.out);
+        float bv = -__builtin_inff();
+        int32_t bi = INT32_MAX;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int64_t row = unit * 4 + r;
-                if (row < a.n) {
-                    if (lane == r) y[row] = acc[0][r];
-                    if constexpr (EPI == kEpiArgmax) {
-                        if (better(acc[0][r], (int32_t)row, best_v, best_i)) {
-                            best_v = acc[0][r];
-                            best_i = (int32_t)row;
-                        }
+                const int64_t row = (unit * U + u) * 4 + r;
+                if (owner && row < a.n) {
+                    if (lane == r) y[row] = acc[u][r];
+                    if (EPI == kEpiArgmax && better(acc[u][r], (int32_t)row, bv, bi)) {
+                        bv = acc[u][r];
+                        bi = (int32_t)row;
                     }
                 }
             }
-        }
-    }
-
-    if constexpr (EPI == kEpiArgmax) {
-        // Deterministic two-level argmax: each block publishes its best
-        // (value, row) to the workspace; the last block to finish (counted
-        // with one device-scope atomic) reduces the partials in index order
-        // and re-arms the counter, so the workspace is reusable and the
-        // result is independent of block scheduling.
-        __shared__ float red_v[kBlockThreads];
-        __shared__ int32_t red_i[kBlockThreads];
-        __shared__ int is_last;
-        uint32_t* counter = reinterpret_cast<uint32_t*>(a.ws);
-        float* part_v = reinterpret_cast<float*>(a.ws + kArgmaxHeaderBytes);
-        int32_t* part_i = reinterpret_cast<int32_t*>(a.ws + kArgmaxHeaderBytes) + kArgmaxMaxBlocks;
-        if (lane == 0) {
-            red_v[wave] = best_v;
-            red_i[wave] = best_i;
-        }
-        __syncthreads();
-        if (tid == 0) {
-            float bv = red_v[0];
-            int32_t bi = red_i[0];
-            for (int w = 1; w < kWavesPerBlock; ++w)
-                if (better(red_v[w], red_i[w], bv, bi)) {
-                    bv = red_v[w];
-                    bi = red_i[w];
-                }
-            part_v[blockIdx.x] = bv;
-            part_i[blockIdx.x] = bi;
-            __threadfence();
-            const uint32_t done = atomicAdd(counter, 1u);
-            is_last = (done == gridDim.x - 1) ? 1 : 0;
-        }
-        __syncthreads();
-        if (is_last) {
-            __threadfence();
-            float bv = -__builtin_inff();
-            int32_t bi = INT32_MAX;
-            for (int b = tid; b < (int)gridDim.x; b += kBlockThreads) {
-                const float v = __builtin_nontemporal_load(part_v + b);
-                const int32_t i = __builtin_nontemporal_load(part_i + b);
-                if (better(v, i, bv, bi)) {
-                    bv = v;
-                    bi = i;
-                }
+        if constexpr (EPI == kEpiArgmax) {
+            if (sub == 0 && lane == 0) {
+                best_v_s[slot] = bv;
+                best_i_s[slot] = bi;
             }
-            red_v[tid] = bv;
-            red_i[tid] = bi;
             __syncthreads();
-            for (int stride = kBlockThreads / 2; stride > 0; stride >>= 1) {
-                if (tid < stride && better(red_v[tid + stride], red_i[tid + stride], red_v[tid], red_i[tid])) {
-                    red_v[tid] = red_v[tid + stride];
-                    red_i[tid] = red_i[tid + stride];
-                }
-                __syncthreads();
-            }
-            if (tid == 0) {
-                a.argmax[0] = (red_i[0] == INT32_MAX) ? -1 : red_i[0];
-                atomicExch(counter, 0u);
+            if (threadIdx.x == 0) {
+                float v = best_v_s[0];
+                int32_t i = best_i_s[0];
+#pragma unroll
+                for (int q = 1; q < SLOTS; ++q)
+                    if (better(best_v_s[q], best_i_s[q], v, i)) {
+                        v = best_v_s[q];
+                        i = best_i_s[q];
+                    }
+                a.part_v[blockIdx.x] = v;
+                a.part_i[blockIdx.x] = i;
             }
         }
     }
 }
 
-const void* kernel_for(int32_t epi)
-{
-    switch (epi) {
-        case kEpiPlain: return reinterpret_cast<const void*>(&gemv_w4_kernel<1, kEpiPlain>);
-        case kEpiArgmax: return reinterpret_cast<const void*>(&gemv_w4_kernel<1, kEpiArgmax>);
-        case kEpiGateUp: return reinterpret_cast<const void*>(&gemv_w4_kernel<2, kEpiGateUp>);
-        default: return nullptr;
-    }
-}
+constexpr int kFinalThreads = 1024;
 
-// Resident workgroups per device for a kernel and LDS size (cached).
-hipError_t resident_blocks(const void* fn, size_t lds, int* out)
+// Lowest-index maximum over the per-workgroup partials, in index order.
+__global__ void __launch_bounds__(kFinalThreads)
+argmax_finalize_kernel(const float* __restrict__ part_v, const int32_t* __restrict__ part_i, int32_t count,
+                       int32_t* __restrict__ out)
 {
-    static std::mutex mu;
-    static std::map<std::tuple<int, const void*, size_t>, int> cache;
-    int dev = 0;
-    hipError_t err = hipGetDevice(&dev);
-    if (err != hipSuccess) return err;
-    const auto key = std::make_tuple(dev, fn, lds);
-    {
-        std::lock_guard<std::mutex> lock(mu);
-        auto it = cache.find(key);
-        if (it != cache.end()) {
-            *out = it->second;
-            return hipSuccess;
+    __shared__ float sv[kFinalThreads];
+    __shared__ int32_t si[kFinalThreads];
+    const int tid = threadIdx.x;
+    float bv = -__builtin_inff();
+    int32_t bi = INT32_MAX;
+    for (int b = tid; b < count; b += kFinalThreads) {
+        const float v = part_v[b];
+        const int32_t i = part_i[b];
+        if (better(v, i, bv, bi)) {
+            bv = v;
+            bi = i;
         }
     }
-    int cus = 0, per_cu = 0;
-    err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (err != hipSuccess) return err;
-    err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kBlockThreads, lds);
-    if (err != hipSuccess) return err;
-    if (per_cu < 1) per_cu = 1;
-    const int total = cus * per_cu;
-    {
-        std::lock_guard<std::mutex> lock(mu);
-        cache[key] = total;
+    sv[tid] = bv;
+    si[tid] = bi;
+    __syncthreads();
+    for (int stride = kFinalThreads / 2; stride > 0; stride >>= 1) {
+        if (tid < stride && better(sv[tid + stride], si[tid + stride], sv[tid], si[tid])) {
+            sv[tid] = sv[tid + stride];
+            si[tid] = si[tid + stride];
+        }
+        __syncthreads();
     }
-    *out = total;
-    return hipSuccess;
+    if (tid == 0) out[0] = (si[0] == INT32_MAX) ? -1 : si[0];
 }
 
-}  // namespace
+// ----------------------------------------------------------------- launch table
 
-hipError_t prepare_gemv(const GemvCall& c)
+// Instantiated (split, depth) pairs: depth is the number of k iterations a
+// wave loads per round before computing.
+template <int U, int EPI>
+const void* pick(int split, int depth, bool full)
 {
-    const void* fn = kernel_for(c.epi);
-    if (!fn) return hipErrorInvalidValue;
-    int resident = 0;
-    return resident_blocks(fn, (size_t)(c.k / 8) * 16, &resident);
+#define W4_CASE(S, D)                                                                     \
+    if (split == S && depth == D)                                                         \
+        return full ? reinterpret_cast<const void*>(&gemv_w4_kernel<U, EPI, S, D, true>) \
+                    : reinterpret_cast<const void*>(&gemv_w4_kernel<U, EPI, S, D, false>);
+    W4_CASE(1, 2)
+    W4_CASE(1, 4)
+    W4_CASE(1, 8)
+    W4_CASE(2, 2)
+    W4_CASE(2, 4)
+    W4_CASE(2, 8)
+    W4_CASE(4, 2)
+    W4_CASE(4, 4)
+    W4_CASE(4, 8)
+    W4_CASE(8, 2)
+    W4_CASE(8, 5)
+    W4_CASE(8, 8)
+#undef W4_CASE
+    return nullptr;
 }
 
-hipError_t launch_gemv(const GemvCall& c, hipStream_t stream)
+struct Plan {
+    const void* fn;
+    int threads;
+    int64_t grid;
+    KernelArgs args;
+};
+
+Plan make_plan(const GemvCall& c)
 {
     const bool gateup = c.epi == kEpiGateUp;
-    KernelArgs a;
+    Plan p{};
+    KernelArgs& a = p.args;
     a.pw = static_cast<const uint4*>(c.pw);
     a.ps = static_cast<const uint2*>(c.ps);
     a.x = static_cast<const uint4*>(c.x);
     a.out = c.out;
-    a.argmax = c.argmax;
-    a.ws = static_cast<uint8_t*>(c.ws);
     a.n = c.n;
     a.kb = (int32_t)(c.k / 8);
     a.ng = (int32_t)(c.k / c.group);
     int gshift = 0;
     while ((8 << gshift) < c.group) ++gshift;
     a.gshift = gshift;
+    a.iters = (a.kb + 63) / 64;
     const int64_t tiles = tiles_for(c.n, gateup);
     a.tiles_half = gateup ? tiles / 2 : 0;
     a.units = gateup ? tiles / 2 : tiles;
+    const LaunchConfig cfg = choose_config(c.epi, a.units, a.iters);
+    const bool full = (a.kb % 64) == 0;
+    switch (c.epi) {
+        case kEpiPlain: p.fn = pick<1, kEpiPlain>(cfg.split, cfg.depth, full); break;
+        case kEpiArgmax: p.fn = pick<1, kEpiArgmax>(cfg.split, cfg.depth, full); break;
+        case kEpiGateUp: p.fn = pick<2, kEpiGateUp>(cfg.split, cfg.depth, full); break;
+        default: p.fn = nullptr;
+    }
+    const int waves = waves_for(cfg.split);
+    const int slots = waves / cfg.split;
+    p.threads = waves * 64;
+    p.grid = (a.units + slots - 1) / slots;
+    if (c.epi == kEpiArgmax) {
+        uint8_t* ws = static_cast<uint8_t*>(c.ws);
+        a.part_v = reinterpret_cast<float*>(ws);
+        a.part_i = reinterpret_cast<int32_t*>(ws + argmax_index_offset(p.grid));
+    }
+    return p;
+}
 
-    const void* fn = kernel_for(c.epi);
-    if (!fn) return hipErrorInvalidValue;
-    const size_t lds = (size_t)a.kb * 16;
-    int resident = 0;
-    hipError_t err = resident_blocks(fn, lds, &resident);
-    if (err != hipSuccess) return err;
-    int64_t grid = (a.units + kWavesPerBlock - 1) / kWavesPerBlock;
-    if (grid > resident) grid = resident;
-    if (c.epi == kEpiArgmax && grid > kArgmaxMaxBlocks) grid = kArgmaxMaxBlocks;
-    if (grid < 1) grid = 1;
-    void* args[] = {&a};
-    return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kBlockThreads), args, lds, stream);
+}  // namespace
+
+int64_t launch_grid(const GemvCall& c)
+{
+    return make_plan(c).grid;
+}
+
+hipError_t launch_gemv(const GemvCall& c, hipStream_t stream)
+{
+    Plan p = make_plan(c);
+    if (!p.fn) return hipErrorInvalidValue;
+    if (p.grid < 1 || p.grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+    void* args[] = {&p.args};
+    hipError_t err = hipLaunchKernel(p.fn, dim3((unsigned)p.grid), dim3(p.threads), args, 0, stream);
+    if (err != hipSuccess || c.epi != kEpiArgmax) return err;
+    const float* pv = p.args.part_v;
+    const int32_t* pi = p.args.part_i;
+    int32_t count = (int32_t)p.grid;
+    int32_t* out = c.argmax;
+    void* fargs[] = {&pv, &pi, &count, &out};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&argmax_finalize_kernel), dim3(1), dim3(kFinalThreads),
+                           fargs, 0, stream);
 }
 
 }  // namespace w4i

@@ -166,8 +166,8 @@ def _stream(stream) -> int:
 
 def gemv(packed_w, packed_s, x, y, n: int, k: int, group: int, argmax=None, workspace=None,
          stream=None):
-    """y[n] (fp32) = W x; with `argmax` (int32 [1]) and `workspace` (zero-filled
-    uint8, gemv_workspace_size bytes) also the lowest-index argmax of y."""
+    """y[n] (fp32) = W x; with `argmax` (int32 [1]) and `workspace` (uint8,
+    gemv_workspace_size bytes) also the lowest-index argmax of y."""
     import torch
     wb, sb = packed_size(n, k, group, "plain")
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0

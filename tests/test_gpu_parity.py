@@ -266,14 +266,15 @@ def test_argmax_planted_and_ties():
 
 
 def test_argmax_workspace_reuse():
-    """The workspace re-arms itself: repeated calls agree and it ends zeroed."""
+    """The workspace needs no initial contents: starting from garbage, repeated
+    calls agree bit for bit."""
     w4 = _w4()
     c = synthetic.CONFIG_LMHEAD
     n, k, group = c["n"], c["k"], c["group"]
     q, s, x = synthetic.logical(4, n, k, group)
     pw, ps = w4.pack(q, s, group)
     dpw, dps, dx = dev_u8(pw), dev_u8(ps), dev_f16(x)
-    ws = torch.zeros(w4.gemv_workspace_size(n, k, group, True), dtype=torch.uint8, device="cuda")
+    ws = torch.full((w4.gemv_workspace_size(n, k, group, True),), 0xA5, dtype=torch.uint8, device="cuda")
     outs = []
     for _ in range(4):
         y = torch.empty(n, dtype=torch.float32, device="cuda")
@@ -284,7 +285,6 @@ def test_argmax_workspace_reuse():
     for y, am in outs[1:]:
         assert torch.equal(y, outs[0][0]) and int(am.item()) == int(outs[0][1].item())
     assert int(outs[0][1].item()) == oracle.argmax(outs[0][0].cpu().numpy().astype(np.float64))
-    assert int(ws[:4].view(torch.int32).item()) == 0
 
 
 # ----------------------------------------------------------------- ABI on device
