@@ -39,25 +39,33 @@ hipError_t launch_gemv(const GemvCall& call, hipStream_t stream);
 // Workgroups of the main kernel for this call (only n, k, group, epi used).
 int64_t launch_grid(const GemvCall& call);
 
-// Launch shape: SPLIT waves share one unit (k split inside the workgroup),
-// each loading DEPTH k iterations per round before computing.  Chosen from
-// measurements on MI355X at the decode-step shapes: enough waves to cover
-// 256 CUs (split-k for the projections with few rows or long k) and, where
-// registers allow, a wave's whole k range in one round.
+// Launch shape: a unit is TILES tiles (1 or 2) processed together by SPLIT
+// waves (k split inside the workgroup), each loading DEPTH k iterations per
+// round before computing.  Chosen from measurements on MI355X at the
+// decode-step shapes: enough waves to cover 256 CUs (split-k for the
+// projections with few rows or long k), one load round per wave where
+// registers allow, and two tiles per unit for very tall matrices (lm_head),
+// which halves the number of workgroups to dispatch.
 struct LaunchConfig {
+    int tiles;
     int split;
     int depth;
 };
 
-inline LaunchConfig choose_config(int32_t epi, int64_t units, int32_t iters)
+inline LaunchConfig choose_config(int32_t epi, int64_t tiles, int32_t iters)
 {
+    int per_unit = epi == kEpiGateUp ? 2 : 1;
     int split;
-    if (epi == kEpiGateUp || units >= 8192)
+    if (epi == kEpiGateUp) {
         split = 2;
-    else if (iters > 8)
+    } else if (tiles >= 16384) {
+        split = 2;
+        per_unit = 2;
+    } else if (iters > 8) {
         split = 8;
-    else
+    } else {
         split = 4;
+    }
     while (split > 1 && split > iters) split >>= 1;
     const int per_wave = (iters + split - 1) / split;
     int depth;
@@ -67,7 +75,7 @@ inline LaunchConfig choose_config(int32_t epi, int64_t units, int32_t iters)
         depth = per_wave <= 5 ? 5 : 8;
     else
         depth = per_wave <= 4 ? 4 : 8;
-    return LaunchConfig{split, depth};
+    return LaunchConfig{per_unit, split, depth};
 }
 
 // Argmax workspace: per-workgroup best values (fp32), then, from a 256-byte
