@@ -177,6 +177,49 @@ __device__ __forceinline__ bool better(float v, int32_t i, float bv, int32_t bi)
     return v > bv || (v == bv && i < bi);
 }
 
+// Straight-line body for exactly C k iterations of one wave: all loads first
+// (weights and scales non-temporal, x through L1), then the math for each
+// iteration in order.  With no branches between the loads the compiler's
+// wait counters are exact, so iteration d waits only for its own three
+// loads and its math overlaps the loads still in flight (with branches it
+// falls back to waiting for every load before any math).
+template <int C, int U>
+__device__ __forceinline__ void accumulate_exact(float (&acc)[U][4], const uint4* const (&wp)[U],
+                                                 const uint2* const (&sp)[U], const bool (&tile_ok)[U],
+                                                 const uint4* __restrict__ x, int i0, int lane, int gshift,
+                                                 uint32_t magic)
+{
+    uint4 w[C][U];
+    uint2 s[C][U];
+    uint4 xr[C];
+#pragma unroll
+    for (int d = 0; d < C; ++d) {
+        const int j = (i0 + d) * 64 + lane;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            w[d][u] = ld_stream(wp[u] + j);
+            s[d][u] = ld_stream(sp[u] + (j >> gshift));
+        }
+        xr[d] = x[j];
+    }
+#pragma unroll
+    for (int d = 0; d < C; ++d) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            // a unit's missing second tile reads tile 0 (in bounds) with its
+            // scales masked to zero (a mask, not a select, so the scale load
+            // stays unconditional and in issue order)
+            const uint32_t keep = 0u - (uint32_t)tile_ok[u];
+            const uint2 sc = make_uint2(s[d][u].x & keep, s[d][u].y & keep);
+            acc[u][0] = __builtin_fmaf(dot8(w[d][u].x, xr[d], magic), half_lo(sc.x), acc[u][0]);
+            acc[u][1] = __builtin_fmaf(dot8(w[d][u].y, xr[d], magic), half_hi(sc.x), acc[u][1]);
+            acc[u][2] = __builtin_fmaf(dot8(w[d][u].z, xr[d], magic), half_lo(sc.y), acc[u][2]);
+            acc[u][3] = __builtin_fmaf(dot8(w[d][u].w, xr[d], magic), half_hi(sc.y), acc[u][3]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 constexpr int waves_for(int split) { return split < 4 ? 4 : split; }
 
 // U tiles per unit, epilogue EPI, SPLIT waves per unit, D iterations per load
@@ -218,7 +261,21 @@ __global__ void __launch_bounds__(waves_for(SPLIT) * 64) gemv_w4_kernel(KernelAr
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[u][r] = 0.0f;
 
-    if (live) {
+    const int count = it1 - it0;  // this wave's k iterations (uniform)
+    if (live && FULL && (count == D || count == D - 1)) {
+        const uint4* wp[U];
+        const uint2* sp[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t t = tile_ok[u] ? tile_of[u] : 0;
+            wp[u] = a.pw + t * a.kb;
+            sp[u] = a.ps + t * a.ng;
+        }
+        if (count == D)
+            accumulate_exact<D, U>(acc, wp, sp, tile_ok, a.x, it0, lane, a.gshift, magic);
+        else if constexpr (D > 1)
+            accumulate_exact<D - 1, U>(acc, wp, sp, tile_ok, a.x, it0, lane, a.gshift, magic);
+    } else if (live) {
         const uint4* wp[U];
         const uint2* sp[U];
 #pragma unroll
