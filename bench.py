@@ -120,19 +120,22 @@ def time_graph(sweep, stream, steps: int, warmup: int):
     return ev_ms, wall * 1e3 / steps
 
 
-def time_dominant_kernel(projs, stream, replays: int = 10):
+def time_dominant_kernel(projs, stream, replays: int = 4):
     """Average duration of one gate/up + SiLU launch (the kernel that moves the
     most bytes in the sweep): the 28 layers' gate/up launches are captured in
     their own HIP graph (1.96 GB of weights, so nothing is served from the
-    256 MB Infinity Cache) and replayed between HIP events recorded on the
-    launch stream; the per-launch figure includes the ~0.2 us gap between
-    graph nodes."""
+    256 MB Infinity Cache), replayed once to warm up, then `replays` times
+    between HIP events recorded on the launch stream.  The per-launch figure
+    includes the time between graph nodes (about 1.4 us from the last wave of
+    one kernel to the first wave of the next).  The loop is kept short: after
+    a few milliseconds of back-to-back gate/up launches (about 5 TB/s
+    sustained) the kernel was seen to slow down in steps, which the sweep, at
+    a lower average bandwidth, does not show."""
     import torch
     from int4_weight_only_04_amd import w4
     gu = [p for p in projs if p.kind == w4.PROJ_GATEUP_SILU]
     g = w4.Sweep(gu, use_graph=True)
-    for _ in range(2):
-        g.run(stream)
+    g.run(stream)
     stream.synchronize()
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
