@@ -12,6 +12,7 @@ inputs per row are the workload definition's format, the pages being silent):
 
     w[n, k] = (q[n, k] - 8) * s[n, k // G]
     y[n]    = sum_k w[n, k] * x[k]          (fp64, exact products)
+    Y[m, n] = sum_k X[m, k] * w[n, k]       (prefill: one y per token row)
     A[n]    = sum_k |w[n, k] * x[k]|
     h[j]    = silu(y[j]) * y[I + j],  silu(t) = t / (1 + exp(-t))
     argmax  = lowest index of max y
@@ -63,6 +64,10 @@ class Oracle:
         lib.oracle_gemv.argtypes = [p, p, p, i64, i64, i32, p, p]
         lib.oracle_gemv_packed_rows.restype = None
         lib.oracle_gemv_packed_rows.argtypes = [p, p, p, i64, i64, i32, i32, p, i64, p, p]
+        lib.oracle_gemm.restype = None
+        lib.oracle_gemm.argtypes = [p, p, p, i64, i64, i64, i32, p, p]
+        lib.oracle_gemm_packed.restype = None
+        lib.oracle_gemm_packed.argtypes = [p, p, p, i64, i64, i32, i32, p, i64, p, i64, p, p]
         lib.oracle_silu.restype = ctypes.c_double
         lib.oracle_silu.argtypes = [ctypes.c_double]
         lib.oracle_silu_gate.restype = None
@@ -146,6 +151,39 @@ class Oracle:
                                          int(gateup), _ptr(rows), rows.size, _ptr(y), _ptr(a))
         return y, a
 
+    def gemm(self, q: np.ndarray, s_bits: np.ndarray, xm_bits: np.ndarray, group: int):
+        """Prefill product: (Y, A) float64 [m, n] for token rows xm_bits [m, k]."""
+        q = np.ascontiguousarray(q, dtype=np.uint8)
+        s_bits = np.ascontiguousarray(s_bits, dtype=np.uint16)
+        xm_bits = np.ascontiguousarray(xm_bits, dtype=np.uint16)
+        n, k = q.shape
+        m = xm_bits.shape[0]
+        assert s_bits.shape == (n, k // group) and xm_bits.shape == (m, k)
+        y = np.empty((m, n), np.float64)
+        a = np.empty((m, n), np.float64)
+        self.lib.oracle_gemm(_ptr(q), _ptr(s_bits), _ptr(xm_bits), m, n, k, group, _ptr(y), _ptr(a))
+        return y, a
+
+    def gemm_packed(self, pw: np.ndarray, ps: np.ndarray, xm_bits: np.ndarray, n: int, k: int,
+                    group: int, gateup: bool = False, mrows=None, ncols=None):
+        """(Y, A) float64 [len(mrows), len(ncols)] from the packed buffers;
+        defaults: every token row, every weight row."""
+        pw = np.ascontiguousarray(pw, dtype=np.uint8)
+        ps = np.ascontiguousarray(ps, dtype=np.uint8)
+        xm_bits = np.ascontiguousarray(xm_bits, dtype=np.uint16)
+        wb, sb = self.packed_sizes(n, k, group, gateup)
+        assert pw.size >= wb and ps.size >= sb and xm_bits.ndim == 2 and xm_bits.shape[1] == k
+        mt = xm_bits.shape[0]
+        mrows = np.arange(mt, dtype=np.int64) if mrows is None else np.ascontiguousarray(mrows, dtype=np.int64)
+        ncols = np.arange(n, dtype=np.int64) if ncols is None else np.ascontiguousarray(ncols, dtype=np.int64)
+        assert mrows.size == 0 or (mrows.min() >= 0 and mrows.max() < mt)
+        assert ncols.size == 0 or (ncols.min() >= 0 and ncols.max() < n)
+        y = np.empty((mrows.size, ncols.size), np.float64)
+        a = np.empty((mrows.size, ncols.size), np.float64)
+        self.lib.oracle_gemm_packed(_ptr(pw), _ptr(ps), _ptr(xm_bits), n, k, group, int(gateup),
+                                    _ptr(mrows), mrows.size, _ptr(ncols), ncols.size, _ptr(y), _ptr(a))
+        return y, a
+
     def silu(self, t: float) -> float:
         return self.lib.oracle_silu(float(t))
 
@@ -198,6 +236,14 @@ def unpack(pw, ps, n, k, group, gateup=False):
 
 def gemv(q, s_bits, x_bits, group, rows=None):
     return default().gemv(q, s_bits, x_bits, group, rows)
+
+
+def gemm(q, s_bits, xm_bits, group):
+    return default().gemm(q, s_bits, xm_bits, group)
+
+
+def gemm_packed(pw, ps, xm_bits, n, k, group, gateup=False, mrows=None, ncols=None):
+    return default().gemm_packed(pw, ps, xm_bits, n, k, group, gateup, mrows, ncols)
 
 
 def gemv_packed(pw, ps, x_bits, n, k, group, gateup=False, rows=None):

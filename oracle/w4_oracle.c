@@ -1,5 +1,5 @@
 /*
- * CPU oracle for the INT4 weight-only decode GEMV.
+ * CPU oracle for the INT4 weight-only decode GEMV and its prefill GEMM.
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
  * call this file: only the tests, the smoke check and the CPU-baseline leg of
@@ -25,6 +25,9 @@
  * 11-bit significand), every product w*x is exact in double (at most 26
  * significant bits), and the sums are accumulated in double in increasing k,
  * so y is the exact dot product up to the rounding of a plain fp64 sum.
+ *
+ * Prefill (a block of m prompt tokens through the same layers):
+ *     Y[m][n] = sum_k X[m][k] * w[n][k]                     (one y per token)
  *
  * Fused epilogues:
  *     gate/up:  g = y[0..I), u = y[I..2I), h[j] = silu(g[j]) * u[j],
@@ -244,6 +247,33 @@ void oracle_gemv_packed_rows(const uint8_t* pw, const uint8_t* ps, const uint16_
         }
         y[i] = acc;
         a[i] = mag;
+    }
+}
+
+/* Prefill product over a block of tokens (the 512-token prompt whose
+ * first-token latency the pages report: "How To Build Your Own LLM Runtime
+ * From Scratch", aitrending.vip, "Technical Details", performance-metrics
+ * bullet; brifing.si section 6).  The prompt's tokens go through the same
+ * INT4 linear layers, so each token row is the GEMV above: X holds m_total
+ * fp16 rows of k inputs (row-major) and Y[m][n] = sum_k X[m][k] * w[n][k].
+ * Logical inputs; y and a are [m_total][n]. */
+void oracle_gemm(const uint8_t* q, const uint16_t* s, const uint16_t* xm, int64_t m_total, int64_t n,
+                 int64_t k, int32_t group, double* y, double* a)
+{
+    for (int64_t m = 0; m < m_total; ++m)
+        oracle_gemv_rows(q, s, xm + m * k, n, k, group, NULL, n, y + m * n, a + m * n);
+}
+
+/* The same product read from the packed buffers, for the listed token rows
+ * and weight rows: y[i][j] and a[i][j] belong to token mrows[i] and weight
+ * row ncols[j] (ncols == NULL: all n weight rows, nn == n). */
+void oracle_gemm_packed(const uint8_t* pw, const uint8_t* ps, const uint16_t* xm, int64_t n, int64_t k,
+                        int32_t group, int32_t gateup, const int64_t* mrows, int64_t nm,
+                        const int64_t* ncols, int64_t nn, double* y, double* a)
+{
+    for (int64_t i = 0; i < nm; ++i) {
+        int64_t m = mrows[i];
+        oracle_gemv_packed_rows(pw, ps, xm + m * k, n, k, group, gateup, ncols, nn, y + i * nn, a + i * nn);
     }
 }
 

@@ -7,9 +7,11 @@ routine fixes:
   * the hand-derived packing and GEMV example in tests/golden/ (bytes and
     products worked out by hand from the layout rules);
   * IEEE binary16 decoding checked against numpy's float16 for every pattern;
-  * the plain GEMV checked against numpy's float64 matrix product of the
-    dequantized matrix (a library routine, independent of the C loops);
-  * closed forms (zero point, constant nibbles, one-hot activations);
+  * the plain GEMV and the prefill GEMM checked against numpy's float64
+    matrix product of the dequantized matrix (a library routine, independent
+    of the C loops);
+  * closed forms (zero point, constant nibbles, one-hot activations, one-hot
+    token rows selecting weight columns);
   * exact invariants (power-of-two scaling, A >= |y|);
   * silu against scipy's logistic function, argmax against numpy.argmax.
 
@@ -251,6 +253,74 @@ def pin_argmax(orc):
     assert orc.argmax(y) == int(np.argmax(y)) == 1
     y = np.array([np.nan, -1.0, 5.0, np.nan, 5.0])
     assert orc.argmax(y) == 2
+
+
+def pin_gemm_vs_numpy(orc):
+    """The prefill product against numpy's float64 matrix product of the
+    dequantized weights, for the logical and both packed layouts."""
+    rng = np.random.default_rng(19)
+    for m, n, k, group in ((7, 37, 384, 128), (3, 10, 256, 64), (1, 6, 96, 32)):
+        q = rng.integers(0, 16, (n, k), dtype=np.uint8)
+        s = _h(rng.uniform(0.001, 0.02, (n, k // group)))
+        xm = _h(rng.standard_normal((m, k)))
+        w = _dequant_numpy(q, s, group)
+        xf = xm.view(np.float16).astype(np.float64)
+        ref = xf @ w.T
+        refa = np.abs(xf) @ np.abs(w).T
+        y, a = orc.gemm(q, s, xm, group)
+        assert y.shape == (m, n) and a.shape == (m, n)
+        assert np.all(np.abs(y - ref) <= 1e-12 * refa + 1e-300), (m, n, k, group)
+        assert np.allclose(a, refa, rtol=1e-12, atol=0), (m, n, k, group)
+        for gateup in (False, True):
+            if gateup and n % 2:
+                continue
+            pw, ps = orc.pack(q, s, group, gateup)
+            yp, ap = orc.gemm_packed(pw, ps, xm, n, k, group, gateup)
+            assert np.array_equal(yp, y) and np.array_equal(ap, a), (m, n, k, group, gateup)
+
+
+def pin_gemm_onehot_rows(orc):
+    """Token row m one-hot at input k_m selects column k_m of the weights:
+    Y[m, n] = w[n, k_m] exactly (catches a transposed operand or a wrong x row)."""
+    rng = np.random.default_rng(23)
+    n, k, group = 12, 256, 64
+    ks = np.array([0, 1, 7, 8, 63, 64, 130, 255])
+    q = rng.integers(0, 16, (n, k), dtype=np.uint8)
+    s = _h(rng.uniform(-0.02, 0.02, (n, k // group)))
+    sv = s.view(np.float16).astype(np.float64)
+    xm = _h(np.eye(k)[ks])
+    expect = ((q[:, ks].astype(np.float64) - 8.0) * sv[:, ks // group]).T
+    y, a = orc.gemm(q, s, xm, group)
+    assert np.array_equal(y, expect) and np.array_equal(a, np.abs(expect))
+    for gateup in (False, True):
+        pw, ps = orc.pack(q, s, group, gateup)
+        yp, _ = orc.gemm_packed(pw, ps, xm, n, k, group, gateup)
+        assert np.array_equal(yp, expect), gateup
+
+
+def pin_gemm_rows_and_subsets(orc):
+    """Token rows are independent: doubling one row of X doubles that row of Y
+    only, equal rows give equal outputs, and the (token, weight) subsets pick
+    the matching entries of the full product."""
+    rng = np.random.default_rng(29)
+    m, n, k, group = 6, 14, 128, 32
+    q = rng.integers(0, 16, (n, k), dtype=np.uint8)
+    s = _h(rng.uniform(0.001, 0.02, (n, k // group)))
+    xm = _h(rng.standard_normal((m, k)))
+    xm[4] = xm[1]
+    y, a = orc.gemm(q, s, xm, group)
+    assert np.array_equal(y[4], y[1])
+    x2 = xm.copy()
+    x2[2] = _h(2.0 * xm[2].view(np.float16).astype(np.float64))
+    y2, _ = orc.gemm(q, s, x2, group)
+    assert np.array_equal(y2[2], 2 * y[2])
+    keep = np.arange(m) != 2
+    assert np.array_equal(y2[keep], y[keep])
+    pw, ps = orc.pack(q, s, group, False)
+    mr = np.array([5, 0, 3, 3], np.int64)
+    nc = np.array([13, 2, 2, 0, 7], np.int64)
+    ys, as_ = orc.gemm_packed(pw, ps, xm, n, k, group, False, mrows=mr, ncols=nc)
+    assert np.array_equal(ys, y[np.ix_(mr, nc)]) and np.array_equal(as_, a[np.ix_(mr, nc)])
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -42,6 +42,9 @@ MUTANTS = [
     ("unpack_nibble_shift", "q[row * k + 8 * j + e] = (uint8_t)((word >> (4 * slot_of_offset(e))) & 0xfu);",
      "q[row * k + 8 * j + e] = (uint8_t)((word >> (4 * e)) & 0xfu);", None),
     ("sizes_scale_bytes", "(k / group) * 8;", "(k / group) * 16;", None),
+    ("gemm_x_row_fixed", "oracle_gemv_rows(q, s, xm + m * k,", "oracle_gemv_rows(q, s, xm,", None),
+    ("gemm_packed_token_index", "int64_t m = mrows[i];", "int64_t m = i;", None),
+    ("gemm_packed_x_row_fixed", "oracle_gemv_packed_rows(pw, ps, xm + m * k,", "oracle_gemv_packed_rows(pw, ps, xm,", None),
 ]
 
 
