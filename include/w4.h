@@ -143,6 +143,34 @@ w4_status w4_gemv(const void* packed_w, const void* packed_s, const uint16_t* x,
 w4_status w4_gemv_gateup_silu(const void* packed_w, const void* packed_s, const uint16_t* x,
                               uint16_t* h, int64_t n_total, int64_t k, int32_t group, void* stream);
 
+/*
+ * Prefill GEMM over a block of m prompt tokens (the pages report the
+ * first-token latency of a 512-token prompt: "How To Build Your Own LLM
+ * Runtime From Scratch", aitrending.vip, "Technical Details",
+ * performance-metrics bullet): y[t][j] = sum_k x[t][k] * w[j][k] for every
+ * token row t < m and weight row j < n, with w = (q - 8) * s as for w4_gemv.
+ * The weights are dequantized to fp16 (rounded to nearest even) and
+ * multiplied on the matrix cores with fp32 accumulation.  Device,
+ * asynchronous on `stream`.
+ *   packed_w, packed_s  device, from w4_pack(..., W4_LAYOUT_PLAIN, ...);
+ *   x  device, fp16 [m][k] row-major (16-byte aligned);
+ *   y  device, fp32 [m][n] row-major (4-byte aligned), written in full.
+ * Shape rules as for w4_gemv, plus 1 <= m <= 2^20 (W4_ESHAPE otherwise).
+ */
+w4_status w4_gemm(const void* packed_w, const void* packed_s, const uint16_t* x, float* y, int64_t m,
+                  int64_t n, int64_t k, int32_t group, void* stream);
+
+/*
+ * Prefill gate/up + SiLU: with I = n_total / 2, for every token row t,
+ * h[t][j] = silu(g) * u rounded to fp16, g = row t of the product with weight
+ * rows [0, I), u = with rows [I, 2I).  Same arithmetic as w4_gemm.
+ *   packed_w, packed_s  device, from w4_pack(..., W4_LAYOUT_GATEUP, ...);
+ *   x  device fp16 [m][k] row-major;  h  device fp16 [m][n_total / 2] row-major.
+ */
+w4_status w4_gemm_gateup_silu(const void* packed_w, const void* packed_s, const uint16_t* x,
+                              uint16_t* h, int64_t m, int64_t n_total, int64_t k, int32_t group,
+                              void* stream);
+
 /* One projection of the per-token linear sweep. */
 #define W4_PROJ_PLAIN 0         /* w4_gemv, out = float y[n]                  */
 #define W4_PROJ_GATEUP_SILU 1   /* w4_gemv_gateup_silu, out = fp16 h[n/2]     */

@@ -93,6 +93,23 @@ w4_status validate_gemv(const GemvCall& c, const char* who)
     return W4_OK;
 }
 
+w4_status validate_gemm(const GemmCall& c, const char* who)
+{
+    const bool gateup = c.epi == kEpiGateUp;
+    w4_status st = check_shape(c.n, c.k, c.group, gateup, who);
+    if (st != W4_OK) return st;
+    if (c.m < 1 || c.m > ((int64_t)1 << 20))
+        return fail(W4_ESHAPE, "%s: m=%lld must be in [1, 2^20]", who, (long long)c.m);
+    if (!c.pw || !c.ps || !c.x || !c.out)
+        return fail(W4_EINVAL, "%s: null pointer (packed_w=%p packed_s=%p x=%p out=%p)", who, c.pw,
+                    c.ps, c.x, c.out);
+    if (!aligned16(c.pw) || !aligned16(c.ps) || !aligned16(c.x))
+        return fail(W4_EALIGN, "%s: packed_w, packed_s and x must be 16-byte aligned", who);
+    if ((reinterpret_cast<uintptr_t>(c.out) & (gateup ? 1u : 3u)) != 0)
+        return fail(W4_EALIGN, "%s: output must be aligned to its element size", who);
+    return W4_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -218,6 +235,37 @@ w4_status w4_gemv_gateup_silu(const void* packed_w, const void* packed_s, const 
         return ok();
     } catch (...) {
         return fail(W4_EINVAL, "w4_gemv_gateup_silu: internal exception");
+    }
+}
+
+w4_status w4_gemm(const void* packed_w, const void* packed_s, const uint16_t* x, float* y, int64_t m,
+                  int64_t n, int64_t k, int32_t group, void* stream)
+{
+    try {
+        GemmCall c{packed_w, packed_s, x, y, m, n, k, group, kEpiPlain};
+        w4_status st = validate_gemm(c, "w4_gemm");
+        if (st != W4_OK) return st;
+        hipError_t err = launch_gemm(c, static_cast<hipStream_t>(stream));
+        if (err != hipSuccess) return hip_fail(err, "w4_gemm launch");
+        return ok();
+    } catch (...) {
+        return fail(W4_EINVAL, "w4_gemm: internal exception");
+    }
+}
+
+w4_status w4_gemm_gateup_silu(const void* packed_w, const void* packed_s, const uint16_t* x,
+                              uint16_t* h, int64_t m, int64_t n_total, int64_t k, int32_t group,
+                              void* stream)
+{
+    try {
+        GemmCall c{packed_w, packed_s, x, h, m, n_total, k, group, kEpiGateUp};
+        w4_status st = validate_gemm(c, "w4_gemm_gateup_silu");
+        if (st != W4_OK) return st;
+        hipError_t err = launch_gemm(c, static_cast<hipStream_t>(stream));
+        if (err != hipSuccess) return hip_fail(err, "w4_gemm_gateup_silu launch");
+        return ok();
+    } catch (...) {
+        return fail(W4_EINVAL, "w4_gemm_gateup_silu: internal exception");
     }
 }
 

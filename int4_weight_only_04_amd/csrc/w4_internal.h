@@ -32,6 +32,40 @@ struct GemvCall {
     int32_t epi;
 };
 
+// Prefill GEMM: y[m][n] = sum_k x[m][k] * w[n][k] for a block of token rows
+// (x fp16 [m][k] row-major; y fp32 [m][n], or h fp16 [m][n/2] for gate/up).
+struct GemmCall {
+    const void* pw;
+    const void* ps;
+    const void* x;
+    void* out;
+    int64_t m;
+    int64_t n;
+    int64_t k;
+    int32_t group;
+    int32_t epi;         // kEpiPlain or kEpiGateUp
+};
+
+hipError_t launch_gemm(const GemmCall& call, hipStream_t stream);
+
+// Output tile of the prefill GEMM: 128 x 128 by default; 64-row tiles, then
+// 64-column tiles (plain only), while the grid would leave CUs of the 256
+// idle.  Gate/up tiles always hold 64 gate rows and the matching 64 up rows.
+struct GemmShape {
+    int bm;
+    int bn;
+};
+
+inline GemmShape choose_gemm_shape(int32_t epi, int64_t m, int64_t n)
+{
+    const int64_t cols = epi == kEpiGateUp ? n / 2 : n;
+    const int64_t per_tile = epi == kEpiGateUp ? 64 : 128;
+    auto tiles = [&](int64_t bm, int64_t cn) { return ((m + bm - 1) / bm) * ((cols + cn - 1) / cn); };
+    if (tiles(128, per_tile) >= 512) return GemmShape{128, 128};
+    if (epi == kEpiGateUp || tiles(64, 128) >= 256) return GemmShape{64, 128};
+    return GemmShape{64, 64};
+}
+
 // Launch one GEMV on `stream` (shape already validated by the caller); the
 // argmax epilogue adds a one-workgroup finalize kernel on the same stream.
 hipError_t launch_gemv(const GemvCall& call, hipStream_t stream);

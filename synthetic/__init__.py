@@ -31,6 +31,7 @@ VOCAB = 152064
 LAYERS = 28
 QKV = 4608
 GROUP = 128
+PROMPT = 512   # prompt tokens of the prefill workload (the pages' 512-token first-token latency)
 
 
 def _rng(seed: int) -> np.random.Generator:
@@ -76,6 +77,12 @@ def packed_random(seed: int, weight_bytes: int, scale_count: int, k: int,
     return np.ascontiguousarray(pw), ps, x
 
 
+def prompt_acts(seed: int, m: int, k: int) -> np.ndarray:
+    """A block of m token activation rows for the prefill product: fp16 bits
+    [m, k], N(0, 1) drawn in float32 and rounded to fp16, row after row."""
+    return _acts(_rng(seed), m * k).reshape(m, k)
+
+
 @dataclass(frozen=True)
 class Proj:
     """One projection of the decode-step linear sweep."""
@@ -95,6 +102,19 @@ CONFIG_GATEUP = dict(name="gateup", kind="gateup", n=2 * MLP, k=HIDDEN, group=GR
                      s_lo=0.001, s_hi=0.02)
 CONFIG_LMHEAD = dict(name="lmhead", kind="lmhead", n=VOCAB, k=HIDDEN, group=GROUP, seed=3,
                      s_lo=0.001, s_hi=0.02)
+
+
+def prefill_projections(layers: int = LAYERS) -> list[Proj]:
+    """The 28 layers' four prefill products in order (lm_head runs as the
+    decode GEMV on the last prompt token).  Weights of layer l, projection p
+    use seed 2000 + 10*l + p; the token block feeding it uses that seed + 5."""
+    out = []
+    for l in range(layers):
+        out.append(Proj(f"L{l}.qkv", "plain", QKV, HIDDEN, GROUP, 2000 + 10 * l + 0))
+        out.append(Proj(f"L{l}.o", "plain", HIDDEN, HIDDEN, GROUP, 2000 + 10 * l + 1))
+        out.append(Proj(f"L{l}.gateup", "gateup", 2 * MLP, HIDDEN, GROUP, 2000 + 10 * l + 2))
+        out.append(Proj(f"L{l}.down", "plain", HIDDEN, MLP, GROUP, 2000 + 10 * l + 3))
+    return out
 
 
 def sweep_projections(layers: int = LAYERS) -> list[Proj]:

@@ -149,6 +149,25 @@ def test_gemv_validation_before_launch():
     assert L.w4_gemv_gateup_silu(A, None, A, A, 6, 64, 32, None) == w4.EINVAL
 
 
+def test_gemm_validation_before_launch():
+    """Prefill GEMM argument checks run before any device call."""
+    L = w4.lib()
+    A = 1 << 20
+    assert L.w4_gemm(None, A, A, A, 8, 4, 64, 32, None) == w4.EINVAL
+    assert L.w4_gemm(A, A, A, None, 8, 4, 64, 32, None) == w4.EINVAL
+    assert L.w4_gemm(A, A, A + 2, A, 8, 4, 64, 32, None) == w4.EALIGN
+    assert L.w4_gemm(A + 8, A, A, A, 8, 4, 64, 32, None) == w4.EALIGN
+    assert L.w4_gemm(A, A, A, A + 2, 8, 4, 64, 32, None) == w4.EALIGN
+    assert L.w4_gemm(A, A, A, A, 0, 4, 64, 32, None) == w4.ESHAPE
+    assert L.w4_gemm(A, A, A, A, (1 << 20) + 1, 4, 64, 32, None) == w4.ESHAPE
+    assert L.w4_gemm(A, A, A, A, 8, 4, 96, 64, None) == w4.ESHAPE
+    assert L.w4_gemm(A, A, A, A, 8, 0, 64, 32, None) == w4.ESHAPE
+    assert L.w4_gemm_gateup_silu(A, A, A, A, 8, 5, 64, 32, None) == w4.ESHAPE
+    assert L.w4_gemm_gateup_silu(A, A, A, A + 1, 8, 6, 64, 32, None) == w4.EALIGN
+    assert L.w4_gemm_gateup_silu(A, None, A, A, 8, 6, 64, 32, None) == w4.EINVAL
+    assert "w4_gemm_gateup_silu" in w4.last_error()
+
+
 def test_sweep_create_validation():
     L = w4.lib()
     A = 1 << 20
