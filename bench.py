@@ -12,6 +12,13 @@ prints one JSON line: achieved GB/s over the whole sweep (value), ms per
 sweep, the eager-launch sweep for comparison, the dominant kernel's roofline
 (gate/up + SiLU, timed per launch with HIP events on the launch stream) and
 the CPU oracle timed on a bounded sample on the host.
+
+    python bench.py --workload prefill [--steps 10] [--warmup 2]
+
+times the prefill counterpart instead: the 28 layers' four INT4 products for
+a 512-token prompt (112 GEMMs on the matrix cores) plus lm_head on the last
+token, captured in one HIP graph; value is TFLOP/s over the sweep, the
+roofline is the gate/up GEMM's against the fp16 matrix-core peak.
 """
 from __future__ import annotations
 
@@ -31,7 +38,9 @@ import numpy as np  # noqa: E402
 import synthetic  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 matrix-core peak
 METRIC = "achieved HBM GB/s (% of peak) and ms per 28-layer+lm_head INT4 linear sweep"
+PREFILL_METRIC = "prefill TFLOP/s (% of fp16 MFMA peak) and ms per 28-layer 512-token INT4 linear sweep"
 KERNEL_SRC = os.path.join(ROOT, "int4_weight_only_04_amd", "csrc", "w4_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gateup_silu_37888x3584.json")
 
@@ -178,6 +187,175 @@ def cpu_baseline():
     }
 
 
+def build_prefill(layers: int, device: str = "cuda"):
+    """Device buffers of the prefill sweep: packed weights drawn like the decode
+    sweep's, one seeded 512-row token block per projection, and lm_head as
+    the decode GEMV (with argmax) on one token."""
+    import torch
+    from int4_weight_only_04_amd import w4
+
+    m = synthetic.PROMPT
+    items = []
+    for p in synthetic.prefill_projections(layers):
+        layout = "gateup" if p.kind == "gateup" else "plain"
+        wb, sb = w4.packed_size(p.n, p.k, p.group, layout)
+        pw, ps, _ = synthetic.packed_random(p.seed, wb, sb // 2, p.k)
+        xm = synthetic.prompt_acts(p.seed + 5, m, p.k)
+        dx = torch.from_numpy(xm.view(np.int16)).to(device).view(torch.float16)
+        cols = p.n // 2 if p.kind == "gateup" else p.n
+        out = torch.empty((m, cols), dtype=torch.float16 if p.kind == "gateup" else torch.float32,
+                          device=device)
+        items.append((p, torch.from_numpy(pw).to(device), torch.from_numpy(ps).to(device), dx, out))
+    lm = synthetic.sweep_projections(0)[-1]
+    wb, sb = w4.packed_size(lm.n, lm.k, lm.group, "plain")
+    pw, ps, x = synthetic.packed_random(lm.seed, wb, sb // 2, lm.k)
+    lm_buf = (lm, torch.from_numpy(pw).to(device), torch.from_numpy(ps).to(device),
+              torch.from_numpy(x.view(np.int16)).to(device).view(torch.float16),
+              torch.empty(lm.n, dtype=torch.float32, device=device),
+              torch.full((1,), -1, dtype=torch.int32, device=device),
+              torch.zeros(w4.gemv_workspace_size(lm.n, lm.k, lm.group, True), dtype=torch.uint8,
+                          device=device))
+    return items, lm_buf
+
+
+def prefill_flops(items, lm_buf) -> int:
+    m = synthetic.PROMPT
+    return sum(2 * m * p.n * p.k for (p, *_rest) in items) + 2 * lm_buf[0].n * lm_buf[0].k
+
+
+def launch_prefill(items, lm_buf, stream, only_gateup: bool = False):
+    from int4_weight_only_04_amd import w4
+    m = synthetic.PROMPT
+    for p, pw, ps, x, out in items:
+        if p.kind == "gateup":
+            w4.gemm_gateup_silu(pw, ps, x, out, m, p.n, p.k, p.group, stream=stream)
+        elif not only_gateup:
+            w4.gemm(pw, ps, x, out, m, p.n, p.k, p.group, stream=stream)
+    if not only_gateup:
+        lm, pw, ps, x, y, am, ws = lm_buf
+        w4.gemv(pw, ps, x, y, lm.n, lm.k, lm.group, argmax=am, workspace=ws, stream=stream)
+
+
+def capture(fn, stream):
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        fn(torch.cuda.current_stream())
+    return g
+
+
+def replay_ms(g, stream, steps: int, warmup: int) -> float:
+    import torch
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            g.replay()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        a.record(stream)
+        for _ in range(steps):
+            g.replay()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def prefill_cpu_baseline(tokens: int = 4):
+    """The oracle's prefill product (single thread, fp64) on a bounded sample:
+    layer 0's four projections, all weight rows, for the first `tokens` rows
+    of their token blocks."""
+    import oracle
+    from int4_weight_only_04_amd import w4
+    flops = 0
+    t_total = 0.0
+    for p in synthetic.prefill_projections(1):
+        layout = "gateup" if p.kind == "gateup" else "plain"
+        wb, sb = w4.packed_size(p.n, p.k, p.group, layout)
+        pw, ps, _ = synthetic.packed_random(p.seed, wb, sb // 2, p.k)
+        xm = synthetic.prompt_acts(p.seed + 5, tokens, p.k)
+        t0 = time.perf_counter()
+        y, _ = oracle.gemm_packed(pw, ps, xm, p.n, p.k, p.group, gateup=(layout == "gateup"))
+        if p.kind == "gateup":
+            for row in y:
+                oracle.silu_gate(row)
+        t_total += time.perf_counter() - t0
+        flops += 2 * tokens * p.n * p.k
+    return {
+        "value": flops / t_total / 1e12,
+        "unit": "TFLOP/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"layer 0 of the prefill sweep (qkv, o_proj, gate/up+silu, down), all rows, first "
+                  f"{tokens} prompt tokens: {flops} flops in {t_total:.1f} s, single-threaded fp64 C",
+        "seconds": t_total,
+    }
+
+
+def run_prefill(args) -> int:
+    import torch
+    print(f"[bench] building prefill sweep ({args.layers} layers, {synthetic.PROMPT} tokens)",
+          file=sys.stderr, flush=True)
+    items, lm_buf = build_prefill(args.layers)
+    flops = prefill_flops(items, lm_buf)
+    stream = torch.cuda.Stream()
+    print("[bench] prefill graph", file=sys.stderr, flush=True)
+    g = capture(lambda s: launch_prefill(items, lm_buf, s), stream)
+    ms = replay_ms(g, stream, args.steps, args.warmup)
+    print("[bench] dominant kernel (gate/up GEMM)", file=sys.stderr, flush=True)
+    gg = capture(lambda s: launch_prefill(items, lm_buf, s, only_gateup=True), stream)
+    n_gu = sum(1 for it in items if it[0].kind == "gateup")
+    reps = 3
+    gu_ms = replay_ms(gg, stream, reps, 1) / n_gu
+    gp = next(it[0] for it in items if it[0].kind == "gateup")
+    gu_flops = 2 * synthetic.PROMPT * gp.n * gp.k
+    gu_tflops = gu_flops / (gu_ms * 1e-3) / 1e12
+    value = flops / (ms * 1e-3) / 1e12
+    out = {
+        "metric": PREFILL_METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"512-token prefill INT4 linear sweep, hipGraph: {args.layers} x (qkv 3584->4608, "
+                         "o_proj 3584->3584, gate/up 3584->2x18944 + silu, down 18944->3584) as GEMMs on "
+                         "512 token rows + lm_head 3584->152064 + argmax on the last token; int4 zero point "
+                         "8, fp16 scales per 128 inputs dequantized to fp16, fp16 activations, fp32 "
+                         "accumulation"),
+            "prompt_tokens": synthetic.PROMPT,
+            "gemms_per_step": len(items),
+            "flops_per_step": flops,
+            "pct_of_mfma_f16_peak": round(100.0 * value / MFMA_F16_PEAK_TFLOPS, 2),
+        },
+        "roofline": {
+            "kernel": "gemm_w4_kernel<128, 128, gate/up+silu> 512x37888x3584 g128",
+            "bound": "mfma",
+            "achieved": round(gu_tflops, 2),
+            "peak": MFMA_F16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(gu_tflops / MFMA_F16_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "algorithmic_flops_per_launch": gu_flops,
+            "avg_launch_us": round(gu_ms * 1e3, 3),
+            "launches_timed": reps * n_gu,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle prefill product)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = prefill_cpu_baseline()
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -186,6 +364,8 @@ def main(argv=None):
     ap.add_argument("--layers", type=int, default=synthetic.LAYERS)
     ap.add_argument("--eager-steps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", choices=("decode", "prefill"), default="decode",
+                    help="decode: the per-token GEMV sweep (default); prefill: the 512-token GEMM sweep")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args(argv)
@@ -211,6 +391,9 @@ def main(argv=None):
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": nbytes, "launches": 3}), flush=True)
         return 0
+
+    if args.workload == "prefill":
+        return run_prefill(args)
 
     print(f"[bench] building sweep ({args.layers} layers)", file=sys.stderr, flush=True)
     specs, projs = build_sweep(args.layers)
