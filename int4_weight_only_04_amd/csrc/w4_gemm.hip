@@ -71,11 +71,21 @@ __device__ __forceinline__ u32x4_t dequant_word(uint32_t d, uint32_t s2)
     return r;
 }
 
-// BM x BN output tile per workgroup (BM, BN in {64, 128}; gate/up: BN = 128,
-// holding 64 gate and the matching 64 up rows).  Wave (wm, wn) owns a
-// (BM/2) x (BN/2) quarter as (BM/64) x (BN/64) blocks of 32 x 32; for gate/up
-// its two n blocks are a gate block and the up block of the same outputs, so
-// both land in the same lanes and registers.
+// BM x BN output tile per workgroup (BM in {64, 128}, BN = 128; for gate/up
+// the 128 weight rows are 64 gate rows and the matching 64 up rows).  Wave
+// (wm, wn) owns a (BM/2) x (BN/2) quarter as (BM/64) x 2 blocks of 32 x 32;
+// for gate/up its two n blocks are a gate block and the up block of the same
+// outputs, so both land in the same lanes and registers.
+//
+// Pipeline: the global loads of k step s+4 go out while step s is computed
+// (a ring of 4 register slots, the loop unrolled by 4 so every slot index is a
+// constant), and the LDS tiles are double-buffered, so one barrier per k step
+// separates a step's LDS writes from its MFMA reads.  Loads are never
+// predicated: past-the-end addresses are clamped in bounds and the values
+// masked when stored to LDS (k tail: x and the scale zeroed, so the weight is
+// 0; rows past m are read from the last row and never written out).
+constexpr int kRing = 4;
+
 template <int BM, int BN, int EPI>
 __global__ void __launch_bounds__(kThreads) gemm_w4_kernel(GemmArgs a)
 {
@@ -83,9 +93,9 @@ __global__ void __launch_bounds__(kThreads) gemm_w4_kernel(GemmArgs a)
     constexpr int NB = BN / 64;
     constexpr int XCHUNKS = BM * 8 / kThreads;          // 16-B chunks of X per thread per step
     constexpr int WITEMS = BN / 4 * 8;                   // (tile, block) items of W per step
-    static_assert(EPI != kEpiGateUp || BN == 128, "gate/up tiles pair 64 gate with 64 up rows");
-    __shared__ __attribute__((aligned(16))) _Float16 xs[BM * kRowHalves];
-    __shared__ __attribute__((aligned(16))) _Float16 wsm[BN * kRowHalves];
+    static_assert(BN == 128 && WITEMS == kThreads, "one W item per thread");
+    __shared__ __attribute__((aligned(16))) _Float16 xs[2][BM * kRowHalves];
+    __shared__ __attribute__((aligned(16))) _Float16 wsm[2][BN * kRowHalves];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -96,65 +106,70 @@ __global__ void __launch_bounds__(kThreads) gemm_w4_kernel(GemmArgs a)
     // first output column of the tile (gate/up: first h column, 64 per tile)
     const int64_t c0 = (int64_t)blockIdx.x * (EPI == kEpiGateUp ? BN / 2 : BN);
 
-    // ---- global -> register assignment
-    // X: chunk c = tid + kThreads * i -> row c / 8, 16-byte column c % 8
+    // X: chunk c = tid + kThreads * i -> tile row c / 8, 16-byte column c % 8
     int64_t xrow_off[XCHUNKS];
-    bool xrow_ok[XCHUNKS];
 #pragma unroll
     for (int i = 0; i < XCHUNKS; ++i) {
         const int c = tid + kThreads * i;
-        const int64_t row = m0 + c / 8;
-        xrow_ok[i] = row < a.m;
-        xrow_off[i] = (xrow_ok[i] ? row : 0) * a.kb + (c % 8);
+        int64_t row = m0 + c / 8;
+        if (row >= a.m) row = a.m - 1;
+        xrow_off[i] = row * a.kb + (c % 8);
     }
-    // W: item tid (when tid < WITEMS) -> LDS tile tt = tid / 8, block jj = tid % 8
-    const bool witem = tid < WITEMS;
+    // W: thread tid -> LDS tile tt = tid / 8 (4 rows), 8-input block jj = tid % 8
     const int tt = tid / 8;
     const int jj = tid % 8;
     int64_t ptile;
     bool wok;
     if constexpr (EPI == kEpiGateUp) {
         const int64_t t = (int64_t)blockIdx.x * 16 + (tt % 16);  // tile within the half
-        wok = witem && t < a.tiles_half;
+        wok = t < a.tiles_half;
         ptile = (tt < 16 ? t : a.tiles_half + t);
     } else {
         ptile = (int64_t)blockIdx.x * (BN / 4) + tt;
-        wok = witem && ptile < a.tiles;
+        wok = ptile < a.tiles;
     }
     if (!wok) ptile = 0;
-    const uint4* wbase = a.pw + ptile * a.kb + jj;
+    const uint4* wbase = a.pw + ptile * a.kb;
     const uint2* sbase = a.ps + ptile * a.ng;
 
-    uint4 xr[XCHUNKS];
-    uint4 wr;
-    uint2 sr;
-    auto gload = [&](int step) {
+    struct Slot {
+        uint4 x[XCHUNKS];
+        uint4 w;
+        uint2 s;
+    };
+    Slot ring[kRing];
+
+    auto issue = [&](Slot& sl, int step) {
+        if (step >= a.steps) step = a.steps - 1;  // in bounds, never stored
+        const int blk0 = step * 8;
+#pragma unroll
+        for (int i = 0; i < XCHUNKS; ++i) {
+            int blk = blk0 + ((tid + kThreads * i) % 8);
+            if (blk >= a.kb) blk = a.kb - 1;
+            sl.x[i] = a.x[xrow_off[i] - ((tid + kThreads * i) % 8) + blk];
+        }
+        int wblk = blk0 + jj;
+        if (wblk >= a.kb) wblk = a.kb - 1;
+        sl.w = wbase[wblk];
+        sl.s = sbase[wblk >> a.gshift];
+    };
+    auto lstore = [&](const Slot& sl, int step, int b) {
         const int blk0 = step * 8;
 #pragma unroll
         for (int i = 0; i < XCHUNKS; ++i) {
             const int c = tid + kThreads * i;
-            const bool ok = xrow_ok[i] && blk0 + (c % 8) < a.kb;
-            xr[i] = ok ? a.x[xrow_off[i] + blk0] : make_uint4(0, 0, 0, 0);
+            const uint32_t keep = 0u - (uint32_t)(blk0 + (c % 8) < a.kb);
+            const uint4 v = make_uint4(sl.x[i].x & keep, sl.x[i].y & keep, sl.x[i].z & keep, sl.x[i].w & keep);
+            *reinterpret_cast<uint4*>(&xs[b][(c / 8) * kRowHalves + (c % 8) * 8]) = v;
         }
-        const bool ok = wok && blk0 + jj < a.kb;
-        wr = ok ? wbase[blk0] : make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
-        sr = ok ? sbase[(blk0 + jj) >> a.gshift] : make_uint2(0, 0);
-    };
-    auto lstore = [&]() {
+        const uint32_t keep = 0u - (uint32_t)(wok && blk0 + jj < a.kb);
+        const uint32_t wd[4] = {sl.w.x, sl.w.y, sl.w.z, sl.w.w};
+        const uint32_t sx = sl.s.x & keep, sy = sl.s.y & keep;
+        const uint32_t sd[4] = {sx & 0xFFFFu, sx >> 16, sy & 0xFFFFu, sy >> 16};
 #pragma unroll
-        for (int i = 0; i < XCHUNKS; ++i) {
-            const int c = tid + kThreads * i;
-            *reinterpret_cast<uint4*>(&xs[(c / 8) * kRowHalves + (c % 8) * 8]) = xr[i];
-        }
-        if (witem) {
-            const uint32_t wd[4] = {wr.x, wr.y, wr.z, wr.w};
-            const uint32_t sd[4] = {sr.x & 0xFFFFu, sr.x >> 16, sr.y & 0xFFFFu, sr.y >> 16};
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const uint32_t s2 = sd[r] | (sd[r] << 16);
-                const u32x4_t v = dequant_word(wd[r], s2);
-                *reinterpret_cast<u32x4_t*>(&wsm[(tt * 4 + r) * kRowHalves + jj * 8]) = v;
-            }
+        for (int r = 0; r < 4; ++r) {
+            const uint32_t s2 = sd[r] | (sd[r] << 16);
+            *reinterpret_cast<u32x4_t*>(&wsm[b][(tt * 4 + r) * kRowHalves + jj * 8]) = dequant_word(wd[r], s2);
         }
     };
 
@@ -178,28 +193,49 @@ __global__ void __launch_bounds__(kThreads) gemm_w4_kernel(GemmArgs a)
             brow[j] = wn * (BN / 2) + j * 32 + (lane & 31);
     }
     const int kofs = 8 * (lane >> 5);
-
-    gload(0);
-    for (int step = 0; step < a.steps; ++step) {
-        lstore();
-        __syncthreads();
-        if (step + 1 < a.steps) gload(step + 1);
+    auto mfma_step = [&](int b) {
 #pragma unroll
         for (int kk = 0; kk < kStepK / 16; ++kk) {
             h8_t av[MB], bv[NB];
 #pragma unroll
             for (int i = 0; i < MB; ++i)
-                av[i] = *reinterpret_cast<const h8_t*>(&xs[arow[i] * kRowHalves + kk * 16 + kofs]);
+                av[i] = *reinterpret_cast<const h8_t*>(&xs[b][arow[i] * kRowHalves + kk * 16 + kofs]);
 #pragma unroll
             for (int j = 0; j < NB; ++j)
-                bv[j] = *reinterpret_cast<const h8_t*>(&wsm[brow[j] * kRowHalves + kk * 16 + kofs]);
+                bv[j] = *reinterpret_cast<const h8_t*>(&wsm[b][brow[j] * kRowHalves + kk * 16 + kofs]);
 #pragma unroll
             for (int i = 0; i < MB; ++i)
 #pragma unroll
                 for (int j = 0; j < NB; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
         }
-        __syncthreads();
+    };
+
+#pragma unroll
+    for (int u = 0; u < kRing; ++u) issue(ring[u], u);
+    // whole groups of kRing steps: a branch-free body, so the compiler can wait
+    // for exactly one slot's loads before each LDS store
+    const int whole = a.steps - a.steps % kRing;
+    for (int base = 0; base < whole; base += kRing) {
+#pragma unroll
+        for (int u = 0; u < kRing; ++u) {
+            // keep each step's work in place: hoisting a later slot's dequant
+            // above this point would make it wait for that slot's loads
+            __builtin_amdgcn_sched_barrier(0);
+            lstore(ring[u], base + u, u & 1);
+            issue(ring[u], base + u + kRing);
+            __syncthreads();
+            mfma_step(u & 1);
+        }
+    }
+    // the last steps % kRing steps (their slots are the first ones of the ring)
+#pragma unroll
+    for (int u = 0; u < kRing - 1; ++u) {
+        if (whole + u < a.steps) {
+            lstore(ring[u], whole + u, u & 1);
+            __syncthreads();
+            mfma_step(u & 1);
+        }
     }
 
     // ---- epilogue: register r of lane l holds row 8(r/4) + 4(l/32) + r%4, column l%32 of its block
@@ -262,14 +298,9 @@ GemmPlan make_gemm_plan(const GemmCall& c)
     if (gateup)
         p.fn = sh.bm == 128 ? reinterpret_cast<const void*>(&gemm_w4_kernel<128, 128, kEpiGateUp>)
                             : reinterpret_cast<const void*>(&gemm_w4_kernel<64, 128, kEpiGateUp>);
-    else if (sh.bm == 128 && sh.bn == 128)
-        p.fn = reinterpret_cast<const void*>(&gemm_w4_kernel<128, 128, kEpiPlain>);
-    else if (sh.bm == 64 && sh.bn == 128)
-        p.fn = reinterpret_cast<const void*>(&gemm_w4_kernel<64, 128, kEpiPlain>);
-    else if (sh.bm == 64 && sh.bn == 64)
-        p.fn = reinterpret_cast<const void*>(&gemm_w4_kernel<64, 64, kEpiPlain>);
     else
-        p.fn = nullptr;
+        p.fn = sh.bm == 128 ? reinterpret_cast<const void*>(&gemm_w4_kernel<128, 128, kEpiPlain>)
+                            : reinterpret_cast<const void*>(&gemm_w4_kernel<64, 128, kEpiPlain>);
     return p;
 }
 

@@ -48,9 +48,9 @@ struct GemmCall {
 
 hipError_t launch_gemm(const GemmCall& call, hipStream_t stream);
 
-// Output tile of the prefill GEMM: 128 x 128 by default; 64-row tiles, then
-// 64-column tiles (plain only), while the grid would leave CUs of the 256
-// idle.  Gate/up tiles always hold 64 gate rows and the matching 64 up rows.
+// Output tile of the prefill GEMM: 128 x 128, or 64 x 128 while 128-row
+// tiles would give fewer than two workgroups per CU of the 256.  Gate/up
+// tiles hold 64 gate rows and the matching 64 up rows.
 struct GemmShape {
     int bm;
     int bn;
@@ -60,10 +60,8 @@ inline GemmShape choose_gemm_shape(int32_t epi, int64_t m, int64_t n)
 {
     const int64_t cols = epi == kEpiGateUp ? n / 2 : n;
     const int64_t per_tile = epi == kEpiGateUp ? 64 : 128;
-    auto tiles = [&](int64_t bm, int64_t cn) { return ((m + bm - 1) / bm) * ((cols + cn - 1) / cn); };
-    if (tiles(128, per_tile) >= 512) return GemmShape{128, 128};
-    if (epi == kEpiGateUp || tiles(64, 128) >= 256) return GemmShape{64, 128};
-    return GemmShape{64, 64};
+    const int64_t tiles128 = ((m + 127) / 128) * ((cols + per_tile - 1) / per_tile);
+    return tiles128 >= 512 ? GemmShape{128, 128} : GemmShape{64, 128};
 }
 
 // Launch one GEMV on `stream` (shape already validated by the caller); the
