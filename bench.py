@@ -206,6 +206,10 @@ def build_prefill(layers: int, device: str = "cuda"):
         out = torch.empty((m, cols), dtype=torch.float16 if p.kind == "gateup" else torch.float32,
                           device=device)
         items.append((p, torch.from_numpy(pw).to(device), torch.from_numpy(ps).to(device), dx, out))
+    # one split-k workspace serves every product: they run one after another
+    ws_bytes = max([w4.gemm_workspace_size(m, p.n, p.k, p.group) for (p, *_r) in items if p.kind != "gateup"]
+                   + [16])
+    workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=device)
     lm = synthetic.sweep_projections(0)[-1]
     wb, sb = w4.packed_size(lm.n, lm.k, lm.group, "plain")
     pw, ps, x = synthetic.packed_random(lm.seed, wb, sb // 2, lm.k)
@@ -215,7 +219,7 @@ def build_prefill(layers: int, device: str = "cuda"):
               torch.full((1,), -1, dtype=torch.int32, device=device),
               torch.zeros(w4.gemv_workspace_size(lm.n, lm.k, lm.group, True), dtype=torch.uint8,
                           device=device))
-    return items, lm_buf
+    return items, lm_buf, workspace
 
 
 def prefill_flops(items, lm_buf) -> int:
@@ -223,14 +227,14 @@ def prefill_flops(items, lm_buf) -> int:
     return sum(2 * m * p.n * p.k for (p, *_rest) in items) + 2 * lm_buf[0].n * lm_buf[0].k
 
 
-def launch_prefill(items, lm_buf, stream, only_gateup: bool = False):
+def launch_prefill(items, lm_buf, workspace, stream, only_gateup: bool = False):
     from int4_weight_only_04_amd import w4
     m = synthetic.PROMPT
     for p, pw, ps, x, out in items:
         if p.kind == "gateup":
             w4.gemm_gateup_silu(pw, ps, x, out, m, p.n, p.k, p.group, stream=stream)
         elif not only_gateup:
-            w4.gemm(pw, ps, x, out, m, p.n, p.k, p.group, stream=stream)
+            w4.gemm(pw, ps, x, out, m, p.n, p.k, p.group, workspace=workspace, stream=stream)
     if not only_gateup:
         lm, pw, ps, x, y, am, ws = lm_buf
         w4.gemv(pw, ps, x, y, lm.n, lm.k, lm.group, argmax=am, workspace=ws, stream=stream)
@@ -296,14 +300,14 @@ def run_prefill(args) -> int:
     import torch
     print(f"[bench] building prefill sweep ({args.layers} layers, {synthetic.PROMPT} tokens)",
           file=sys.stderr, flush=True)
-    items, lm_buf = build_prefill(args.layers)
+    items, lm_buf, workspace = build_prefill(args.layers)
     flops = prefill_flops(items, lm_buf)
     stream = torch.cuda.Stream()
     print("[bench] prefill graph", file=sys.stderr, flush=True)
-    g = capture(lambda s: launch_prefill(items, lm_buf, s), stream)
+    g = capture(lambda s: launch_prefill(items, lm_buf, workspace, s), stream)
     ms = replay_ms(g, stream, args.steps, args.warmup)
     print("[bench] dominant kernel (gate/up GEMM)", file=sys.stderr, flush=True)
-    gg = capture(lambda s: launch_prefill(items, lm_buf, s, only_gateup=True), stream)
+    gg = capture(lambda s: launch_prefill(items, lm_buf, workspace, s, only_gateup=True), stream)
     n_gu = sum(1 for it in items if it[0].kind == "gateup")
     reps = 3
     gu_ms = replay_ms(gg, stream, reps, 1) / n_gu
@@ -336,7 +340,7 @@ def run_prefill(args) -> int:
             "pct_of_mfma_f16_peak": round(100.0 * value / MFMA_F16_PEAK_TFLOPS, 2),
         },
         "roofline": {
-            "kernel": "gemm_w4_kernel<128, 128, gate/up+silu> 512x37888x3584 g128",
+            "kernel": "gemm_w4_kernel<gate/up+silu> 512x37888x3584 g128",
             "bound": "mfma",
             "achieved": round(gu_tflops, 2),
             "peak": MFMA_F16_PEAK_TFLOPS,

@@ -144,21 +144,33 @@ w4_status w4_gemv_gateup_silu(const void* packed_w, const void* packed_s, const 
                               uint16_t* h, int64_t n_total, int64_t k, int32_t group, void* stream);
 
 /*
+ * Workspace bytes w4_gemm needs for an m x n x k product: 0 when the grid
+ * already covers the chip, else the split-k partials (splits x m x n fp32,
+ * splits <= 8; 37.7 MB for 512 x 4608 x 3584).  Host only.
+ */
+w4_status w4_gemm_workspace_size(int64_t m, int64_t n, int64_t k, int32_t group, size_t* bytes);
+
+/*
  * Prefill GEMM over a block of m prompt tokens (the pages report the
  * first-token latency of a 512-token prompt: "How To Build Your Own LLM
  * Runtime From Scratch", aitrending.vip, "Technical Details",
  * performance-metrics bullet): y[t][j] = sum_k x[t][k] * w[j][k] for every
  * token row t < m and weight row j < n, with w = (q - 8) * s as for w4_gemv.
  * The weights are dequantized to fp16 (rounded to nearest even) and
- * multiplied on the matrix cores with fp32 accumulation.  Device,
- * asynchronous on `stream`.
+ * multiplied on the matrix cores with fp32 accumulation; split-k partials
+ * are summed in a fixed order, so results are deterministic.  Device,
+ * asynchronous on `stream` (one kernel, or two when split).
  *   packed_w, packed_s  device, from w4_pack(..., W4_LAYOUT_PLAIN, ...);
  *   x  device, fp16 [m][k] row-major (16-byte aligned);
- *   y  device, fp32 [m][n] row-major (4-byte aligned), written in full.
+ *   y  device, fp32 [m][n] row-major (4-byte aligned), written in full;
+ *   workspace  device, >= w4_gemm_workspace_size bytes, 16-byte aligned (may
+ *              be NULL when that size is 0); no initial contents; calls that
+ *              may run at the same time need separate workspaces.
  * Shape rules as for w4_gemv, plus 1 <= m <= 2^20 (W4_ESHAPE otherwise).
  */
-w4_status w4_gemm(const void* packed_w, const void* packed_s, const uint16_t* x, float* y, int64_t m,
-                  int64_t n, int64_t k, int32_t group, void* stream);
+w4_status w4_gemm(const void* packed_w, const void* packed_s, const uint16_t* x, float* y,
+                  void* workspace, size_t workspace_bytes, int64_t m, int64_t n, int64_t k,
+                  int32_t group, void* stream);
 
 /*
  * Prefill gate/up + SiLU: with I = n_total / 2, for every token row t,

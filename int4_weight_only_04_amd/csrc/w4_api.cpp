@@ -110,6 +110,16 @@ w4_status validate_gemm(const GemmCall& c, const char* who)
     return W4_OK;
 }
 
+w4_status check_gemm_workspace(const GemmCall& c, size_t ws_bytes, const char* who)
+{
+    const size_t need = gemm_workspace_bytes(c.epi, c.m, c.n, c.k);
+    if (need == 0) return W4_OK;
+    if (!c.ws) return fail(W4_EINVAL, "%s: this shape needs a workspace of %zu bytes", who, need);
+    if (ws_bytes < need) return fail(W4_EINVAL, "%s: workspace of %zu bytes, need %zu", who, ws_bytes, need);
+    if (!aligned16(c.ws)) return fail(W4_EALIGN, "%s: workspace must be 16-byte aligned", who);
+    return W4_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -238,12 +248,29 @@ w4_status w4_gemv_gateup_silu(const void* packed_w, const void* packed_s, const 
     }
 }
 
-w4_status w4_gemm(const void* packed_w, const void* packed_s, const uint16_t* x, float* y, int64_t m,
-                  int64_t n, int64_t k, int32_t group, void* stream)
+w4_status w4_gemm_workspace_size(int64_t m, int64_t n, int64_t k, int32_t group, size_t* bytes)
 {
     try {
-        GemmCall c{packed_w, packed_s, x, y, m, n, k, group, kEpiPlain};
+        if (!bytes) return fail(W4_EINVAL, "w4_gemm_workspace_size: null output");
+        w4_status st = check_shape(n, k, group, false, "w4_gemm_workspace_size");
+        if (st != W4_OK) return st;
+        if (m < 1 || m > ((int64_t)1 << 20))
+            return fail(W4_ESHAPE, "w4_gemm_workspace_size: m=%lld must be in [1, 2^20]", (long long)m);
+        *bytes = gemm_workspace_bytes(kEpiPlain, m, n, k);
+        return ok();
+    } catch (...) {
+        return fail(W4_EINVAL, "w4_gemm_workspace_size: internal exception");
+    }
+}
+
+w4_status w4_gemm(const void* packed_w, const void* packed_s, const uint16_t* x, float* y, void* workspace,
+                  size_t workspace_bytes, int64_t m, int64_t n, int64_t k, int32_t group, void* stream)
+{
+    try {
+        GemmCall c{packed_w, packed_s, x, y, workspace, m, n, k, group, kEpiPlain};
         w4_status st = validate_gemm(c, "w4_gemm");
+        if (st != W4_OK) return st;
+        st = check_gemm_workspace(c, workspace_bytes, "w4_gemm");
         if (st != W4_OK) return st;
         hipError_t err = launch_gemm(c, static_cast<hipStream_t>(stream));
         if (err != hipSuccess) return hip_fail(err, "w4_gemm launch");
@@ -258,7 +285,7 @@ w4_status w4_gemm_gateup_silu(const void* packed_w, const void* packed_s, const 
                               void* stream)
 {
     try {
-        GemmCall c{packed_w, packed_s, x, h, m, n_total, k, group, kEpiGateUp};
+        GemmCall c{packed_w, packed_s, x, h, nullptr, m, n_total, k, group, kEpiGateUp};
         w4_status st = validate_gemm(c, "w4_gemm_gateup_silu");
         if (st != W4_OK) return st;
         hipError_t err = launch_gemm(c, static_cast<hipStream_t>(stream));

@@ -38,6 +38,7 @@ struct GemmArgs {
     int32_t ng;          // k / G
     int32_t gshift;      // log2(G / 8)
     int32_t steps;       // ceil(kb / 8): k steps of 64 inputs
+    int32_t splits;      // k ranges (blockIdx.z); > 1 writes fp32 partials [splits][m][n]
 };
 
 constexpr int kStepK = 64;                  // inputs per k step
@@ -77,18 +78,20 @@ __device__ __forceinline__ u32x4_t dequant_word(uint32_t d, uint32_t s2)
 // for gate/up its two n blocks are a gate block and the up block of the same
 // outputs, so both land in the same lanes and registers.
 //
-// Pipeline: the global loads of k step s+4 go out while step s is computed
-// (a ring of 4 register slots, the loop unrolled by 4 so every slot index is a
-// constant), and the LDS tiles are double-buffered, so one barrier per k step
-// separates a step's LDS writes from its MFMA reads.  Loads are never
+// Pipeline: the global loads of k step s+RING go out while step s is
+// computed (a ring of RING register slots, the loop unrolled by RING so every
+// slot index is a constant), and the LDS tiles are double-buffered, so one
+// barrier per k step separates a step's LDS writes from its MFMA reads.  With
+// 128-row tiles a 2-slot ring keeps a wave within 256 registers, so two
+// workgroups share a CU and hide each other's waits.  Loads are never
 // predicated: past-the-end addresses are clamped in bounds and the values
 // masked when stored to LDS (k tail: x and the scale zeroed, so the weight is
 // 0; rows past m are read from the last row and never written out).
-constexpr int kRing = 4;
-
-template <int BM, int BN, int EPI>
-__global__ void __launch_bounds__(kThreads) gemm_w4_kernel(GemmArgs a)
+template <int BM, int BN, int EPI, int RING>
+__global__ void __launch_bounds__(kThreads, 2) gemm_w4_kernel(GemmArgs a)
 {
+    constexpr int kRing = RING;
+    static_assert(RING % 2 == 0, "consecutive k steps alternate LDS buffers by slot parity");
     constexpr int MB = BM / 64;
     constexpr int NB = BN / 64;
     constexpr int XCHUNKS = BM * 8 / kThreads;          // 16-B chunks of X per thread per step
@@ -139,8 +142,13 @@ __global__ void __launch_bounds__(kThreads) gemm_w4_kernel(GemmArgs a)
     };
     Slot ring[kRing];
 
+    // k range of this split
+    const int s_begin = (int)((int64_t)blockIdx.z * a.steps / a.splits);
+    const int s_end = (int)((int64_t)(blockIdx.z + 1) * a.steps / a.splits);
+    const int nsteps = s_end - s_begin;
+
     auto issue = [&](Slot& sl, int step) {
-        if (step >= a.steps) step = a.steps - 1;  // in bounds, never stored
+        if (step >= s_end) step = s_end - 1;  // in bounds, never stored
         const int blk0 = step * 8;
 #pragma unroll
         for (int i = 0; i < XCHUNKS; ++i) {
@@ -212,27 +220,27 @@ __global__ void __launch_bounds__(kThreads) gemm_w4_kernel(GemmArgs a)
     };
 
 #pragma unroll
-    for (int u = 0; u < kRing; ++u) issue(ring[u], u);
+    for (int u = 0; u < kRing; ++u) issue(ring[u], s_begin + u);
     // whole groups of kRing steps: a branch-free body, so the compiler can wait
     // for exactly one slot's loads before each LDS store
-    const int whole = a.steps - a.steps % kRing;
+    const int whole = nsteps - nsteps % kRing;
     for (int base = 0; base < whole; base += kRing) {
 #pragma unroll
         for (int u = 0; u < kRing; ++u) {
             // keep each step's work in place: hoisting a later slot's dequant
             // above this point would make it wait for that slot's loads
             __builtin_amdgcn_sched_barrier(0);
-            lstore(ring[u], base + u, u & 1);
-            issue(ring[u], base + u + kRing);
+            lstore(ring[u], s_begin + base + u, u & 1);
+            issue(ring[u], s_begin + base + u + kRing);
             __syncthreads();
             mfma_step(u & 1);
         }
     }
-    // the last steps % kRing steps (their slots are the first ones of the ring)
+    // the last nsteps % kRing steps (their slots are the first ones of the ring)
 #pragma unroll
     for (int u = 0; u < kRing - 1; ++u) {
-        if (whole + u < a.steps) {
-            lstore(ring[u], whole + u, u & 1);
+        if (whole + u < nsteps) {
+            lstore(ring[u], s_begin + whole + u, u & 1);
             __syncthreads();
             mfma_step(u & 1);
         }
@@ -259,10 +267,23 @@ __global__ void __launch_bounds__(kThreads) gemm_w4_kernel(GemmArgs a)
 #pragma unroll
                 for (int j = 0; j < NB; ++j) {
                     const int64_t col = c0 + wn * (BN / 2) + j * 32 + col_in;
-                    if (col < a.n) reinterpret_cast<float*>(a.out)[row * a.n + col] = acc[i][j][r];
+                    if (col < a.n)
+                        reinterpret_cast<float*>(a.out)[(int64_t)blockIdx.z * a.m * a.n + row * a.n + col] = acc[i][j][r];
                 }
             }
         }
+    }
+}
+
+// y = sum of the split partials, in split order (deterministic).
+__global__ void __launch_bounds__(256) gemm_reduce_kernel(const float* __restrict__ part, float* __restrict__ y,
+                                                          int64_t count, int32_t splits)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride) {
+        float t = part[i];
+        for (int s = 1; s < splits; ++s) t += part[(int64_t)s * count + i];
+        y[i] = t;
     }
 }
 
@@ -294,13 +315,16 @@ GemmPlan make_gemm_plan(const GemmCall& c)
     const GemmShape sh = choose_gemm_shape(c.epi, c.m, c.n);
     const int64_t cols = gateup ? c.n / 2 : c.n;
     const int64_t per_tile = gateup ? sh.bn / 2 : sh.bn;
-    p.grid = dim3((unsigned)((cols + per_tile - 1) / per_tile), (unsigned)((c.m + sh.bm - 1) / sh.bm));
+    a.splits = gemm_splits(c.epi, c.m, c.n, c.k);
+    if (a.splits > 1) a.out = c.ws;
+    p.grid = dim3((unsigned)((cols + per_tile - 1) / per_tile), (unsigned)((c.m + sh.bm - 1) / sh.bm),
+                  (unsigned)a.splits);
     if (gateup)
-        p.fn = sh.bm == 128 ? reinterpret_cast<const void*>(&gemm_w4_kernel<128, 128, kEpiGateUp>)
-                            : reinterpret_cast<const void*>(&gemm_w4_kernel<64, 128, kEpiGateUp>);
+        p.fn = sh.bm == 128 ? reinterpret_cast<const void*>(&gemm_w4_kernel<128, 128, kEpiGateUp, 2>)
+                            : reinterpret_cast<const void*>(&gemm_w4_kernel<64, 128, kEpiGateUp, 4>);
     else
-        p.fn = sh.bm == 128 ? reinterpret_cast<const void*>(&gemm_w4_kernel<128, 128, kEpiPlain>)
-                            : reinterpret_cast<const void*>(&gemm_w4_kernel<64, 128, kEpiPlain>);
+        p.fn = sh.bm == 128 ? reinterpret_cast<const void*>(&gemm_w4_kernel<128, 128, kEpiPlain, 2>)
+                            : reinterpret_cast<const void*>(&gemm_w4_kernel<64, 128, kEpiPlain, 4>);
     return p;
 }
 
@@ -311,7 +335,17 @@ hipError_t launch_gemm(const GemmCall& c, hipStream_t stream)
     GemmPlan p = make_gemm_plan(c);
     if (!p.fn) return hipErrorInvalidValue;
     void* args[] = {&p.args};
-    return hipLaunchKernel(p.fn, p.grid, dim3(kThreads), args, 0, stream);
+    hipError_t err = hipLaunchKernel(p.fn, p.grid, dim3(kThreads), args, 0, stream);
+    if (err != hipSuccess || p.args.splits == 1) return err;
+    const float* part = static_cast<const float*>(c.ws);
+    float* y = static_cast<float*>(c.out);
+    int64_t count = c.m * c.n;
+    int32_t splits = p.args.splits;
+    void* rargs[] = {&part, &y, &count, &splits};
+    int64_t blocks = (count + 255) / 256;
+    if (blocks > 2048) blocks = 2048;
+    return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_reduce_kernel), dim3((unsigned)blocks), dim3(256),
+                           rargs, 0, stream);
 }
 
 }  // namespace w4i

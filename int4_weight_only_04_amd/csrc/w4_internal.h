@@ -39,6 +39,7 @@ struct GemmCall {
     const void* ps;
     const void* x;
     void* out;
+    void* ws;            // split-k partials (plain only, when gemm_splits > 1)
     int64_t m;
     int64_t n;
     int64_t k;
@@ -62,6 +63,30 @@ inline GemmShape choose_gemm_shape(int32_t epi, int64_t m, int64_t n)
     const int64_t per_tile = epi == kEpiGateUp ? 64 : 128;
     const int64_t tiles128 = ((m + 127) / 128) * ((cols + per_tile - 1) / per_tile);
     return tiles128 >= 512 ? GemmShape{128, 128} : GemmShape{64, 128};
+}
+
+// Split-k factor: when the output tiles give fewer than 256 workgroups (one
+// per CU), the k range is split so the grid covers the chip, at most 8 ways
+// and at least one 64-input step per split; the partials are summed in a
+// fixed order by a second kernel.  Gate/up is never split (its SiLU needs the
+// full sums).
+inline int32_t gemm_splits(int32_t epi, int64_t m, int64_t n, int64_t k)
+{
+    if (epi == kEpiGateUp) return 1;
+    const GemmShape sh = choose_gemm_shape(epi, m, n);
+    const int64_t wgs = ((n + sh.bn - 1) / sh.bn) * ((m + sh.bm - 1) / sh.bm);
+    if (wgs >= 256) return 1;
+    const int64_t steps = (k / 8 + 7) / 8;
+    int64_t s = (256 + wgs - 1) / wgs;
+    if (s > 8) s = 8;
+    if (s > steps) s = steps;
+    return (int32_t)(s < 1 ? 1 : s);
+}
+
+inline size_t gemm_workspace_bytes(int32_t epi, int64_t m, int64_t n, int64_t k)
+{
+    const int32_t s = gemm_splits(epi, m, n, k);
+    return s > 1 ? (size_t)s * (size_t)m * (size_t)n * 4 : 0;
 }
 
 // Launch one GEMV on `stream` (shape already validated by the caller); the

@@ -22,7 +22,7 @@ PROJ_PLAIN, PROJ_GATEUP_SILU, PROJ_LMHEAD_ARGMAX = 0, 1, 2
 
 EXPORTED = (
     "w4_status_string", "w4_last_error", "w4_abi_version", "w4_packed_size", "w4_pack",
-    "w4_gemv_workspace_size", "w4_gemv", "w4_gemv_gateup_silu", "w4_gemm", "w4_gemm_gateup_silu",
+    "w4_gemv_workspace_size", "w4_gemv", "w4_gemv_gateup_silu", "w4_gemm_workspace_size", "w4_gemm", "w4_gemm_gateup_silu",
     "w4_decode_linear_sweep_create", "w4_decode_linear_sweep", "w4_decode_linear_sweep_destroy",
 )
 
@@ -78,8 +78,10 @@ def lib():
     L.w4_gemv.argtypes = [vp, vp, vp, vp, vp, vp, sz, i64, i64, i32, vp]
     L.w4_gemv_gateup_silu.restype = i32
     L.w4_gemv_gateup_silu.argtypes = [vp, vp, vp, vp, i64, i64, i32, vp]
+    L.w4_gemm_workspace_size.restype = i32
+    L.w4_gemm_workspace_size.argtypes = [i64, i64, i64, i32, ctypes.POINTER(sz)]
     L.w4_gemm.restype = i32
-    L.w4_gemm.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, vp]
+    L.w4_gemm.argtypes = [vp, vp, vp, vp, vp, sz, i64, i64, i64, i32, vp]
     L.w4_gemm_gateup_silu.restype = i32
     L.w4_gemm_gateup_silu.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, vp]
     L.w4_decode_linear_sweep_create.restype = i32
@@ -197,14 +199,23 @@ def gemv_gateup_silu(packed_w, packed_s, x, h, n_total: int, k: int, group: int,
                                      n_total, k, group, _stream(stream)), "w4_gemv_gateup_silu")
 
 
-def gemm(packed_w, packed_s, x, y, m: int, n: int, k: int, group: int, stream=None):
-    """Prefill product y[m, n] (fp32) = x[m, k] (fp16) times W^T."""
+def gemm_workspace_size(m: int, n: int, k: int, group: int) -> int:
+    out = ctypes.c_size_t()
+    _check(lib().w4_gemm_workspace_size(m, n, k, group, ctypes.byref(out)), "w4_gemm_workspace_size")
+    return int(out.value)
+
+
+def gemm(packed_w, packed_s, x, y, m: int, n: int, k: int, group: int, workspace=None, stream=None):
+    """Prefill product y[m, n] (fp32) = x[m, k] (fp16) times W^T; `workspace`
+    (uint8, gemm_workspace_size bytes) is needed when that size is nonzero."""
     import torch
     wb, sb = packed_size(n, k, group, "plain")
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().w4_gemm(_dev_ptr(packed_w, "packed_w", torch.uint8, wb),
                          _dev_ptr(packed_s, "packed_s", torch.uint8, sb),
                          _dev_ptr(x, "x", torch.float16, m * k),
                          _dev_ptr(y, "y", torch.float32, m * n),
+                         _dev_ptr(workspace, "workspace"), ws_bytes,
                          m, n, k, group, _stream(stream)), "w4_gemm")
 
 

@@ -153,19 +153,34 @@ def test_gemm_validation_before_launch():
     """Prefill GEMM argument checks run before any device call."""
     L = w4.lib()
     A = 1 << 20
-    assert L.w4_gemm(None, A, A, A, 8, 4, 64, 32, None) == w4.EINVAL
-    assert L.w4_gemm(A, A, A, None, 8, 4, 64, 32, None) == w4.EINVAL
-    assert L.w4_gemm(A, A, A + 2, A, 8, 4, 64, 32, None) == w4.EALIGN
-    assert L.w4_gemm(A + 8, A, A, A, 8, 4, 64, 32, None) == w4.EALIGN
-    assert L.w4_gemm(A, A, A, A + 2, 8, 4, 64, 32, None) == w4.EALIGN
-    assert L.w4_gemm(A, A, A, A, 0, 4, 64, 32, None) == w4.ESHAPE
-    assert L.w4_gemm(A, A, A, A, (1 << 20) + 1, 4, 64, 32, None) == w4.ESHAPE
-    assert L.w4_gemm(A, A, A, A, 8, 4, 96, 64, None) == w4.ESHAPE
-    assert L.w4_gemm(A, A, A, A, 8, 0, 64, 32, None) == w4.ESHAPE
+    W = 1 << 30  # a workspace size large enough for the small shapes below
+    assert L.w4_gemm(None, A, A, A, A, W, 8, 4, 64, 32, None) == w4.EINVAL
+    assert L.w4_gemm(A, A, A, None, A, W, 8, 4, 64, 32, None) == w4.EINVAL
+    assert L.w4_gemm(A, A, A + 2, A, A, W, 8, 4, 64, 32, None) == w4.EALIGN
+    assert L.w4_gemm(A + 8, A, A, A, A, W, 8, 4, 64, 32, None) == w4.EALIGN
+    assert L.w4_gemm(A, A, A, A + 2, A, W, 8, 4, 64, 32, None) == w4.EALIGN
+    assert L.w4_gemm(A, A, A, A, A, W, 0, 4, 64, 32, None) == w4.ESHAPE
+    assert L.w4_gemm(A, A, A, A, A, W, (1 << 20) + 1, 4, 64, 32, None) == w4.ESHAPE
+    assert L.w4_gemm(A, A, A, A, A, W, 8, 4, 96, 64, None) == w4.ESHAPE
+    assert L.w4_gemm(A, A, A, A, A, W, 8, 0, 64, 32, None) == w4.ESHAPE
+    # a split shape without (or with too small, or misaligned) workspace
+    need = w4.gemm_workspace_size(512, 3584, 18944, 128)
+    assert need > 0
+    assert L.w4_gemm(A, A, A, A, None, 0, 512, 3584, 18944, 128, None) == w4.EINVAL
+    assert L.w4_gemm(A, A, A, A, A, need - 1, 512, 3584, 18944, 128, None) == w4.EINVAL
+    assert L.w4_gemm(A, A, A, A, A + 4, need, 512, 3584, 18944, 128, None) == w4.EALIGN
     assert L.w4_gemm_gateup_silu(A, A, A, A, 8, 5, 64, 32, None) == w4.ESHAPE
     assert L.w4_gemm_gateup_silu(A, A, A, A + 1, 8, 6, 64, 32, None) == w4.EALIGN
     assert L.w4_gemm_gateup_silu(A, None, A, A, 8, 6, 64, 32, None) == w4.EINVAL
     assert "w4_gemm_gateup_silu" in w4.last_error()
+
+
+def test_gemm_workspace_sizes():
+    # split-k partials: splits x m x n fp32; no split once the grid covers the chip
+    assert w4.gemm_workspace_size(512, 4608, 3584, 128) == 0            # 288 tiles of 64 x 128
+    assert w4.gemm_workspace_size(512, 3584, 18944, 128) == 2 * 512 * 3584 * 4
+    assert w4.gemm_workspace_size(4096, 37888, 3584, 128) == 0
+    assert w4.gemm_workspace_size(1, 64, 64, 64) == 0  # one k step: nothing to split
 
 
 def test_sweep_create_validation():

@@ -37,7 +37,9 @@ def gemm_plain(pw, ps, xm, n, k, group):
     w4 = _w4()
     m = xm.shape[0]
     y = torch.full((m, n), float("nan"), dtype=torch.float32, device="cuda")
-    w4.gemm(dev_u8(pw), dev_u8(ps), dev_f16(xm), y, m, n, k, group)
+    wsb = w4.gemm_workspace_size(m, n, k, group)
+    ws = torch.full((max(wsb, 16),), 0xFF, dtype=torch.uint8, device="cuda") if wsb else None
+    w4.gemm(dev_u8(pw), dev_u8(ps), dev_f16(xm), y, m, n, k, group, workspace=ws)
     torch.cuda.synchronize()
     return y.cpu().numpy().astype(np.float64)
 
