@@ -43,6 +43,8 @@ METRIC = "achieved HBM GB/s (% of peak) and ms per 28-layer+lm_head INT4 linear 
 PREFILL_METRIC = "prefill TFLOP/s (% of fp16 MFMA peak) and ms per 28-layer 512-token INT4 linear sweep"
 KERNEL_SRC = os.path.join(ROOT, "int4_weight_only_04_amd", "csrc", "w4_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gateup_silu_37888x3584.json")
+GEMM_SRC = os.path.join(ROOT, "int4_weight_only_04_amd", "csrc", "w4_gemm.hip")
+GEMM_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_gateup_512x37888x3584.json")
 
 
 def algorithmic_bytes(kind: str, n: int, k: int, group: int) -> int:
@@ -92,20 +94,20 @@ def build_sweep(layers: int = synthetic.LAYERS, device: str = "cuda"):
     return specs, projs
 
 
-def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
+def kernel_source_hash(path: str = KERNEL_SRC) -> str:
+    with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def read_traffic(launch_bytes_alg: int):
+def read_traffic(launch_bytes_alg: int = 0, path: str = TRAFFIC_FILE, src: str = KERNEL_SRC):
     """HBM bytes per launch of the dominant kernel from the committed counter
     summary, or None if absent or taken on another kernel source."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+    if t.get("kernel_source_sha256_16") != kernel_source_hash(src):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -346,8 +348,10 @@ def run_prefill(args) -> int:
             "peak": MFMA_F16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(gu_tflops / MFMA_F16_PEAK_TFLOPS, 4),
-            "traffic": None,
+            "traffic": read_traffic(path=GEMM_TRAFFIC_FILE, src=GEMM_SRC),
             "algorithmic_flops_per_launch": gu_flops,
+            "algorithmic_bytes_per_launch": (gp.n * gp.k // 2 + 2 * gp.n * (gp.k // gp.group)
+                                             + 2 * synthetic.PROMPT * gp.k + synthetic.PROMPT * gp.n),
             "avg_launch_us": round(gu_ms * 1e3, 3),
             "launches_timed": reps * n_gu,
         },
