@@ -13,6 +13,7 @@ inputs per row are the workload definition's format, the pages being silent):
     w[n, k] = (q[n, k] - 8) * s[n, k // G]
     y[n]    = sum_k w[n, k] * x[k]          (fp64, exact products)
     Y[m, n] = sum_k X[m, k] * w[n, k]       (prefill: one y per token row)
+    o[h, :] = softmax_t(scale q[h] . K[t, g(h)]) V[t, g(h)]   (decode attention, paged KV)
     A[n]    = sum_k |w[n, k] * x[k]|
     h[j]    = silu(y[j]) * y[I + j],  silu(t) = t / (1 + exp(-t))
     argmax  = lowest index of max y
@@ -68,6 +69,8 @@ class Oracle:
         lib.oracle_gemm.argtypes = [p, p, p, i64, i64, i64, i32, p, p]
         lib.oracle_gemm_packed.restype = None
         lib.oracle_gemm_packed.argtypes = [p, p, p, i64, i64, i32, i32, p, i64, p, i64, p, p]
+        lib.oracle_attn_decode.restype = None
+        lib.oracle_attn_decode.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, ctypes.c_double, p, p]
         lib.oracle_silu.restype = ctypes.c_double
         lib.oracle_silu.argtypes = [ctypes.c_double]
         lib.oracle_silu_gate.restype = None
@@ -184,6 +187,25 @@ class Oracle:
                                     _ptr(mrows), mrows.size, _ptr(ncols), ncols.size, _ptr(y), _ptr(a))
         return y, a
 
+    def attn_decode(self, q_bits: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
+                    page_table: np.ndarray, ctx: int, n_kv: int, page: int, scale: float):
+        """(o, A) float64 [n_heads, dim]: softmax(scale * q K^T) V of one token
+        over the first ctx cached tokens; caches fp16 bits
+        [num_pages, n_kv, page, dim], q fp16 bits [n_heads, dim]."""
+        q_bits = np.ascontiguousarray(q_bits, dtype=np.uint16)
+        k_cache = np.ascontiguousarray(k_cache, dtype=np.uint16)
+        v_cache = np.ascontiguousarray(v_cache, dtype=np.uint16)
+        page_table = np.ascontiguousarray(page_table, dtype=np.int32)
+        n_heads, dim = q_bits.shape
+        assert k_cache.shape == v_cache.shape and k_cache.shape[1:] == (n_kv, page, dim)
+        assert n_heads % n_kv == 0 and 1 <= ctx <= page_table.size * page
+        assert page_table[: (ctx + page - 1) // page].max() < k_cache.shape[0]
+        o = np.empty((n_heads, dim), np.float64)
+        a = np.empty((n_heads, dim), np.float64)
+        self.lib.oracle_attn_decode(_ptr(q_bits), _ptr(k_cache), _ptr(v_cache), _ptr(page_table), ctx, n_heads,
+                                    n_kv, dim, page, float(scale), _ptr(o), _ptr(a))
+        return o, a
+
     def silu(self, t: float) -> float:
         return self.lib.oracle_silu(float(t))
 
@@ -248,6 +270,10 @@ def gemm_packed(pw, ps, xm_bits, n, k, group, gateup=False, mrows=None, ncols=No
 
 def gemv_packed(pw, ps, x_bits, n, k, group, gateup=False, rows=None):
     return default().gemv_packed(pw, ps, x_bits, n, k, group, gateup, rows)
+
+
+def attn_decode(q_bits, k_cache, v_cache, page_table, ctx, n_kv, page, scale):
+    return default().attn_decode(q_bits, k_cache, v_cache, page_table, ctx, n_kv, page, scale)
 
 
 def silu(t):

@@ -26,6 +26,8 @@
  * significant bits), and the sums are accumulated in double in increasing k,
  * so y is the exact dot product up to the rounding of a plain fp64 sum.
  *
+ * Decode attention over a paged KV cache: see oracle_attn_decode.
+ *
  * Prefill (a block of m prompt tokens through the same layers):
  *     Y[m][n] = sum_k X[m][k] * w[n][k]                     (one y per token)
  *
@@ -274,6 +276,63 @@ void oracle_gemm_packed(const uint8_t* pw, const uint8_t* ps, const uint16_t* xm
     for (int64_t i = 0; i < nm; ++i) {
         int64_t m = mrows[i];
         oracle_gemv_packed_rows(pw, ps, xm + m * k, n, k, group, gateup, ncols, nn, y + i * nn, a + i * nn);
+    }
+}
+
+/* Decode attention over a paged KV cache (the step between the QKV and
+ * o_proj projections: "How To Build Your Own LLM Runtime From Scratch",
+ * aitrending.vip, "Technical Details", architecture bullet -- paged KV cache
+ * and attention; noticiai.com.br, "As tres licoes", lesson 1 -- the softmax
+ * runs across KV pages and must stay correct at a page's tail).  Plain
+ * scaled dot-product attention of one new token, with grouped KV heads:
+ *
+ *   g(h)     = h / (n_heads / n_kv)                  KV head of query head h
+ *   s[h][t]  = scale * sum_d q[h][d] * K[t][g(h)][d]   for t < ctx
+ *   p[h][t]  = exp(s[h][t] - max_t s[h][t]) / sum_t exp(s[h][t] - max_t s[h][t])
+ *   o[h][d]  = sum_t p[h][t] * V[t][g(h)][d]
+ *   A[h][d]  = sum_t p[h][t] * |V[t][g(h)][d]|        (tolerance scale)
+ *
+ * Token t lives in physical page page_table[t / page] at slot t % page; a
+ * cache is fp16 [num_pages][n_kv][page][dim].  q is fp16 [n_heads][dim].
+ * Everything in double. */
+void oracle_attn_decode(const uint16_t* q, const uint16_t* kc, const uint16_t* vc, const int32_t* page_table,
+                        int32_t ctx, int32_t n_heads, int32_t n_kv, int32_t dim, int32_t page, double scale,
+                        double* o, double* a)
+{
+    int32_t group = n_heads / n_kv;
+    for (int32_t h = 0; h < n_heads; ++h) {
+        int32_t g = h / group;
+        double mx = -HUGE_VAL;
+        for (int32_t t = 0; t < ctx; ++t) {
+            int64_t base = (((int64_t)page_table[t / page] * n_kv + g) * page + t % page) * dim;
+            double sdot = 0.0;
+            for (int32_t d = 0; d < dim; ++d)
+                sdot += oracle_half_to_double(q[(int64_t)h * dim + d]) * oracle_half_to_double(kc[base + d]);
+            sdot *= scale;
+            if (sdot > mx) mx = sdot;
+        }
+        double den = 0.0;
+        for (int32_t d = 0; d < dim; ++d) {
+            o[(int64_t)h * dim + d] = 0.0;
+            a[(int64_t)h * dim + d] = 0.0;
+        }
+        for (int32_t t = 0; t < ctx; ++t) {
+            int64_t base = (((int64_t)page_table[t / page] * n_kv + g) * page + t % page) * dim;
+            double sdot = 0.0;
+            for (int32_t d = 0; d < dim; ++d)
+                sdot += oracle_half_to_double(q[(int64_t)h * dim + d]) * oracle_half_to_double(kc[base + d]);
+            double w = exp(sdot * scale - mx);
+            den += w;
+            for (int32_t d = 0; d < dim; ++d) {
+                double v = oracle_half_to_double(vc[base + d]);
+                o[(int64_t)h * dim + d] += w * v;
+                a[(int64_t)h * dim + d] += w * fabs(v);
+            }
+        }
+        for (int32_t d = 0; d < dim; ++d) {
+            o[(int64_t)h * dim + d] /= den;
+            a[(int64_t)h * dim + d] /= den;
+        }
     }
 }
 

@@ -13,7 +13,10 @@ routine fixes:
   * closed forms (zero point, constant nibbles, one-hot activations, one-hot
     token rows selecting weight columns);
   * exact invariants (power-of-two scaling, A >= |y|);
-  * silu against scipy's logistic function, argmax against numpy.argmax.
+  * silu against scipy's logistic function, argmax against numpy.argmax;
+  * decode attention against scipy's softmax on the gathered KV cache, and its
+    closed forms (uniform weights, one token, one dominating key) and
+    page-layout invariance.
 
 The same pins run against deliberately mutated copies of the oracle
 (test_oracle_mutants.py) to show that each plausible mistake trips one.
@@ -321,6 +324,95 @@ def pin_gemm_rows_and_subsets(orc):
     nc = np.array([13, 2, 2, 0, 7], np.int64)
     ys, as_ = orc.gemm_packed(pw, ps, xm, n, k, group, False, mrows=mr, ncols=nc)
     assert np.array_equal(ys, y[np.ix_(mr, nc)]) and np.array_equal(as_, a[np.ix_(mr, nc)])
+
+
+def _attn_numpy(q_bits, kc, vc, table, ctx, n_kv, page, scale):
+    """softmax(scale Q K^T) V with numpy/scipy on the gathered cache."""
+    n_heads, dim = q_bits.shape
+    qf = q_bits.view(np.float16).astype(np.float64)
+    t = np.arange(ctx)
+    kf = kc.view(np.float16).astype(np.float64)[table[t // page], :, t % page, :]   # [ctx, n_kv, dim]
+    vf = vc.view(np.float16).astype(np.float64)[table[t // page], :, t % page, :]
+    group = n_heads // n_kv
+    o = np.empty((n_heads, dim))
+    a = np.empty((n_heads, dim))
+    for h in range(n_heads):
+        sc = scale * (kf[:, h // group, :] @ qf[h])
+        p = scipy.special.softmax(sc)
+        o[h] = p @ vf[:, h // group, :]
+        a[h] = p @ np.abs(vf[:, h // group, :])
+    return o, a
+
+
+def _attn_inputs(rng, n_heads, n_kv, dim, page, pages, ctx):
+    q = _h(rng.standard_normal((n_heads, dim)))
+    kc = _h(rng.standard_normal((pages, n_kv, page, dim)))
+    vc = _h(rng.standard_normal((pages, n_kv, page, dim)))
+    table = rng.permutation(pages).astype(np.int32)[: (ctx + page - 1) // page]
+    return q, kc, vc, table
+
+
+def pin_attn_vs_numpy(orc):
+    """Decode attention against numpy/scipy softmax on the gathered cache, with
+    grouped KV heads, permuted page tables and ragged page tails."""
+    rng = np.random.default_rng(37)
+    for n_heads, n_kv, dim, page, ctx in ((4, 1, 16, 4, 13), (28, 4, 128, 16, 37), (6, 2, 8, 8, 8), (3, 3, 32, 16, 1)):
+        pages = (ctx + page - 1) // page + 3
+        q, kc, vc, table = _attn_inputs(rng, n_heads, n_kv, dim, page, pages, ctx)
+        scale = 1.0 / np.sqrt(dim)
+        o, a = orc.attn_decode(q, kc, vc, table, ctx, n_kv, page, scale)
+        ro, ra = _attn_numpy(q, kc, vc, table, ctx, n_kv, page, scale)
+        assert np.allclose(o, ro, rtol=1e-12, atol=1e-13), (n_heads, n_kv, ctx)
+        assert np.allclose(a, ra, rtol=1e-12, atol=1e-13), (n_heads, n_kv, ctx)
+
+
+def pin_attn_closed_forms(orc):
+    """q = 0 averages V uniformly; one cached token returns its V exactly; one
+    key that dominates by a huge score returns its V exactly (and needs the
+    max subtracted before exp to stay finite)."""
+    rng = np.random.default_rng(41)
+    n_heads, n_kv, dim, page, ctx = 4, 2, 16, 8, 21
+    q, kc, vc, table = _attn_inputs(rng, n_heads, n_kv, dim, page, 4, ctx)
+    t = np.arange(ctx)
+    vf = vc.view(np.float16).astype(np.float64)[table[t // page], :, t % page, :]
+    o, a = orc.attn_decode(np.zeros_like(q), kc, vc, table, ctx, n_kv, page, 0.25)
+    for h in range(n_heads):
+        assert np.allclose(o[h], vf[:, h // 2, :].mean(axis=0), rtol=1e-13, atol=1e-15)
+        assert np.allclose(a[h], np.abs(vf[:, h // 2, :]).mean(axis=0), rtol=1e-13, atol=1e-15)
+    o, _ = orc.attn_decode(q, kc, vc, table, 1, n_kv, page, 0.25)
+    for h in range(n_heads):
+        assert np.array_equal(o[h], vf[0, h // 2, :])
+    # token 11 gets key = 64 * q-direction: its score exceeds the others by far more than exp's range
+    q1 = _h(np.ones((n_heads, dim)))
+    kc2 = kc.copy()
+    tstar = 11
+    kc2[table[tstar // page], :, tstar % page, :] = _h(np.full((n_kv, dim), 64.0))
+    o, _ = orc.attn_decode(q1, kc2, vc, table, ctx, n_kv, page, 1.0)
+    assert np.all(np.isfinite(o))
+    for h in range(n_heads):
+        assert np.array_equal(o[h], vf[tstar, h // 2, :])
+
+
+def pin_attn_page_layouts(orc):
+    """The same logical cache laid out with another page size and another page
+    order gives the same result bit for bit (the sum runs in token order)."""
+    rng = np.random.default_rng(43)
+    n_heads, n_kv, dim, ctx = 8, 2, 32, 45
+    q = _h(rng.standard_normal((n_heads, dim)))
+    k_log = _h(rng.standard_normal((ctx, n_kv, dim)))
+    v_log = _h(rng.standard_normal((ctx, n_kv, dim)))
+    outs = []
+    for page, seed in ((4, 1), (16, 2), (64, 3)):
+        npages = (ctx + page - 1) // page
+        table = np.random.default_rng(seed).permutation(npages + 2).astype(np.int32)[:npages]
+        kc = np.zeros((npages + 2, n_kv, page, dim), np.uint16)
+        vc = np.zeros_like(kc)
+        for t in range(ctx):
+            kc[table[t // page], :, t % page, :] = k_log[t]
+            vc[table[t // page], :, t % page, :] = v_log[t]
+        outs.append(orc.attn_decode(q, kc, vc, table, ctx, n_kv, page, 0.2))
+    for o, a in outs[1:]:
+        assert np.array_equal(o, outs[0][0]) and np.array_equal(a, outs[0][1])
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -44,6 +44,11 @@ MUTANTS = [
     ("sizes_scale_bytes", "(k / group) * 8;", "(k / group) * 16;", None),
     ("gemm_x_row_fixed", "oracle_gemv_rows(q, s, xm + m * k,", "oracle_gemv_rows(q, s, xm,", None),
     ("gemm_packed_token_index", "int64_t m = mrows[i];", "int64_t m = i;", None),
+    ("attn_group_map", "int32_t g = h / group;", "int32_t g = h % n_kv;", None),
+    ("attn_no_max", "double w = exp(sdot * scale - mx);", "double w = exp(sdot * scale);", None),
+    ("attn_page_table_ignored", "(int64_t)page_table[t / page] * n_kv", "(int64_t)(t / page) * n_kv", None),
+    ("attn_scale_dropped", "            sdot *= scale;\n", "\n", None),
+    ("attn_abs_dropped", "a[(int64_t)h * dim + d] += w * fabs(v);", "a[(int64_t)h * dim + d] += w * v;", None),
     ("gemm_packed_x_row_fixed", "oracle_gemv_packed_rows(pw, ps, xm + m * k,", "oracle_gemv_packed_rows(pw, ps, xm,", None),
 ]
 
