@@ -183,6 +183,43 @@ w4_status w4_gemm_gateup_silu(const void* packed_w, const void* packed_s, const 
                               uint16_t* h, int64_t m, int64_t n_total, int64_t k, int32_t group,
                               void* stream);
 
+/*
+ * Workspace bytes w4_attn_decode needs: (130 x 4) bytes per query head per
+ * 64-token chunk of max_ctx (about 0.9 MB for 28 heads at 4096).  Host only.
+ */
+w4_status w4_attn_decode_workspace_size(int32_t n_heads, int32_t max_ctx, size_t* bytes);
+
+/*
+ * Decode attention of one new token over a paged KV cache, the step between
+ * the QKV and o_proj projections ("How To Build Your Own LLM Runtime From
+ * Scratch", aitrending.vip, "Technical Details", architecture bullet: paged
+ * KV cache and attention).  For query head h and KV head g = h / (n_heads /
+ * n_kv_heads):
+ *     o[h] = sum_{t < ctx} softmax_t(scale * q[h] . K[t][g]) V[t][g]
+ * with token t in physical page page_table[t / page_size], slot
+ * t % page_size.  fp32 arithmetic, fp16 output (nearest even).  Device,
+ * asynchronous on `stream` (two kernels).
+ *   q           device fp16 [n_heads][128];
+ *   k_cache, v_cache  device fp16 [num_pages][n_kv_heads][page_size][128];
+ *   page_table  device int32, >= ceil(max_ctx / page_size) entries, each in
+ *               [0, num_pages) (an entry outside is clamped into range: a
+ *               wrong result, never a read outside the caches);
+ *   ctx_len     device int32 [1]: tokens in the cache, read by the kernels
+ *               (so a captured graph replays as the context grows), clamped
+ *               to [1, max_ctx];
+ *   out         device fp16 [n_heads][128];
+ *   workspace   device, >= w4_attn_decode_workspace_size(n_heads, max_ctx)
+ *               bytes, 16-byte aligned; no initial contents; calls that may
+ *               run at the same time need separate workspaces.
+ * Shape rules: head_dim == 128; n_heads = 1..8 x n_kv_heads; page_size a
+ * power of two <= 4096; 1 <= max_ctx <= 2^20 (W4_ESHAPE otherwise).
+ */
+w4_status w4_attn_decode(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                         const int32_t* page_table, int32_t num_pages, const int32_t* ctx_len,
+                         int32_t max_ctx, uint16_t* out, int32_t n_heads, int32_t n_kv_heads,
+                         int32_t head_dim, int32_t page_size, float scale, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
 /* One projection of the per-token linear sweep. */
 #define W4_PROJ_PLAIN 0         /* w4_gemv, out = float y[n]                  */
 #define W4_PROJ_GATEUP_SILU 1   /* w4_gemv_gateup_silu, out = fp16 h[n/2]     */

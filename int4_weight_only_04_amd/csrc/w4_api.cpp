@@ -296,6 +296,52 @@ w4_status w4_gemm_gateup_silu(const void* packed_w, const void* packed_s, const 
     }
 }
 
+w4_status w4_attn_decode_workspace_size(int32_t n_heads, int32_t max_ctx, size_t* bytes)
+{
+    try {
+        if (!bytes) return fail(W4_EINVAL, "w4_attn_decode_workspace_size: null output");
+        if (n_heads < 1 || max_ctx < 1 || max_ctx > kAttnMaxCtx)
+            return fail(W4_ESHAPE, "w4_attn_decode_workspace_size: n_heads=%d max_ctx=%d", n_heads, max_ctx);
+        *bytes = attn_workspace_bytes(n_heads, max_ctx);
+        return ok();
+    } catch (...) {
+        return fail(W4_EINVAL, "w4_attn_decode_workspace_size: internal exception");
+    }
+}
+
+w4_status w4_attn_decode(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                         const int32_t* page_table, int32_t num_pages, const int32_t* ctx_len, int32_t max_ctx,
+                         uint16_t* out, int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, int32_t page_size,
+                         float scale, void* workspace, size_t workspace_bytes, void* stream)
+{
+    try {
+        const char* who = "w4_attn_decode";
+        if (!q || !k_cache || !v_cache || !page_table || !ctx_len || !out || !workspace)
+            return fail(W4_EINVAL, "%s: null pointer", who);
+        if (head_dim != kAttnHeadDim) return fail(W4_ESHAPE, "%s: head_dim=%d must be 128", who, head_dim);
+        if (n_kv_heads < 1 || n_heads < n_kv_heads || n_heads % n_kv_heads != 0 || n_heads / n_kv_heads > 8)
+            return fail(W4_ESHAPE, "%s: n_heads=%d must be 1..8 times n_kv_heads=%d", who, n_heads, n_kv_heads);
+        if (page_size < 1 || page_size > 4096 || (page_size & (page_size - 1)) != 0)
+            return fail(W4_ESHAPE, "%s: page_size=%d must be a power of two <= 4096", who, page_size);
+        if (max_ctx < 1 || max_ctx > kAttnMaxCtx || num_pages < 1)
+            return fail(W4_ESHAPE, "%s: max_ctx=%d num_pages=%d", who, max_ctx, num_pages);
+        if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(workspace) ||
+            (reinterpret_cast<uintptr_t>(out) & 1u) || (reinterpret_cast<uintptr_t>(page_table) & 3u) ||
+            (reinterpret_cast<uintptr_t>(ctx_len) & 3u))
+            return fail(W4_EALIGN, "%s: q, caches and workspace must be 16-byte aligned", who);
+        const size_t need = attn_workspace_bytes(n_heads, max_ctx);
+        if (workspace_bytes < need)
+            return fail(W4_EINVAL, "%s: workspace of %zu bytes, need %zu", who, workspace_bytes, need);
+        AttnCall c{q, k_cache, v_cache, page_table, ctx_len, out, workspace, scale, max_ctx, n_heads, n_kv_heads,
+                   page_size, num_pages};
+        hipError_t err = launch_attn(c, static_cast<hipStream_t>(stream));
+        if (err != hipSuccess) return hip_fail(err, "w4_attn_decode launch");
+        return ok();
+    } catch (...) {
+        return fail(W4_EINVAL, "w4_attn_decode: internal exception");
+    }
+}
+
 }  // extern "C"
 
 struct w4_sweep {

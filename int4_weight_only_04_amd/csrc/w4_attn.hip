@@ -1,0 +1,271 @@
+// Decode attention over a paged KV cache: the step between the QKV and o_proj
+// projections of a decode token ("How To Build Your Own LLM Runtime From
+// Scratch", aitrending.vip, "Technical Details", architecture bullet: paged
+// KV cache and attention).  For query head h with KV head g = h / group:
+//
+//   s[t] = scale * q[h] . K[t][g],  p = softmax over t < ctx,  o[h] = sum_t p[t] V[t][g]
+//
+// Token t sits in physical page page_table[t / page] at slot t % page; the
+// caches are fp16 [num_pages][n_kv][page][128].
+//
+// Two kernels.  The first splits the context into chunks of 64 tokens; a
+// workgroup takes one chunk of one KV head, so K and V are read once for all
+// the query heads that share them, and writes the chunk's softmax max, sum
+// and unnormalised fp32 output.  The second merges the chunks in chunk order
+// (deterministic).  The context length is read from device memory, so a
+// captured graph replays unchanged from token to token; the grid is sized for
+// max_ctx and chunks past the context write an empty partial.  A chunk's
+// softmax covers every token in it, the page's tail included: all waves reach
+// every barrier, and tokens past the context are masked, never skipped with
+// an early exit (the barrier-in-a-branch mistake the pages describe corrupted
+// exactly those tails: noticiai.com.br, "As tres licoes", lesson 1).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "w4_internal.h"
+
+namespace w4i {
+namespace {
+
+constexpr int kDim = 128;          // head dimension
+constexpr int kChunk = 64;         // tokens per workgroup
+constexpr int kAttnThreads = 256;  // 4 waves
+
+struct AttnArgs {
+    const uint4* q;          // fp16 [n_heads][128], 16 per head
+    const uint4* kc;         // fp16 cache, 16 uint4 per token row
+    const uint32_t* vc;      // fp16 cache, 64 words per token row
+    const int32_t* table;    // page table
+    const int32_t* ctx_ptr;  // device context length
+    float* part_o;           // [chunks][n_heads][128]
+    float* part_ml;          // [chunks][n_heads][2]: max, sum
+    uint16_t* out;           // fp16 [n_heads][128]
+    float scale;
+    int32_t max_ctx;
+    int32_t n_heads;
+    int32_t n_kv;
+    int32_t page_shift;
+    int32_t num_pages;
+};
+
+__device__ __forceinline__ int clamp_ctx(const AttnArgs& a)
+{
+    int c = *a.ctx_ptr;
+    if (c < 1) c = 1;
+    if (c > a.max_ctx) c = a.max_ctx;
+    return c;
+}
+
+// cache row index (in token rows) of token t of KV head g
+__device__ __forceinline__ int64_t cache_row(const AttnArgs& a, int t, int g)
+{
+    int pg = a.table[t >> a.page_shift];
+    pg = pg < 0 ? 0 : (pg >= a.num_pages ? a.num_pages - 1 : pg);  // never read outside the cache
+    return ((int64_t)pg * a.n_kv + g) * (1 << a.page_shift) + (t & ((1 << a.page_shift) - 1));
+}
+
+__device__ __forceinline__ void half8_to_float(uint4 v, float (&f)[8])
+{
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] & 0xFFFFu));
+        f[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] >> 16));
+    }
+}
+
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    return v;
+}
+
+// GQ query heads per KV head (1..8).
+template <int GQ>
+__global__ void __launch_bounds__(kAttnThreads) attn_partial_kernel(AttnArgs a)
+{
+    __shared__ float s_sc[GQ][kChunk];
+    __shared__ float s_o[4][GQ][kDim];
+    __shared__ float s_m[GQ];
+    __shared__ float s_l[GQ];
+
+    const int chunk = blockIdx.x;
+    const int g = blockIdx.y;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int ctx = clamp_ctx(a);
+    const int t0 = chunk * kChunk;
+    float* po = a.part_o + ((int64_t)chunk * a.n_heads + (int64_t)g * GQ) * kDim;
+    float* pml = a.part_ml + ((int64_t)chunk * a.n_heads + (int64_t)g * GQ) * 2;
+    if (t0 >= ctx) {  // whole workgroup: a chunk past the context is empty
+        for (int i = tid; i < GQ * kDim; i += kAttnThreads) po[i] = 0.0f;
+        if (tid < GQ) {
+            pml[2 * tid] = -__builtin_inff();
+            pml[2 * tid + 1] = 0.0f;
+        }
+        return;
+    }
+
+    // ---- scores: 16 lanes per token, 8 dimensions per lane, 4 tokens per wave step
+    const int dpart = lane & 15;
+    const int tq = lane >> 4;
+    float qr[GQ][8];
+#pragma unroll
+    for (int h = 0; h < GQ; ++h) half8_to_float(a.q[(int64_t)(g * GQ + h) * (kDim / 8) + dpart], qr[h]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int tl = wave * 16 + i * 4 + tq;
+        const int t = t0 + tl;
+        const bool valid = t < ctx;
+        const int64_t row = cache_row(a, valid ? t : ctx - 1, g);  // masked tokens read a real row
+        float kf[8];
+        half8_to_float(a.kc[row * (kDim / 8) + dpart], kf);
+#pragma unroll
+        for (int h = 0; h < GQ; ++h) {
+            float d = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) d = __builtin_fmaf(qr[h][j], kf[j], d);
+#pragma unroll
+            for (int off = 8; off >= 1; off >>= 1) d += __shfl_xor(d, off);
+            if (dpart == 0) s_sc[h][tl] = valid ? d * a.scale : -__builtin_inff();
+        }
+    }
+    __syncthreads();
+
+    // ---- chunk softmax: one wave per head, one lane per token
+    for (int h = wave; h < GQ; h += 4) {
+        const float v = s_sc[h][lane];
+        const float m = wave_max(v);
+        const float e = v == -__builtin_inff() ? 0.0f : __expf(v - m);
+        const float l = wave_sum(e);
+        s_sc[h][lane] = e;
+        if (lane == 0) {
+            s_m[h] = m;
+            s_l[h] = l;
+        }
+    }
+    __syncthreads();
+
+    // ---- unnormalised output: wave w takes tokens [16w, 16w+16), lane = 2 dimensions
+    float acc[GQ][2];
+#pragma unroll
+    for (int h = 0; h < GQ; ++h) acc[h][0] = acc[h][1] = 0.0f;
+    uint32_t vv[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int t = t0 + wave * 16 + j;
+        const int64_t row = cache_row(a, t < ctx ? t : ctx - 1, g);
+        vv[j] = a.vc[row * (kDim / 2) + lane];
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int tl = wave * 16 + j;
+        // a token past the context (weight 0) contributes exactly 0, even if
+        // the row it was read from holds an infinity
+        const uint32_t keep = 0u - (uint32_t)(t0 + tl < ctx);
+        const float v0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(vv[j] & keep & 0xFFFFu));
+        const float v1 = (float)__builtin_bit_cast(_Float16, (uint16_t)((vv[j] & keep) >> 16));
+#pragma unroll
+        for (int h = 0; h < GQ; ++h) {
+            const float w = s_sc[h][tl];  // 0 for tokens past the context
+            acc[h][0] = __builtin_fmaf(w, v0, acc[h][0]);
+            acc[h][1] = __builtin_fmaf(w, v1, acc[h][1]);
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < GQ; ++h) {
+        s_o[wave][h][2 * lane] = acc[h][0];
+        s_o[wave][h][2 * lane + 1] = acc[h][1];
+    }
+    __syncthreads();
+    for (int i = tid; i < GQ * kDim; i += kAttnThreads) {
+        const int h = i / kDim, d = i % kDim;
+        po[i] = ((s_o[0][h][d] + s_o[1][h][d]) + s_o[2][h][d]) + s_o[3][h][d];
+    }
+    if (tid < GQ) {
+        pml[2 * tid] = s_m[tid];
+        pml[2 * tid + 1] = s_l[tid];
+    }
+}
+
+// one workgroup per query head, one thread per dimension
+__global__ void __launch_bounds__(kDim) attn_combine_kernel(AttnArgs a)
+{
+    const int h = blockIdx.x;
+    const int d = threadIdx.x;
+    const int ctx = clamp_ctx(a);
+    const int nch = (ctx + kChunk - 1) / kChunk;
+    float mx = -__builtin_inff();
+    for (int c = 0; c < nch; ++c) mx = fmaxf(mx, a.part_ml[((int64_t)c * a.n_heads + h) * 2]);
+    float l = 0.0f, o = 0.0f;
+    for (int c = 0; c < nch; ++c) {
+        const float* ml = a.part_ml + ((int64_t)c * a.n_heads + h) * 2;
+        const float f = __expf(ml[0] - mx);
+        l = __builtin_fmaf(f, ml[1], l);
+        o = __builtin_fmaf(f, a.part_o[((int64_t)c * a.n_heads + h) * kDim + d], o);
+    }
+    a.out[(int64_t)h * kDim + d] = __builtin_bit_cast(uint16_t, (_Float16)(o / l));
+}
+
+}  // namespace
+
+int64_t attn_chunks(int32_t max_ctx)
+{
+    return (max_ctx + kChunk - 1) / kChunk;
+}
+
+size_t attn_workspace_bytes(int32_t n_heads, int32_t max_ctx)
+{
+    return (size_t)attn_chunks(max_ctx) * (size_t)n_heads * (kDim + 2) * sizeof(float);
+}
+
+hipError_t launch_attn(const AttnCall& c, hipStream_t stream)
+{
+    AttnArgs a{};
+    a.q = static_cast<const uint4*>(c.q);
+    a.kc = static_cast<const uint4*>(c.k_cache);
+    a.vc = static_cast<const uint32_t*>(c.v_cache);
+    a.table = c.page_table;
+    a.ctx_ptr = c.ctx_len;
+    const int64_t chunks = attn_chunks(c.max_ctx);
+    a.part_o = static_cast<float*>(c.ws);
+    a.part_ml = a.part_o + chunks * c.n_heads * kDim;
+    a.out = c.out;
+    a.scale = c.scale;
+    a.max_ctx = c.max_ctx;
+    a.n_heads = c.n_heads;
+    a.n_kv = c.n_kv;
+    int shift = 0;
+    while ((1 << shift) < c.page_size) ++shift;
+    a.page_shift = shift;
+    a.num_pages = c.num_pages;
+    const int group = c.n_heads / c.n_kv;
+    const void* fn = nullptr;
+    switch (group) {
+        case 1: fn = reinterpret_cast<const void*>(&attn_partial_kernel<1>); break;
+        case 2: fn = reinterpret_cast<const void*>(&attn_partial_kernel<2>); break;
+        case 3: fn = reinterpret_cast<const void*>(&attn_partial_kernel<3>); break;
+        case 4: fn = reinterpret_cast<const void*>(&attn_partial_kernel<4>); break;
+        case 5: fn = reinterpret_cast<const void*>(&attn_partial_kernel<5>); break;
+        case 6: fn = reinterpret_cast<const void*>(&attn_partial_kernel<6>); break;
+        case 7: fn = reinterpret_cast<const void*>(&attn_partial_kernel<7>); break;
+        case 8: fn = reinterpret_cast<const void*>(&attn_partial_kernel<8>); break;
+        default: return hipErrorInvalidValue;
+    }
+    void* args[] = {&a};
+    hipError_t err = hipLaunchKernel(fn, dim3((unsigned)chunks, (unsigned)c.n_kv), dim3(kAttnThreads), args, 0, stream);
+    if (err != hipSuccess) return err;
+    return hipLaunchKernel(reinterpret_cast<const void*>(&attn_combine_kernel), dim3((unsigned)c.n_heads), dim3(kDim),
+                           args, 0, stream);
+}
+
+}  // namespace w4i

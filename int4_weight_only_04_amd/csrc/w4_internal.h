@@ -89,6 +89,30 @@ inline size_t gemm_workspace_bytes(int32_t epi, int64_t m, int64_t n, int64_t k)
     return s > 1 ? (size_t)s * (size_t)m * (size_t)n * 4 : 0;
 }
 
+// Decode attention over a paged KV cache (head dimension 128).
+struct AttnCall {
+    const void* q;            // fp16 [n_heads][128]
+    const void* k_cache;      // fp16 [num_pages][n_kv][page_size][128]
+    const void* v_cache;
+    const int32_t* page_table;
+    const int32_t* ctx_len;   // device int32, clamped to [1, max_ctx]
+    uint16_t* out;            // fp16 [n_heads][128]
+    void* ws;
+    float scale;
+    int32_t max_ctx;
+    int32_t n_heads;
+    int32_t n_kv;
+    int32_t page_size;
+    int32_t num_pages;
+};
+
+constexpr int32_t kAttnHeadDim = 128;
+constexpr int32_t kAttnMaxCtx = 1 << 20;
+
+int64_t attn_chunks(int32_t max_ctx);
+size_t attn_workspace_bytes(int32_t n_heads, int32_t max_ctx);
+hipError_t launch_attn(const AttnCall& call, hipStream_t stream);
+
 // Launch one GEMV on `stream` (shape already validated by the caller); the
 // argmax epilogue adds a one-workgroup finalize kernel on the same stream.
 hipError_t launch_gemv(const GemvCall& call, hipStream_t stream);

@@ -23,6 +23,7 @@ PROJ_PLAIN, PROJ_GATEUP_SILU, PROJ_LMHEAD_ARGMAX = 0, 1, 2
 EXPORTED = (
     "w4_status_string", "w4_last_error", "w4_abi_version", "w4_packed_size", "w4_pack",
     "w4_gemv_workspace_size", "w4_gemv", "w4_gemv_gateup_silu", "w4_gemm_workspace_size", "w4_gemm", "w4_gemm_gateup_silu",
+    "w4_attn_decode_workspace_size", "w4_attn_decode",
     "w4_decode_linear_sweep_create", "w4_decode_linear_sweep", "w4_decode_linear_sweep_destroy",
 )
 
@@ -82,6 +83,10 @@ def lib():
     L.w4_gemm_workspace_size.argtypes = [i64, i64, i64, i32, ctypes.POINTER(sz)]
     L.w4_gemm.restype = i32
     L.w4_gemm.argtypes = [vp, vp, vp, vp, vp, sz, i64, i64, i64, i32, vp]
+    L.w4_attn_decode_workspace_size.restype = i32
+    L.w4_attn_decode_workspace_size.argtypes = [i32, i32, ctypes.POINTER(sz)]
+    L.w4_attn_decode.restype = i32
+    L.w4_attn_decode.argtypes = [vp, vp, vp, vp, i32, vp, i32, vp, i32, i32, i32, i32, ctypes.c_float, vp, sz, vp]
     L.w4_gemm_gateup_silu.restype = i32
     L.w4_gemm_gateup_silu.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, vp]
     L.w4_decode_linear_sweep_create.restype = i32
@@ -229,6 +234,32 @@ def gemm_gateup_silu(packed_w, packed_s, x, h, m: int, n_total: int, k: int, gro
                                      _dev_ptr(x, "x", torch.float16, m * k),
                                      _dev_ptr(h, "h", torch.float16, m * (n_total // 2)),
                                      m, n_total, k, group, _stream(stream)), "w4_gemm_gateup_silu")
+
+
+def attn_decode_workspace_size(n_heads: int, max_ctx: int) -> int:
+    out = ctypes.c_size_t()
+    _check(lib().w4_attn_decode_workspace_size(n_heads, max_ctx, ctypes.byref(out)),
+           "w4_attn_decode_workspace_size")
+    return int(out.value)
+
+
+def attn_decode(q, k_cache, v_cache, page_table, ctx_len, max_ctx: int, out, n_kv_heads: int,
+                page_size: int, scale: float, workspace, stream=None):
+    """o[n_heads, 128] (fp16) = softmax(scale q K^T) V over the paged cache;
+    ctx_len is a device int32 tensor of one element."""
+    import torch
+    n_heads = q.shape[0]
+    num_pages = k_cache.shape[0]
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().w4_attn_decode(_dev_ptr(q, "q", torch.float16, n_heads * 128),
+                                _dev_ptr(k_cache, "k_cache", torch.float16),
+                                _dev_ptr(v_cache, "v_cache", torch.float16, k_cache.numel()),
+                                _dev_ptr(page_table, "page_table", torch.int32, -(-max_ctx // page_size)),
+                                num_pages, _dev_ptr(ctx_len, "ctx_len", torch.int32, 1), max_ctx,
+                                _dev_ptr(out, "out", torch.float16, n_heads * 128),
+                                n_heads, n_kv_heads, 128, page_size, float(scale),
+                                _dev_ptr(workspace, "workspace"), ws_bytes, _stream(stream)),
+           "w4_attn_decode")
 
 
 @dataclass

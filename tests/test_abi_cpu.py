@@ -183,6 +183,34 @@ def test_gemm_workspace_sizes():
     assert w4.gemm_workspace_size(1, 64, 64, 64) == 0  # one k step: nothing to split
 
 
+def test_attn_validation_before_launch():
+    """Decode-attention argument checks run before any device call."""
+    L = w4.lib()
+    A = 1 << 20
+    W = 1 << 30
+
+    def call(q=A, kc=A, vc=A, tab=A, npages=4, ctx=A, max_ctx=64, out=A, nh=28, nkv=4, dim=128, page=16,
+             ws=A, wsb=W):
+        return L.w4_attn_decode(q, kc, vc, tab, npages, ctx, max_ctx, out, nh, nkv, dim, page, 0.088, ws, wsb,
+                                None)
+
+    assert call(q=None) == w4.EINVAL
+    assert call(ctx=None) == w4.EINVAL
+    assert call(ws=None) == w4.EINVAL
+    assert call(dim=64) == w4.ESHAPE
+    assert call(nh=30) == w4.ESHAPE            # not a multiple of n_kv
+    assert call(nh=40) == w4.ESHAPE            # 10 query heads per KV head
+    assert call(page=24) == w4.ESHAPE          # not a power of two
+    assert call(max_ctx=0) == w4.ESHAPE
+    assert call(npages=0) == w4.ESHAPE
+    assert call(q=A + 2) == w4.EALIGN
+    assert call(ctx=A + 2) == w4.EALIGN
+    need = w4.attn_decode_workspace_size(28, 64)
+    assert need == 28 * 130 * 4
+    assert call(wsb=need - 1) == w4.EINVAL
+    assert w4.attn_decode_workspace_size(28, 4096) == 64 * 28 * 130 * 4
+
+
 def test_sweep_create_validation():
     L = w4.lib()
     A = 1 << 20
