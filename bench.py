@@ -13,6 +13,11 @@ sweep, the eager-launch sweep for comparison, the dominant kernel's roofline
 (gate/up + SiLU, timed per launch with HIP events on the launch stream) and
 the CPU oracle timed on a bounded sample on the host.
 
+    python bench.py --workload attention
+
+times 28 layers' decode attention over a paged fp16 KV cache at a
+4096-token context (GB/s against the HBM peak).
+
     python bench.py --workload prefill [--steps 10] [--warmup 2]
 
 times the prefill counterpart instead: the 28 layers' four INT4 products for
@@ -41,6 +46,8 @@ HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 matrix-core peak
 METRIC = "achieved HBM GB/s (% of peak) and ms per 28-layer+lm_head INT4 linear sweep"
 PREFILL_METRIC = "prefill TFLOP/s (% of fp16 MFMA peak) and ms per 28-layer 512-token INT4 linear sweep"
+ATTN_METRIC = "decode attention GB/s (% of HBM peak) and ms per 28-layer paged-KV attention at 4096-token context"
+ATTN_HEADS, ATTN_KV_HEADS, ATTN_PAGE, ATTN_CTX = 28, 4, 16, 4096
 KERNEL_SRC = os.path.join(ROOT, "int4_weight_only_04_amd", "csrc", "w4_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gateup_silu_37888x3584.json")
 GEMM_SRC = os.path.join(ROOT, "int4_weight_only_04_amd", "csrc", "w4_gemm.hip")
@@ -364,6 +371,112 @@ def run_prefill(args) -> int:
     return 0
 
 
+def attn_bytes(ctx: int) -> int:
+    """K and V rows of the context, q, the output and the page table."""
+    return 2 * ctx * ATTN_KV_HEADS * 128 * 2 + 2 * ATTN_HEADS * 128 * 2 + 4 * (-(-ctx // ATTN_PAGE))
+
+
+def attn_cpu_baseline(layers: int = 12):
+    """The oracle's attention (single thread, fp64) on `layers` layers' caches
+    at the full context."""
+    import oracle
+    rng = np.random.default_rng(4000)
+    npages = ATTN_CTX // ATTN_PAGE
+    total = 0.0
+    for _ in range(layers):
+        q = rng.standard_normal((ATTN_HEADS, 128)).astype(np.float16).view(np.uint16)
+        kc = rng.standard_normal((npages, ATTN_KV_HEADS, ATTN_PAGE, 128)).astype(np.float16).view(np.uint16)
+        vc = rng.standard_normal((npages, ATTN_KV_HEADS, ATTN_PAGE, 128)).astype(np.float16).view(np.uint16)
+        table = rng.permutation(npages).astype(np.int32)
+        t0 = time.perf_counter()
+        oracle.attn_decode(q, kc, vc, table, ATTN_CTX, ATTN_KV_HEADS, ATTN_PAGE, 1.0 / np.sqrt(128.0))
+        total += time.perf_counter() - t0
+    nbytes = layers * attn_bytes(ATTN_CTX)
+    return {
+        "value": nbytes / total / 1e9,
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{layers} layers' attention at context {ATTN_CTX} (28 query heads, 4 KV heads, pages of "
+                  f"{ATTN_PAGE}): {nbytes} algorithmic bytes in {total:.1f} s, single-threaded fp64 C",
+        "seconds": total,
+    }
+
+
+def run_attention(args) -> int:
+    """28 layers' decode attention at a 4096-token context: two sets of 28
+    caches (470 MB, beyond the 256 MB Infinity Cache) alternate, each layer
+    with its own seeded cache and a permuted page table, in one HIP graph."""
+    import torch
+    from int4_weight_only_04_amd import w4
+    layers = args.layers
+    npages = ATTN_CTX // ATTN_PAGE
+    dev = "cuda"
+    g = torch.Generator(device="cpu").manual_seed(4001)
+    calls = []
+    for i in range(2 * layers):
+        kc = torch.randn((npages, ATTN_KV_HEADS, ATTN_PAGE, 128), generator=g).to(torch.float16).to(dev)
+        vc = torch.randn((npages, ATTN_KV_HEADS, ATTN_PAGE, 128), generator=g).to(torch.float16).to(dev)
+        q = torch.randn((ATTN_HEADS, 128), generator=g).to(torch.float16).to(dev)
+        table = torch.randperm(npages, generator=g).to(torch.int32).to(dev)
+        out = torch.empty((ATTN_HEADS, 128), dtype=torch.float16, device=dev)
+        calls.append((q, kc, vc, table, out))
+    ctx = torch.full((1,), ATTN_CTX, dtype=torch.int32, device=dev)
+    ws = torch.empty(w4.attn_decode_workspace_size(ATTN_HEADS, ATTN_CTX), dtype=torch.uint8, device=dev)
+    scale = 1.0 / float(np.sqrt(128.0))
+
+    def launch(s, subset=None):
+        for (q, kc, vc, table, out) in (calls if subset is None else subset):
+            w4.attn_decode(q, kc, vc, table, ctx, ATTN_CTX, out, ATTN_KV_HEADS, ATTN_PAGE, scale, ws, stream=s)
+
+    stream = torch.cuda.Stream()
+    print(f"[bench] attention graph ({2 * layers} calls over two cache sets)", file=sys.stderr, flush=True)
+    graph = capture(lambda s: launch(s), stream)
+    per_call_ms = replay_ms(graph, stream, args.steps, args.warmup) / (2 * layers)
+    ms = per_call_ms * layers
+    nbytes = attn_bytes(ATTN_CTX)
+    gbs = nbytes / (per_call_ms * 1e-3) / 1e9
+    out = {
+        "metric": ATTN_METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"batch-1 decode attention, hipGraph: {layers} layers x softmax(q K^T / sqrt(128)) V over "
+                         f"a paged fp16 KV cache, context {ATTN_CTX}, pages of {ATTN_PAGE} tokens, {ATTN_HEADS} query "
+                         f"heads over {ATTN_KV_HEADS} KV heads of 128, fp32 arithmetic, fp16 output"),
+            "algorithmic_bytes_per_layer": nbytes,
+            "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        },
+        "roofline": {
+            "kernel": "attn_partial_kernel<7> + attn_combine_kernel, 4096 tokens",
+            "bound": "hbm",
+            "achieved": round(gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": nbytes,
+            "avg_launch_us": round(per_call_ms * 1e3, 3),
+            "launches_timed": args.steps * 2 * layers,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle attention)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = attn_cpu_baseline()
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -372,8 +485,9 @@ def main(argv=None):
     ap.add_argument("--layers", type=int, default=synthetic.LAYERS)
     ap.add_argument("--eager-steps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", choices=("decode", "prefill"), default="decode",
-                    help="decode: the per-token GEMV sweep (default); prefill: the 512-token GEMM sweep")
+    ap.add_argument("--workload", choices=("decode", "prefill", "attention"), default="decode",
+                    help="decode: the per-token GEMV sweep (default); prefill: the 512-token GEMM sweep; "
+                         "attention: 28 layers' paged-KV decode attention at a 4096-token context")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args(argv)
@@ -402,6 +516,8 @@ def main(argv=None):
 
     if args.workload == "prefill":
         return run_prefill(args)
+    if args.workload == "attention":
+        return run_attention(args)
 
     print(f"[bench] building sweep ({args.layers} layers)", file=sys.stderr, flush=True)
     specs, projs = build_sweep(args.layers)

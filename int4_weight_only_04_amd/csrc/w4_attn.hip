@@ -74,6 +74,17 @@ __device__ __forceinline__ void half8_to_float(uint4 v, float (&f)[8])
     }
 }
 
+// Sum over each row of 16 lanes with DPP row shifts (no LDS traffic): lane 15
+// of the row ends with the total.
+__device__ __forceinline__ float row16_sum(float v)
+{
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x111, 0xF, 0xF, true));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x112, 0xF, 0xF, true));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x114, 0xF, 0xF, true));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x118, 0xF, 0xF, true));
+    return v;
+}
+
 __device__ __forceinline__ float wave_max(float v)
 {
 #pragma unroll
@@ -102,10 +113,34 @@ __global__ void __launch_bounds__(kAttnThreads) attn_partial_kernel(AttnArgs a)
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int ctx = clamp_ctx(a);
     const int t0 = chunk * kChunk;
     float* po = a.part_o + ((int64_t)chunk * a.n_heads + (int64_t)g * GQ) * kDim;
     float* pml = a.part_ml + ((int64_t)chunk * a.n_heads + (int64_t)g * GQ) * 2;
+
+    // ---- every load of the workgroup goes out first, none waiting for the
+    // context length: q, this lane's 4 K row slices and its 16 V words (rows
+    // of tokens past max_ctx are read from the last one; past the context
+    // they are masked below)
+    const int ctx = clamp_ctx(a);
+    const int dpart = lane & 15;
+    const int tq = lane >> 4;
+    uint4 qv[GQ];
+#pragma unroll
+    for (int h = 0; h < GQ; ++h) qv[h] = a.q[(int64_t)(g * GQ + h) * (kDim / 8) + dpart];
+    uint4 kv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int t = t0 + wave * 16 + i * 4 + tq;
+        const int64_t row = cache_row(a, t < a.max_ctx ? t : a.max_ctx - 1, g);
+        kv[i] = a.kc[row * (kDim / 8) + dpart];
+    }
+    uint32_t vv[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int t = t0 + wave * 16 + j;
+        const int64_t row = cache_row(a, t < a.max_ctx ? t : a.max_ctx - 1, g);
+        vv[j] = a.vc[row * (kDim / 2) + lane];
+    }
     if (t0 >= ctx) {  // whole workgroup: a chunk past the context is empty
         for (int i = tid; i < GQ * kDim; i += kAttnThreads) po[i] = 0.0f;
         if (tid < GQ) {
@@ -116,27 +151,22 @@ __global__ void __launch_bounds__(kAttnThreads) attn_partial_kernel(AttnArgs a)
     }
 
     // ---- scores: 16 lanes per token, 8 dimensions per lane, 4 tokens per wave step
-    const int dpart = lane & 15;
-    const int tq = lane >> 4;
     float qr[GQ][8];
 #pragma unroll
-    for (int h = 0; h < GQ; ++h) half8_to_float(a.q[(int64_t)(g * GQ + h) * (kDim / 8) + dpart], qr[h]);
+    for (int h = 0; h < GQ; ++h) half8_to_float(qv[h], qr[h]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int tl = wave * 16 + i * 4 + tq;
-        const int t = t0 + tl;
-        const bool valid = t < ctx;
-        const int64_t row = cache_row(a, valid ? t : ctx - 1, g);  // masked tokens read a real row
+        const bool valid = t0 + tl < ctx;
         float kf[8];
-        half8_to_float(a.kc[row * (kDim / 8) + dpart], kf);
+        half8_to_float(kv[i], kf);
 #pragma unroll
         for (int h = 0; h < GQ; ++h) {
             float d = 0.0f;
 #pragma unroll
             for (int j = 0; j < 8; ++j) d = __builtin_fmaf(qr[h][j], kf[j], d);
-#pragma unroll
-            for (int off = 8; off >= 1; off >>= 1) d += __shfl_xor(d, off);
-            if (dpart == 0) s_sc[h][tl] = valid ? d * a.scale : -__builtin_inff();
+            d = row16_sum(d);  // total in lane 15 of each 16-lane row
+            if (dpart == 15) s_sc[h][tl] = valid ? d * a.scale : -__builtin_inff();
         }
     }
     __syncthreads();
@@ -159,13 +189,6 @@ __global__ void __launch_bounds__(kAttnThreads) attn_partial_kernel(AttnArgs a)
     float acc[GQ][2];
 #pragma unroll
     for (int h = 0; h < GQ; ++h) acc[h][0] = acc[h][1] = 0.0f;
-    uint32_t vv[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        const int t = t0 + wave * 16 + j;
-        const int64_t row = cache_row(a, t < ctx ? t : ctx - 1, g);
-        vv[j] = a.vc[row * (kDim / 2) + lane];
-    }
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
         const int tl = wave * 16 + j;
@@ -197,23 +220,87 @@ __global__ void __launch_bounds__(kAttnThreads) attn_partial_kernel(AttnArgs a)
     }
 }
 
-// one workgroup per query head, one thread per dimension
-__global__ void __launch_bounds__(kDim) attn_combine_kernel(AttnArgs a)
+// One workgroup per query head: the chunk maxima and sums are reduced across
+// the workgroup, then thread (d, j) sums dimension d over the chunks j, j+8,
+// ... with independent loads, and the eight partial sums meet in LDS in a
+// fixed order.
+constexpr int kCombThreads = 1024;
+
+__device__ __forceinline__ float block_reduce(float v, float* red, bool is_max)
 {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const float o = __shfl_xor(v, off);
+        v = is_max ? fmaxf(v, o) : v + o;
+    }
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    float r = red[0];
+#pragma unroll
+    for (int w = 1; w < kCombThreads / 64; ++w) r = is_max ? fmaxf(r, red[w]) : r + red[w];
+    __syncthreads();
+    return r;
+}
+
+__global__ void __launch_bounds__(kCombThreads) attn_combine_kernel(AttnArgs a)
+{
+    constexpr int J = kCombThreads / kDim;  // 8 chunk lanes per dimension
+    constexpr int kMaxPer = 8;              // chunks per thread held in registers
+    __shared__ float red[kCombThreads / 64];
+    __shared__ float part[J][kDim];
     const int h = blockIdx.x;
-    const int d = threadIdx.x;
+    const int tid = threadIdx.x;
+    const int d = tid & (kDim - 1);
+    const int j = tid / kDim;
+    const int chunks = (a.max_ctx + kChunk - 1) / kChunk;
     const int ctx = clamp_ctx(a);
     const int nch = (ctx + kChunk - 1) / kChunk;
+    // the first J * kMaxPer chunks: loads issued together, before the maxima
+    float mv[kMaxPer], lv[kMaxPer], ov[kMaxPer];
+#pragma unroll
+    for (int i = 0; i < kMaxPer; ++i) {
+        int c = j + J * i;
+        if (c >= chunks) c = chunks - 1;  // in bounds; masked below
+        const float* ml = a.part_ml + ((int64_t)c * a.n_heads + h) * 2;
+        mv[i] = ml[0];
+        lv[i] = ml[1];
+        ov[i] = a.part_o[((int64_t)c * a.n_heads + h) * kDim + d];
+    }
     float mx = -__builtin_inff();
-    for (int c = 0; c < nch; ++c) mx = fmaxf(mx, a.part_ml[((int64_t)c * a.n_heads + h) * 2]);
+#pragma unroll
+    for (int i = 0; i < kMaxPer; ++i)
+        if (j + J * i < nch) mx = fmaxf(mx, mv[i]);
+    for (int c = j + J * kMaxPer; c < nch; c += J) mx = fmaxf(mx, a.part_ml[((int64_t)c * a.n_heads + h) * 2]);
+    mx = block_reduce(mx, red, true);
     float l = 0.0f, o = 0.0f;
-    for (int c = 0; c < nch; ++c) {
+#pragma unroll
+    for (int i = 0; i < kMaxPer; ++i) {
+        if (j + J * i < nch) {
+            const float f = __expf(mv[i] - mx);
+            l = __builtin_fmaf(f, lv[i], l);
+            o = __builtin_fmaf(f, ov[i], o);
+        }
+    }
+    for (int c = j + J * kMaxPer; c < nch; c += J) {
         const float* ml = a.part_ml + ((int64_t)c * a.n_heads + h) * 2;
         const float f = __expf(ml[0] - mx);
         l = __builtin_fmaf(f, ml[1], l);
         o = __builtin_fmaf(f, a.part_o[((int64_t)c * a.n_heads + h) * kDim + d], o);
     }
-    a.out[(int64_t)h * kDim + d] = __builtin_bit_cast(uint16_t, (_Float16)(o / l));
+    // every dimension's thread group holds the same l partials: sum them over j only
+    part[j][d] = o;
+    if (d == 0) red[j] = l;  // red is free again after block_reduce
+    __syncthreads();
+    if (j == 0) {
+        float t = part[0][d], ls = red[0];
+#pragma unroll
+        for (int q = 1; q < J; ++q) {
+            t += part[q][d];
+            ls += red[q];
+        }
+        a.out[(int64_t)h * kDim + d] = __builtin_bit_cast(uint16_t, (_Float16)(t / ls));
+    }
 }
 
 }  // namespace
@@ -264,8 +351,8 @@ hipError_t launch_attn(const AttnCall& c, hipStream_t stream)
     void* args[] = {&a};
     hipError_t err = hipLaunchKernel(fn, dim3((unsigned)chunks, (unsigned)c.n_kv), dim3(kAttnThreads), args, 0, stream);
     if (err != hipSuccess) return err;
-    return hipLaunchKernel(reinterpret_cast<const void*>(&attn_combine_kernel), dim3((unsigned)c.n_heads), dim3(kDim),
-                           args, 0, stream);
+    return hipLaunchKernel(reinterpret_cast<const void*>(&attn_combine_kernel), dim3((unsigned)c.n_heads),
+                           dim3(kCombThreads), args, 0, stream);
 }
 
 }  // namespace w4i
