@@ -71,6 +71,10 @@ class Oracle:
         lib.oracle_gemm_packed.argtypes = [p, p, p, i64, i64, i32, i32, p, i64, p, i64, p, p]
         lib.oracle_attn_decode.restype = None
         lib.oracle_attn_decode.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, ctypes.c_double, p, p]
+        lib.oracle_rmsnorm.restype = None
+        lib.oracle_rmsnorm.argtypes = [p, i64, p, ctypes.c_double, p]
+        lib.oracle_rope.restype = None
+        lib.oracle_rope.argtypes = [p, i32, i64, ctypes.c_double, p]
         lib.oracle_silu.restype = ctypes.c_double
         lib.oracle_silu.argtypes = [ctypes.c_double]
         lib.oracle_silu_gate.restype = None
@@ -206,6 +210,23 @@ class Oracle:
                                     n_kv, dim, page, float(scale), _ptr(o), _ptr(a))
         return o, a
 
+    def rmsnorm(self, h: np.ndarray, gamma_bits: np.ndarray, eps: float) -> np.ndarray:
+        """h / sqrt(mean(h^2) + eps) * gamma in float64 (h any float array)."""
+        h = np.ascontiguousarray(h, dtype=np.float64)
+        gamma_bits = np.ascontiguousarray(gamma_bits, dtype=np.uint16)
+        assert gamma_bits.shape == h.shape and h.ndim == 1
+        out = np.empty_like(h)
+        self.lib.oracle_rmsnorm(_ptr(h), h.size, _ptr(gamma_bits), float(eps), _ptr(out))
+        return out
+
+    def rope(self, x: np.ndarray, pos: int, theta: float) -> np.ndarray:
+        """Rotary embedding of each row of x [heads, dim] at position pos."""
+        x = np.ascontiguousarray(x, dtype=np.float64)
+        out = np.empty_like(x)
+        for r in range(x.shape[0]):
+            self.lib.oracle_rope(_ptr(x[r]), x.shape[1], int(pos), float(theta), _ptr(out[r]))
+        return out
+
     def silu(self, t: float) -> float:
         return self.lib.oracle_silu(float(t))
 
@@ -274,6 +295,14 @@ def gemv_packed(pw, ps, x_bits, n, k, group, gateup=False, rows=None):
 
 def attn_decode(q_bits, k_cache, v_cache, page_table, ctx, n_kv, page, scale):
     return default().attn_decode(q_bits, k_cache, v_cache, page_table, ctx, n_kv, page, scale)
+
+
+def rmsnorm(h, gamma_bits, eps):
+    return default().rmsnorm(h, gamma_bits, eps)
+
+
+def rope(x, pos, theta):
+    return default().rope(x, pos, theta)
 
 
 def silu(t):

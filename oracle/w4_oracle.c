@@ -336,6 +336,37 @@ void oracle_attn_decode(const uint16_t* q, const uint16_t* kc, const uint16_t* v
     }
 }
 
+/* Glue of a full decode step (the decoding stack of the pages' runtime --
+ * "How To Build Your Own LLM Runtime From Scratch", aitrending.vip, TL;DR
+ * and "Technical Details"; noticiai.com.br: attention, linear projections,
+ * softmax, sampling -- read as the Qwen2-family pre-norm decoder the pages
+ * name: RMSNorm, rotary position embedding, residual adds).  Double
+ * precision throughout. */
+
+/* out[i] = h[i] / sqrt(mean_j h[j]^2 + eps) * gamma[i]   (gamma fp16 bits) */
+void oracle_rmsnorm(const double* h, int64_t n, const uint16_t* gamma, double eps, double* out)
+{
+    double ss = 0.0;
+    for (int64_t i = 0; i < n; ++i) ss += h[i] * h[i];
+    double r = 1.0 / sqrt(ss / (double)n + eps);
+    for (int64_t i = 0; i < n; ++i) out[i] = h[i] * r * oracle_half_to_double(gamma[i]);
+}
+
+/* Rotary embedding of one head of `dim` values at position pos, rotating the
+ * pairs (i, i + dim/2) by pos * theta^(-2i/dim):
+ *   out[i]         = x[i] cos a - x[i + dim/2] sin a
+ *   out[i + dim/2] = x[i + dim/2] cos a + x[i] sin a */
+void oracle_rope(const double* x, int32_t dim, int64_t pos, double theta, double* out)
+{
+    int32_t half = dim / 2;
+    for (int32_t i = 0; i < half; ++i) {
+        double a = (double)pos * pow(theta, -2.0 * (double)i / (double)dim);
+        double c = cos(a), sn = sin(a);
+        out[i] = x[i] * c - x[i + half] * sn;
+        out[i + half] = x[i + half] * c + x[i] * sn;
+    }
+}
+
 /* silu(t) = t * sigmoid(t) = t / (1 + e^-t) */
 double oracle_silu(double t)
 {

@@ -415,4 +415,45 @@ def pin_attn_page_layouts(orc):
         assert np.array_equal(o, outs[0][0]) and np.array_equal(a, outs[0][1])
 
 
+def pin_rmsnorm(orc):
+    """RMSNorm: scale invariance (with eps scaled alike), constant vectors map
+    to gamma, unit gamma gives a root-mean-square of 1 (eps = 0)."""
+    rng = np.random.default_rng(47)
+    n = 3584
+    h = rng.standard_normal(n) * 3.0
+    g = _h(rng.uniform(0.5, 1.5, n))
+    gv = g.view(np.float16).astype(np.float64)
+    out = orc.rmsnorm(h, g, 1e-6)
+    assert np.allclose(orc.rmsnorm(4.0 * h, g, 16e-6), out, rtol=1e-14, atol=0)
+    assert np.allclose(orc.rmsnorm(np.full(n, 2.5), g, 0.0), gv, rtol=1e-14, atol=0)
+    ones = _h(np.ones(n))
+    o1 = orc.rmsnorm(h, ones, 0.0)
+    assert abs(np.sqrt(np.mean(o1 ** 2)) - 1.0) < 1e-14
+    assert np.allclose(o1 * np.sqrt(np.mean(h ** 2)), h, rtol=1e-13, atol=0)
+
+
+def pin_rope(orc):
+    """RoPE against the complex-number form (x_i + j x_{i+d/2}) e^{j a_i},
+    identity at position 0, norm preservation, composition of positions and
+    dependence of q . k on the position difference only."""
+    rng = np.random.default_rng(53)
+    dim, theta = 128, 1e6
+    x = rng.standard_normal((5, dim))
+    for pos in (0, 1, 17, 4095):
+        out = orc.rope(x, pos, theta)
+        a = pos * theta ** (-np.arange(dim // 2) * 2.0 / dim)
+        z = (x[:, : dim // 2] + 1j * x[:, dim // 2:]) * np.exp(1j * a)
+        assert np.allclose(out[:, : dim // 2], z.real, rtol=0, atol=1e-12)
+        assert np.allclose(out[:, dim // 2:], z.imag, rtol=0, atol=1e-12)
+    assert np.array_equal(orc.rope(x, 0, theta), x)
+    out = orc.rope(x, 333, theta)
+    pairs = lambda v: v[:, : dim // 2] ** 2 + v[:, dim // 2:] ** 2
+    assert np.allclose(pairs(out), pairs(x), rtol=1e-12, atol=0)
+    assert np.allclose(orc.rope(orc.rope(x, 100, theta), 23, theta), orc.rope(x, 123, theta), rtol=0, atol=1e-10)
+    q, k = x[0:1], x[1:2]
+    d1 = float((orc.rope(q, 500, theta) @ orc.rope(k, 480, theta).T)[0, 0])
+    d2 = float((orc.rope(q, 1020, theta) @ orc.rope(k, 1000, theta).T)[0, 0])
+    assert abs(d1 - d2) < 1e-9
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

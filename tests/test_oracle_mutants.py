@@ -49,6 +49,10 @@ MUTANTS = [
     ("attn_page_table_ignored", "(int64_t)page_table[t / page] * n_kv", "(int64_t)(t / page) * n_kv", None),
     ("attn_scale_dropped", "            sdot *= scale;\n", "\n", None),
     ("attn_abs_dropped", "a[(int64_t)h * dim + d] += w * fabs(v);", "a[(int64_t)h * dim + d] += w * v;", None),
+    ("rmsnorm_no_mean", "double r = 1.0 / sqrt(ss / (double)n + eps);", "double r = 1.0 / sqrt(ss + eps);", None),
+    ("rmsnorm_gamma_dropped", "out[i] = h[i] * r * oracle_half_to_double(gamma[i]);", "out[i] = h[i] * r;", None),
+    ("rope_sign", "out[i] = x[i] * c - x[i + half] * sn;", "out[i] = x[i] * c + x[i + half] * sn;", None),
+    ("rope_freq", "pow(theta, -2.0 * (double)i / (double)dim)", "pow(theta, -(double)i / (double)dim)", None),
     ("gemm_packed_x_row_fixed", "oracle_gemv_packed_rows(pw, ps, xm + m * k,", "oracle_gemv_packed_rows(pw, ps, xm,", None),
 ]
 
