@@ -127,3 +127,74 @@ def sweep_projections(layers: int = LAYERS) -> list[Proj]:
         out.append(Proj(f"L{l}.down", "plain", HIDDEN, MLP, GROUP, 1000 + 10 * l + 3))
     out.append(Proj("lm_head", "lmhead", VOCAB, HIDDEN, GROUP, 1280))
     return out
+
+
+# Decoder of the full decode step (the pages' model: 28 query heads over 4 KV
+# heads of 128 give the 4608-wide fused QKV projection).
+HEADS = 28
+KV_HEADS = 4
+PAGE = 16
+MAX_CTX = 4096
+
+
+def step_model(seed: int, *, hidden: int, n_heads: int, n_kv: int, inter: int, vocab: int, group: int,
+               layers: int, bias: bool = False, s_lo: float = 0.001, s_hi: float = 0.02) -> dict:
+    """Logical weights of a small decoder for the full-step tests.
+
+    Layer l draws from seed * 1000 + 10 * l + p with p = 0 qkv, 1 o_proj,
+    2 gate/up, 3 down (nibbles then scales, as `logical`), 4 attention norm,
+    5 MLP norm, 6 qkv bias; the embedding table, final norm and lm_head use
+    seed * 1000 + 900, 901, 902.  Norm weights ~ U[0.5, 1.5] and embeddings
+    ~ N(0, 1) (float32 draws rounded to fp16); biases ~ N(0, 0.5) in float32.
+    Returns plain arrays: {"embed", "final_norm", "lm": (q, s), "layers":
+    [{"attn_norm", "qkv", "qkv_bias", "o", "mlp_norm", "gateup", "down"}]}."""
+    def proj(sd, n, k):
+        rng = _rng(sd)
+        q = _nibbles(rng, n * k).reshape(n, k)
+        s = _scales(rng, n * (k // group), s_lo, s_hi).reshape(n, k // group)
+        return q, s
+
+    def norm(sd, n):
+        return _scales(_rng(sd), n, 0.5, 1.5)
+
+    base = seed * 1000
+    qkv_rows = (n_heads + 2 * n_kv) * 128
+    out = {"layers": []}
+    for l in range(layers):
+        b = base + 10 * l
+        layer = {
+            "qkv": proj(b + 0, qkv_rows, hidden),
+            "o": proj(b + 1, hidden, n_heads * 128),
+            "gateup": proj(b + 2, 2 * inter, hidden),
+            "down": proj(b + 3, hidden, inter),
+            "attn_norm": norm(b + 4, hidden),
+            "mlp_norm": norm(b + 5, hidden),
+            "qkv_bias": (_rng(b + 6).standard_normal(qkv_rows, dtype=np.float32) * np.float32(0.5)) if bias else None,
+        }
+        out["layers"].append(layer)
+    out["embed"] = _acts(_rng(base + 900), vocab * hidden).reshape(vocab, hidden)
+    out["final_norm"] = norm(base + 901, hidden)
+    out["lm"] = proj(base + 902, vocab, hidden)
+    return out
+
+
+def kv_prefix(seed: int, num_pages: int, n_kv: int, page: int) -> tuple[np.ndarray, np.ndarray]:
+    """Cache contents standing in for earlier tokens of the sequence: fp16 bits
+    [num_pages, n_kv, page, 128] for K then V, N(0, 1) rounded to fp16."""
+    rng = _rng(seed)
+    shape = (num_pages, n_kv, page, 128)
+    count = int(np.prod(shape))
+    return _acts(rng, count).reshape(shape), _acts(rng, count).reshape(shape)
+
+
+def page_table(seed: int, num_pages: int, entries: int) -> np.ndarray:
+    """A random assignment of distinct physical pages to the logical pages."""
+    return _rng(seed).permutation(num_pages).astype(np.int32)[:entries]
+
+
+def half_bits_uniform(seed: int, count: int, lo_exp: int = 14) -> np.ndarray:
+    """Cheap fp16 bit patterns for very large tables: random sign and
+    mantissa with a fixed exponent (magnitudes in [2^(lo_exp-15), 2^(lo_exp-14)),
+    i.e. [0.5, 1) by default)."""
+    raw = _rng(seed).bit_generator.random_raw((count + 3) // 4).view(np.uint16)[:count]
+    return (raw & np.uint16(0x83FF)) | np.uint16(lo_exp << 10)
