@@ -73,62 +73,86 @@ class Config:
 
 @dataclass
 class LayerResult:
-    x1: np.ndarray = field(default=None)       # fp16 bits
-    qkv: np.ndarray = field(default=None)      # fp64 (bias added)
-    a_qkv: np.ndarray = field(default=None)    # sum |w x| of the qkv rows
-    q: np.ndarray = field(default=None)        # fp64 rotated [nh, 128]
-    k: np.ndarray = field(default=None)        # fp64 rotated [nkv, 128]
-    v: np.ndarray = field(default=None)        # fp64 [nkv, 128]
-    attn: np.ndarray = field(default=None)     # fp64 [nh, 128]
+    """Stage values of one layer.  fp16 stages hold the unrounded fp64 value
+    (the stored operand is its fp16 rounding); a_* are the sums of |terms|."""
+    x1: np.ndarray = field(default=None)       # fp64 [hidden], stored fp16
+    qkv: np.ndarray = field(default=None)      # fp64, the projection (bias not added)
+    a_qkv: np.ndarray = field(default=None)
+    q: np.ndarray = field(default=None)        # fp64 [nh, 128] rotated, stored fp16
+    k: np.ndarray = field(default=None)        # fp64 [nkv, 128] rotated, stored fp16 in the cache
+    v: np.ndarray = field(default=None)        # fp64 [nkv, 128], stored fp16 in the cache
+    attn: np.ndarray = field(default=None)     # fp64 [nh, 128], stored fp16
     a_attn: np.ndarray = field(default=None)
     o: np.ndarray = field(default=None)
     a_o: np.ndarray = field(default=None)
     h_mid: np.ndarray = field(default=None)
-    x2: np.ndarray = field(default=None)       # fp16 bits
+    x2: np.ndarray = field(default=None)       # fp64 [hidden], stored fp16
     gu: np.ndarray = field(default=None)       # fp64 [2I]
     a_gu: np.ndarray = field(default=None)
-    m: np.ndarray = field(default=None)        # fp64 [I]
+    m: np.ndarray = field(default=None)        # fp64 [I], stored fp16
     d: np.ndarray = field(default=None)
     a_d: np.ndarray = field(default=None)
     h_out: np.ndarray = field(default=None)
 
 
+def _take(forced, name, own):
+    """The value the next stage consumes: the forced one when given."""
+    if forced is not None and name in forced:
+        return forced[name]
+    return own
+
+
 def decoder_layer(h: np.ndarray, layer: Layer, cfg: Config, pos: int, k_cache: np.ndarray,
-                  v_cache: np.ndarray, page_table: np.ndarray, orc=None) -> LayerResult:
+                  v_cache: np.ndarray, page_table: np.ndarray, orc=None, forced: dict | None = None) -> LayerResult:
     """One layer for the token at position pos.  h is the fp64 residual
     stream; k_cache / v_cache (fp16 bits [pages, nkv, page, 128]) hold the
-    earlier tokens and receive this token's k and v (modified in place)."""
+    earlier tokens and receive this token's k and v (modified in place).
+
+    forced (teacher forcing) maps stage names to values that replace this
+    function's own stored results as the input of the following stages, so a
+    stage can be checked from another implementation's input: "x1", "q", "k",
+    "v", "attn", "x2", "m" as fp16 bits; "qkv", "o", "h_mid", "d" as float64.
+    Each stage's own result (computed from the forced inputs) is returned."""
     orc = orc or default()
     r = LayerResult()
     nh, nkv, G = cfg.n_heads, cfg.n_kv, cfg.group
-    r.x1 = to_half_bits(orc.rmsnorm(h, layer.attn_norm, cfg.eps))
-    r.qkv, r.a_qkv = orc.gemv(layer.qkv.q, layer.qkv.s, r.x1, G)
+    r.x1 = orc.rmsnorm(h, layer.attn_norm, cfg.eps)
+    x1 = _take(forced, "x1", to_half_bits(r.x1))
+    r.qkv, r.a_qkv = orc.gemv(layer.qkv.q, layer.qkv.s, x1, G)
+    qkv = _take(forced, "qkv", r.qkv)
     if layer.qkv_bias is not None:
-        r.qkv = r.qkv + layer.qkv_bias
-    parts = r.qkv.reshape(nh + 2 * nkv, HEAD_DIM)
+        qkv = qkv + layer.qkv_bias
+    parts = qkv.reshape(nh + 2 * nkv, HEAD_DIM)
     r.q = orc.rope(parts[:nh], pos, cfg.theta)
     r.k = orc.rope(parts[nh:nh + nkv], pos, cfg.theta)
     r.v = parts[nh + nkv:].copy()
     pg, slot = page_table[pos // cfg.page], pos % cfg.page
-    k_cache[pg, :, slot, :] = to_half_bits(r.k)
-    v_cache[pg, :, slot, :] = to_half_bits(r.v)
-    r.attn, r.a_attn = orc.attn_decode(to_half_bits(r.q), k_cache, v_cache, page_table, pos + 1, nkv, cfg.page,
+    k_cache[pg, :, slot, :] = _take(forced, "k", to_half_bits(r.k))
+    v_cache[pg, :, slot, :] = _take(forced, "v", to_half_bits(r.v))
+    q = _take(forced, "q", to_half_bits(r.q))
+    r.attn, r.a_attn = orc.attn_decode(q, k_cache, v_cache, page_table, pos + 1, nkv, cfg.page,
                                        1.0 / np.sqrt(float(HEAD_DIM)))
-    r.o, r.a_o = orc.gemv(layer.o.q, layer.o.s, to_half_bits(r.attn).reshape(-1), G)
-    r.h_mid = h + r.o
-    r.x2 = to_half_bits(orc.rmsnorm(r.h_mid, layer.mlp_norm, cfg.eps))
-    r.gu, r.a_gu = orc.gemv(layer.gateup.q, layer.gateup.s, r.x2, G)
+    attn = _take(forced, "attn", to_half_bits(r.attn))
+    r.o, r.a_o = orc.gemv(layer.o.q, layer.o.s, np.asarray(attn).reshape(-1), G)
+    r.h_mid = h + _take(forced, "o", r.o)
+    h_mid = _take(forced, "h_mid", r.h_mid)
+    r.x2 = orc.rmsnorm(h_mid, layer.mlp_norm, cfg.eps)
+    x2 = _take(forced, "x2", to_half_bits(r.x2))
+    r.gu, r.a_gu = orc.gemv(layer.gateup.q, layer.gateup.s, x2, G)
     r.m = orc.silu_gate(r.gu)
-    r.d, r.a_d = orc.gemv(layer.down.q, layer.down.s, to_half_bits(r.m), G)
-    r.h_out = r.h_mid + r.d
+    m = _take(forced, "m", to_half_bits(r.m))
+    r.d, r.a_d = orc.gemv(layer.down.q, layer.down.s, m, G)
+    r.h_out = h_mid + _take(forced, "d", r.d)
     return r
 
 
-def final_logits(h: np.ndarray, final_norm: np.ndarray, lm: Proj, cfg: Config, orc=None):
-    """(x_f fp16 bits, logits fp64, A, argmax) after the last layer."""
+def final_logits(h: np.ndarray, final_norm: np.ndarray, lm: Proj, cfg: Config, orc=None, forced_xf=None):
+    """(x_f fp64 (stored fp16), logits fp64, A, argmax) after the last layer;
+    forced_xf (fp16 bits) replaces the stored x_f as the lm_head input."""
     orc = orc or default()
-    xf = to_half_bits(orc.rmsnorm(h, final_norm, cfg.eps))
-    y, a = orc.gemv(lm.q, lm.s, xf, cfg.group)
+    xf = orc.rmsnorm(h, final_norm, cfg.eps)
+    xin = to_half_bits(xf) if forced_xf is None else forced_xf
+    y, a = orc.gemv(lm.q, lm.s, xin, cfg.group)
     return xf, y, a, orc.argmax(y)
 
 

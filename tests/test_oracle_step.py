@@ -67,11 +67,10 @@ def _rope_complex(x, pos):
 
 def layer_numpy(h, L, pos, kc, vc, table):
     nh, nkv = CFG.n_heads, CFG.n_kv
-    x1 = _r16(_rms(h, L.attn_norm))
+    x1u = _rms(h, L.attn_norm)
+    x1 = _r16(x1u)
     qkv = _deq(L.qkv) @ x1
-    if L.qkv_bias is not None:
-        qkv = qkv + L.qkv_bias
-    parts = qkv.reshape(nh + 2 * nkv, 128)
+    parts = (qkv + (L.qkv_bias if L.qkv_bias is not None else 0.0)).reshape(nh + 2 * nkv, 128)
     q = _rope_complex(parts[:nh], pos)
     k = _rope_complex(parts[nh:nh + nkv], pos)
     v = parts[nh + nkv:]
@@ -88,12 +87,13 @@ def layer_numpy(h, L, pos, kc, vc, table):
         att[hh] = p @ V[:, g]
     o = _deq(L.o) @ _r16(att).reshape(-1)
     h_mid = h + o
-    x2 = _r16(_rms(h_mid, L.mlp_norm))
+    x2u = _rms(h_mid, L.mlp_norm)
+    x2 = _r16(x2u)
     gu = _deq(L.gateup) @ x2
     gate, up = gu[:CFG.inter], gu[CFG.inter:]
     m = gate / (1.0 + np.exp(-gate)) * up
     d = _deq(L.down) @ _r16(m)
-    return dict(x1=x1, qkv=qkv, q=q, k=k, v=v, attn=att, o=o, h_mid=h_mid, x2=x2, gu=gu, m=m, d=d,
+    return dict(x1=x1u, qkv=qkv, q=q, k=k, v=v, attn=att, o=o, h_mid=h_mid, x2=x2u, gu=gu, m=m, d=d,
                 h_out=h_mid + d, kc=kc, vc=vc)
 
 
@@ -108,10 +108,8 @@ def pin_step_layer_vs_numpy(st, orc):
     pos = 37
     ref = layer_numpy(h, layers[0], pos, kc, vc, table)
     r = st.decoder_layer(h, layers[0], CFG, pos, kc, vc, table, orc=orc)
-    assert np.array_equal(_half(r.x1), ref["x1"])
-    for name in ("qkv", "q", "k", "v", "attn", "o", "h_mid", "gu", "m", "d", "h_out"):
+    for name in ("x1", "qkv", "q", "k", "v", "attn", "o", "h_mid", "x2", "gu", "m", "d", "h_out"):
         assert _close(getattr(r, name), ref[name]), name
-    assert np.array_equal(_half(r.x2), ref["x2"])
     assert np.array_equal(kc, ref["kc"]) and np.array_equal(vc, ref["vc"])
 
 
@@ -136,7 +134,7 @@ def pin_step_first_token(st, orc):
     h = np.random.default_rng(2).standard_normal(CFG.hidden)
     r = st.decoder_layer(h, layers[0], CFG, 0, kc, vc, table, orc=orc)
     nh, nkv = CFG.n_heads, CFG.n_kv
-    parts = r.qkv.reshape(nh + 2 * nkv, 128)
+    parts = (r.qkv + layers[0].qkv_bias).reshape(nh + 2 * nkv, 128)
     assert np.array_equal(r.k, parts[nh:nh + nkv]) and np.array_equal(r.q, parts[:nh])
     vh = _r16(parts[nh + nkv:])
     for hh in range(nh):
@@ -163,11 +161,38 @@ def pin_step_final_logits(st, orc):
     h = np.random.default_rng(3).standard_normal(CFG.hidden) * 2.0
     lm = ostep.Proj(*m["lm"])
     xf, y, a, best = st.final_logits(h, m["final_norm"], lm, CFG, orc=orc)
-    x_ref = _r16(_rms(h, m["final_norm"]))
-    assert np.array_equal(_half(xf), x_ref)
+    assert _close(xf, _rms(h, m["final_norm"]))
+    x_ref = _r16(xf)
     y_ref = _deq(lm) @ x_ref
     assert _close(y, y_ref) and best == int(np.argmax(y_ref))
     assert _close(a, np.abs(_deq(lm) * x_ref).sum(axis=1))
+
+
+def pin_step_forcing(st, orc):
+    """Teacher forcing: forcing every stage with the layer's own stored values
+    changes nothing; a forced zero attention output gives o = 0 and leaves the
+    residual stream unchanged; a forced x2 is what the gate/up product reads."""
+    _, layers = model(seed=13)
+    L = layers[0]
+    kc, vc, table = cache(14)
+    h = np.random.default_rng(4).standard_normal(CFG.hidden)
+    pos = 29
+    k1, v1 = kc.copy(), vc.copy()
+    r0 = st.decoder_layer(h, L, CFG, pos, k1, v1, table, orc=orc)
+    hb = ostep.to_half_bits
+    forced = dict(x1=hb(r0.x1), qkv=r0.qkv, q=hb(r0.q), k=hb(r0.k), v=hb(r0.v), attn=hb(r0.attn), o=r0.o,
+                  h_mid=r0.h_mid, x2=hb(r0.x2), m=hb(r0.m), d=r0.d)
+    k2, v2 = kc.copy(), vc.copy()
+    r1 = st.decoder_layer(h, L, CFG, pos, k2, v2, table, orc=orc, forced=forced)
+    for name in ("x1", "qkv", "q", "k", "v", "attn", "o", "h_mid", "x2", "gu", "m", "d", "h_out"):
+        assert np.array_equal(getattr(r0, name), getattr(r1, name)), name
+    assert np.array_equal(k1, k2) and np.array_equal(v1, v2)
+    r2 = st.decoder_layer(h, L, CFG, pos, kc.copy(), vc.copy(), table, orc=orc,
+                          forced=dict(attn=np.zeros((CFG.n_heads, 128), np.uint16)))
+    assert np.array_equal(r2.o, np.zeros(CFG.hidden)) and np.array_equal(r2.h_mid, h)
+    x2 = hb(np.random.default_rng(5).standard_normal(CFG.hidden))
+    r3 = st.decoder_layer(h, L, CFG, pos, kc.copy(), vc.copy(), table, orc=orc, forced=dict(x2=x2))
+    assert np.array_equal(r3.gu, orc.gemv(L.gateup.q, L.gateup.s, x2, CFG.group)[0])
 
 
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_step_")]
@@ -185,14 +210,18 @@ MUTANTS = [
     ("k_unrotated", "r.k = orc.rope(parts[nh:nh + nkv], pos, cfg.theta)", "r.k = parts[nh:nh + nkv].copy()"),
     ("q_position_shift", "r.q = orc.rope(parts[:nh], pos, cfg.theta)", "r.q = orc.rope(parts[:nh], pos + 1, cfg.theta)"),
     ("context_short", "page_table, pos + 1, nkv", "page_table, max(pos, 1), nkv"),
-    ("attn_residual_dropped", "r.h_mid = h + r.o", "r.h_mid = r.o"),
-    ("mlp_norm_of_layer_input", "orc.rmsnorm(r.h_mid, layer.mlp_norm", "orc.rmsnorm(h, layer.mlp_norm"),
-    ("mlp_residual_base", "r.h_out = r.h_mid + r.d", "r.h_out = h + r.d"),
-    ("bias_dropped", "r.qkv = r.qkv + layer.qkv_bias", "r.qkv = r.qkv"),
+    ("attn_residual_dropped", "r.h_mid = h + _take(forced, \"o\", r.o)", "r.h_mid = _take(forced, \"o\", r.o)"),
+    ("mlp_norm_of_layer_input", "orc.rmsnorm(h_mid, layer.mlp_norm", "orc.rmsnorm(h, layer.mlp_norm"),
+    ("mlp_residual_base", "r.h_out = h_mid + _take(forced, \"d\", r.d)", "r.h_out = h + _take(forced, \"d\", r.d)"),
+    ("bias_dropped", "qkv = qkv + layer.qkv_bias", "qkv = qkv"),
     ("cache_slot_shift", "pos % cfg.page", "(pos + 1) % cfg.page"),
     ("norm_weights_swapped", "orc.rmsnorm(h, layer.attn_norm", "orc.rmsnorm(h, layer.mlp_norm"),
-    ("final_norm_dropped", "xf = to_half_bits(orc.rmsnorm(h, final_norm, cfg.eps))", "xf = to_half_bits(h)"),
-    ("attn_unrounded_into_o", "to_half_bits(r.attn).reshape(-1)", "to_half_bits(r.attn.T).reshape(-1)"),
+    ("final_norm_dropped", "xf = orc.rmsnorm(h, final_norm, cfg.eps)", "xf = h"),
+    ("attn_transposed_into_o", "np.asarray(attn).reshape(-1)", "np.asarray(attn).T.reshape(-1)"),
+    ("forced_attn_ignored", 'attn = _take(forced, "attn", to_half_bits(r.attn))', "attn = to_half_bits(r.attn)"),
+    ("forced_x2_ignored", 'x2 = _take(forced, "x2", to_half_bits(r.x2))', "x2 = to_half_bits(r.x2)"),
+    ("down_input_from_gate", "r.d, r.a_d = orc.gemv(layer.down.q, layer.down.s, m, G)",
+     "r.d, r.a_d = orc.gemv(layer.down.q, layer.down.s, to_half_bits(r.gu[:cfg.inter]), G)"),
 ]
 
 
