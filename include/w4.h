@@ -262,6 +262,176 @@ w4_status w4_decode_linear_sweep(w4_sweep* sweep, void* stream);
 /* Release the handle (NULL is accepted). */
 w4_status w4_decode_linear_sweep_destroy(w4_sweep* sweep);
 
+/*
+ * The glue of a full decode step.  The pages name the model (Qwen2.5-Coder-7B:
+ * 28 decoder layers, hidden 3584, MLP 18944, vocabulary 152064; second page,
+ * "How to Build Your Own LLM Runtime from Scratch" (brifing.si), section 7
+ * "Model Dimensions and Structure") and the parts of its runtime (first page,
+ * "Technical Details", architecture bullet: INT4 weights, paged KV cache,
+ * attention) but not the decoder's equations.  They are read as that model
+ * family's pre-norm decoder: token embedding, RMSNorm before attention and
+ * before the MLP, rotary position embedding on q and k (pairs (i, i + 64) of
+ * each 128-wide head), grouped KV heads, SiLU-gated MLP, residual adds in
+ * fp32, a final RMSNorm and the lm_head with a greedy argmax.
+ */
+
+/*
+ * Embedding lookup: h[i] = table[t][i] widened to fp32 for i < hidden, with
+ * t = *token read on the device (clamped into [0, vocab): a wrong row, never
+ * a read outside the table).  Device, asynchronous.
+ *   table  device fp16 [vocab][hidden];  token  device int32 [1];
+ *   h      device fp32 [hidden].
+ * Rules: 1 <= hidden <= 2^20, vocab >= 1 (W4_ESHAPE); h 4-byte, table and
+ * token naturally aligned (W4_EALIGN).
+ */
+w4_status w4_embed(const uint16_t* table, int64_t vocab, int64_t hidden, const int32_t* token, float* h,
+                   void* stream);
+
+/*
+ * Residual add and RMSNorm, one kernel: if y != NULL, h[i] += y[i] in fp32
+ * (stored back to h); then
+ *     x[i] = fp16( h[i] * gamma[i] / sqrt(mean_j h[j]^2 + eps) )
+ * (fp32 arithmetic, one rounding to fp16 at the end, nearest even).
+ * Device, asynchronous, one workgroup; the sum of squares is reduced in a
+ * fixed order (deterministic).
+ *   h  device fp32 [n] (read, and written when y != NULL);  y  device fp32 [n]
+ *   or NULL;  gamma  device fp16 [n];  x  device fp16 [n].
+ * Rules: 1 <= n <= 2^20 (W4_ESHAPE); eps >= 0 and finite (W4_EINVAL).
+ */
+w4_status w4_add_rmsnorm(float* h, const float* y, const uint16_t* gamma, int64_t n, float eps, uint16_t* x,
+                         void* stream);
+
+/*
+ * Rotary embedding and KV-cache append for one new token at position
+ * p = *pos (device int32, clamped into [0, max_ctx)).  qkv holds the fused
+ * projection's output: n_heads query heads, then n_kv_heads key heads, then
+ * n_kv_heads value heads, 128 values each; bias (same length) is added first
+ * when not NULL.  Each q and k head is rotated pairwise,
+ *     r[i]      = x[i] cos(a_i) - x[i + 64] sin(a_i)
+ *     r[i + 64] = x[i + 64] cos(a_i) + x[i] sin(a_i),   a_i = p * theta^(-2i/128)
+ * (angle, sine and cosine in double, the rotation in fp32).  Rotated q goes to
+ * q_out (fp16); rotated k and the unrotated v go to the caches' slot of token
+ * p: page page_table[p / page_size] (clamped into [0, num_pages)), slot
+ * p % page_size.  ctx_len (when not NULL) is set to p + 1, the attention's
+ * context length.  Device, asynchronous, one kernel.
+ *   qkv   device fp32 [(n_heads + 2 n_kv_heads) * 128];  bias likewise or NULL;
+ *   q_out device fp16 [n_heads][128];
+ *   k_cache, v_cache  device fp16 [num_pages][n_kv_heads][page_size][128]
+ *   (the layout w4_attn_decode reads);  page_table  device int32.
+ * Rules as for w4_attn_decode (head_dim 128, n_heads 1..8 x n_kv_heads,
+ * power-of-two page_size <= 4096, 1 <= max_ctx <= 2^20); theta > 0.
+ */
+w4_status w4_rope_kv_append(const float* qkv, const float* bias, const int32_t* pos, int32_t n_heads,
+                            int32_t n_kv_heads, int32_t head_dim, double theta, uint16_t* q_out,
+                            uint16_t* k_cache, uint16_t* v_cache, const int32_t* page_table,
+                            int32_t num_pages, int32_t page_size, int32_t max_ctx, int32_t* ctx_len,
+                            void* stream);
+
+/* Weights and KV cache of one decoder layer (all device).  Packed matrices
+ * come from w4_pack (plain layout unless stated). */
+typedef struct w4_layer_desc {
+    const uint16_t* attn_norm;  /* fp16 [hidden]                                   */
+    const void* qkv_w;          /* (n_heads + 2 n_kv) * 128 rows, hidden inputs    */
+    const void* qkv_s;
+    const float* qkv_bias;      /* fp32 [(n_heads + 2 n_kv) * 128] or NULL          */
+    const void* o_w;            /* hidden rows, n_heads * 128 inputs               */
+    const void* o_s;
+    const uint16_t* mlp_norm;   /* fp16 [hidden]                                   */
+    const void* gateup_w;       /* gate/up layout, 2 * inter rows, hidden inputs   */
+    const void* gateup_s;
+    const void* down_w;         /* hidden rows, inter inputs                       */
+    const void* down_s;
+    uint16_t* k_cache;          /* fp16 [num_pages][n_kv][page_size][128]          */
+    uint16_t* v_cache;
+} w4_layer_desc;
+
+typedef struct w4_step_desc {
+    int32_t layers;
+    int32_t hidden;
+    int32_t n_heads;
+    int32_t n_kv_heads;
+    int32_t head_dim;           /* must be 128                                     */
+    int32_t inter;              /* MLP width                                       */
+    int64_t vocab;
+    int32_t group;              /* G of every packed matrix                        */
+    int32_t page_size;
+    int32_t num_pages;          /* pages in each layer's cache                     */
+    int32_t max_ctx;
+    float rms_eps;
+    double rope_theta;
+    const uint16_t* embed;      /* fp16 [vocab][hidden]                            */
+    const w4_layer_desc* layer; /* host array [layers], copied at create           */
+    const uint16_t* final_norm; /* fp16 [hidden]                                   */
+    const void* lm_w;           /* vocab rows, hidden inputs                       */
+    const void* lm_s;
+    const int32_t* page_table;  /* device int32, >= ceil(max_ctx / page_size), shared by the layers */
+    int32_t* token;             /* device int32 [1]: input token, replaced by the argmax */
+    int32_t* pos;               /* device int32 [1]: its position, incremented     */
+    float* logits;              /* device fp32 [vocab], written                    */
+    void* trace;                /* device, w4_decode_step_trace_layout bytes, or NULL */
+} w4_step_desc;
+
+/* Intermediate values a step copies into desc->trace (for checking each
+ * stage on its own); layer l's record starts at l * layer_stride, the field
+ * at offsets[field] within it (256-byte aligned).  The record at
+ * layers * layer_stride holds the final residual stream (W4_TRACE_H_IN) and
+ * the final norm's output (W4_TRACE_X1). */
+#define W4_TRACE_H_IN 0   /* fp32 [hidden]   residual stream at the layer input  */
+#define W4_TRACE_X1 1     /* fp16 [hidden]   attention-norm output               */
+#define W4_TRACE_QKV 2    /* fp32 [(n_heads + 2 n_kv) * 128]  projection, no bias */
+#define W4_TRACE_Q 3      /* fp16 [n_heads * 128]  rotated q                     */
+#define W4_TRACE_ATTN 4   /* fp16 [n_heads * 128]  attention output              */
+#define W4_TRACE_O 5      /* fp32 [hidden]   o_proj output                       */
+#define W4_TRACE_H_MID 6  /* fp32 [hidden]   residual stream after attention     */
+#define W4_TRACE_X2 7     /* fp16 [hidden]   MLP-norm output                     */
+#define W4_TRACE_M 8      /* fp16 [inter]    silu(gate) * up                     */
+#define W4_TRACE_D 9      /* fp32 [hidden]   down output                         */
+#define W4_TRACE_FIELDS 10
+
+/* Trace layout for a descriptor's dimensions (only the dimension fields are
+ * read).  Host only. */
+w4_status w4_decode_step_trace_layout(const w4_step_desc* desc, size_t* offsets, size_t* layer_stride,
+                                      size_t* total_bytes);
+
+typedef struct w4_step w4_step;
+
+/*
+ * Build one full decode step of the decoder read above, for batch 1:
+ *     h = embed[token]
+ *     per layer: x = rmsnorm(h) attn_norm;  qkv = x Wqkv (+ bias);
+ *                rope + append k, v at pos;  a = attention over pos + 1 tokens;
+ *                h += a Wo;  x = rmsnorm(h) mlp_norm;
+ *                h += (silu(x Wgate) * (x Wup)) Wdown
+ *     x = rmsnorm(h) final_norm;  logits = x Wlm;  token = argmax(logits);
+ *     pos += 1
+ * with the library's kernels (w4_embed, w4_add_rmsnorm, w4_gemv,
+ * w4_rope_kv_append, w4_attn_decode, w4_gemv_gateup_silu; each residual add
+ * is fused into the following norm).  Attention scale 1/sqrt(128).  Because
+ * token and pos are read and advanced on the device, one call of
+ * w4_decode_step per token continues the greedy decode with no host work;
+ * use_graph != 0 captures the whole step as one HIP graph (one submission per
+ * token, the pages' "CUDA Graph Optimization" bullet), use_graph == 0 keeps
+ * eager launches for the comparison.  The handle allocates its activation
+ * buffers and workspaces (device, at create, about 1 MB for the 7B shapes)
+ * and frees them at destroy; every pointer in the descriptor is baked in and
+ * must stay valid until destroy.  pos must stay below max_ctx (at max_ctx - 1
+ * the last cache slot is overwritten).  The handle is not thread-safe.
+ * Rules: shapes as for the individual calls; hidden, n_heads * 128, inter
+ * multiples of G; W4_ESHAPE / W4_EINVAL / W4_EALIGN before anything is
+ * allocated or launched.
+ */
+w4_status w4_decode_step_create(const w4_step_desc* desc, int32_t use_graph, w4_step** out);
+
+/* Run one token's step on `stream` (graph launch or eager launches). */
+w4_status w4_decode_step(w4_step* step, void* stream);
+
+/* Operations one step submits (kernels, plus the trace copies when traced):
+ * the graph's node count. */
+w4_status w4_decode_step_launches(const w4_step* step, int32_t* count);
+
+/* Release the handle and its buffers (NULL is accepted). */
+w4_status w4_decode_step_destroy(w4_step* step);
+
 #ifdef __cplusplus
 }
 #endif

@@ -11,6 +11,7 @@
 #include <vector>
 
 #include "w4.h"
+#include "w4_abi_util.h"
 #include "w4_internal.h"
 
 namespace w4i {
@@ -20,9 +21,11 @@ int64_t pack_w4t4(const uint8_t* q, const uint16_t* s, int64_t n, int64_t k, int
 
 using namespace w4i;
 
-namespace {
+namespace w4i {
 
+namespace {
 thread_local std::string g_last_error;
+}
 
 w4_status fail(w4_status code, const char* fmt, ...)
 {
@@ -35,19 +38,23 @@ w4_status fail(w4_status code, const char* fmt, ...)
     return code;
 }
 
-w4_status ok()
-{
-    return W4_OK;
-}
-
 w4_status hip_fail(hipError_t err, const char* what)
 {
     return fail(W4_EHIP, "%s failed: %s (%d)", what, hipGetErrorString(err), (int)err);
 }
 
-bool aligned16(const void* p)
+const char* last_error()
 {
-    return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+    return g_last_error.c_str();
+}
+
+}  // namespace w4i
+
+namespace {
+
+w4_status ok()
+{
+    return W4_OK;
 }
 
 w4_status check_shape(int64_t n, int64_t k, int32_t group, bool gateup, const char* who)
@@ -122,6 +129,15 @@ w4_status check_gemm_workspace(const GemmCall& c, size_t ws_bytes, const char* w
 
 }  // namespace
 
+namespace w4i {
+
+w4_status check_gemv(const GemvCall& c, const char* who)
+{
+    return validate_gemv(c, who);
+}
+
+}  // namespace w4i
+
 extern "C" {
 
 const char* w4_status_string(w4_status status)
@@ -140,7 +156,7 @@ const char* w4_status_string(w4_status status)
 
 const char* w4_last_error(void)
 {
-    return g_last_error.c_str();
+    return last_error();
 }
 
 int32_t w4_abi_version(void)
@@ -318,13 +334,8 @@ w4_status w4_attn_decode(const uint16_t* q, const uint16_t* k_cache, const uint1
         const char* who = "w4_attn_decode";
         if (!q || !k_cache || !v_cache || !page_table || !ctx_len || !out || !workspace)
             return fail(W4_EINVAL, "%s: null pointer", who);
-        if (head_dim != kAttnHeadDim) return fail(W4_ESHAPE, "%s: head_dim=%d must be 128", who, head_dim);
-        if (n_kv_heads < 1 || n_heads < n_kv_heads || n_heads % n_kv_heads != 0 || n_heads / n_kv_heads > 8)
-            return fail(W4_ESHAPE, "%s: n_heads=%d must be 1..8 times n_kv_heads=%d", who, n_heads, n_kv_heads);
-        if (page_size < 1 || page_size > 4096 || (page_size & (page_size - 1)) != 0)
-            return fail(W4_ESHAPE, "%s: page_size=%d must be a power of two <= 4096", who, page_size);
-        if (max_ctx < 1 || max_ctx > kAttnMaxCtx || num_pages < 1)
-            return fail(W4_ESHAPE, "%s: max_ctx=%d num_pages=%d", who, max_ctx, num_pages);
+        w4_status st = check_kv_shape(n_heads, n_kv_heads, head_dim, page_size, max_ctx, num_pages, who);
+        if (st != W4_OK) return st;
         if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(workspace) ||
             (reinterpret_cast<uintptr_t>(out) & 1u) || (reinterpret_cast<uintptr_t>(page_table) & 3u) ||
             (reinterpret_cast<uintptr_t>(ctx_len) & 3u))

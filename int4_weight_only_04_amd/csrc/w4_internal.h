@@ -113,6 +113,33 @@ int64_t attn_chunks(int32_t max_ctx);
 size_t attn_workspace_bytes(int32_t n_heads, int32_t max_ctx);
 hipError_t launch_attn(const AttnCall& call, hipStream_t stream);
 
+// Glue of a full decode step (head dimension 128).
+struct RopeCall {
+    const float* qkv;          // fp32 [(n_heads + 2 n_kv) * 128]: q heads, k heads, v heads
+    const float* bias;         // fp32, same length, or null
+    const int32_t* pos;        // device int32 [1], clamped to [0, max_ctx)
+    uint16_t* q_out;           // fp16 [n_heads][128]
+    uint16_t* k_cache;         // fp16 [num_pages][n_kv][page_size][128]
+    uint16_t* v_cache;
+    const int32_t* page_table;
+    int32_t* ctx_out;          // device int32 [1] <- pos + 1 (or null)
+    double theta;
+    int32_t n_heads;
+    int32_t n_kv;
+    int32_t page_size;         // power of two
+    int32_t num_pages;
+    int32_t max_ctx;
+};
+
+constexpr int64_t kMaxHidden = 1 << 20;
+
+hipError_t launch_embed(const uint16_t* table, int64_t vocab, int64_t hidden, const int32_t* token, float* h,
+                        hipStream_t stream);
+hipError_t launch_add_rmsnorm(float* h, const float* y, const uint16_t* gamma, int64_t n, float eps, uint16_t* x,
+                              hipStream_t stream);
+hipError_t launch_rope_append(const RopeCall& call, hipStream_t stream);
+hipError_t launch_advance(int32_t* pos, hipStream_t stream);
+
 // Launch one GEMV on `stream` (shape already validated by the caller); the
 // argmax epilogue adds a one-workgroup finalize kernel on the same stream.
 hipError_t launch_gemv(const GemvCall& call, hipStream_t stream);

@@ -25,7 +25,12 @@ EXPORTED = (
     "w4_gemv_workspace_size", "w4_gemv", "w4_gemv_gateup_silu", "w4_gemm_workspace_size", "w4_gemm", "w4_gemm_gateup_silu",
     "w4_attn_decode_workspace_size", "w4_attn_decode",
     "w4_decode_linear_sweep_create", "w4_decode_linear_sweep", "w4_decode_linear_sweep_destroy",
+    "w4_embed", "w4_add_rmsnorm", "w4_rope_kv_append",
+    "w4_decode_step_create", "w4_decode_step", "w4_decode_step_launches", "w4_decode_step_destroy",
+    "w4_decode_step_trace_layout",
 )
+
+TRACE_FIELDS = ("h_in", "x1", "qkv", "q", "attn", "o", "h_mid", "x2", "m", "d")
 
 
 class W4Error(RuntimeError):
@@ -47,6 +52,40 @@ class ProjDesc(ctypes.Structure):
         ("argmax", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class LayerDesc(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in (
+        "attn_norm", "qkv_w", "qkv_s", "qkv_bias", "o_w", "o_s", "mlp_norm", "gateup_w", "gateup_s",
+        "down_w", "down_s", "k_cache", "v_cache")]
+
+
+class StepDesc(ctypes.Structure):
+    _fields_ = [
+        ("layers", ctypes.c_int32),
+        ("hidden", ctypes.c_int32),
+        ("n_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("inter", ctypes.c_int32),
+        ("vocab", ctypes.c_int64),
+        ("group", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+        ("max_ctx", ctypes.c_int32),
+        ("rms_eps", ctypes.c_float),
+        ("rope_theta", ctypes.c_double),
+        ("embed", ctypes.c_void_p),
+        ("layer", ctypes.POINTER(LayerDesc)),
+        ("final_norm", ctypes.c_void_p),
+        ("lm_w", ctypes.c_void_p),
+        ("lm_s", ctypes.c_void_p),
+        ("page_table", ctypes.c_void_p),
+        ("token", ctypes.c_void_p),
+        ("pos", ctypes.c_void_p),
+        ("logits", ctypes.c_void_p),
+        ("trace", ctypes.c_void_p),
     ]
 
 
@@ -96,6 +135,24 @@ def lib():
     L.w4_decode_linear_sweep.argtypes = [vp, vp]
     L.w4_decode_linear_sweep_destroy.restype = i32
     L.w4_decode_linear_sweep_destroy.argtypes = [vp]
+    L.w4_embed.restype = i32
+    L.w4_embed.argtypes = [vp, i64, i64, vp, vp, vp]
+    L.w4_add_rmsnorm.restype = i32
+    L.w4_add_rmsnorm.argtypes = [vp, vp, vp, i64, ctypes.c_float, vp, vp]
+    L.w4_rope_kv_append.restype = i32
+    L.w4_rope_kv_append.argtypes = [vp, vp, vp, i32, i32, i32, ctypes.c_double, vp, vp, vp, vp, i32, i32, i32,
+                                    vp, vp]
+    L.w4_decode_step_create.restype = i32
+    L.w4_decode_step_create.argtypes = [ctypes.POINTER(StepDesc), i32, ctypes.POINTER(vp)]
+    L.w4_decode_step.restype = i32
+    L.w4_decode_step.argtypes = [vp, vp]
+    L.w4_decode_step_launches.restype = i32
+    L.w4_decode_step_launches.argtypes = [vp, ctypes.POINTER(i32)]
+    L.w4_decode_step_destroy.restype = i32
+    L.w4_decode_step_destroy.argtypes = [vp]
+    L.w4_decode_step_trace_layout.restype = i32
+    L.w4_decode_step_trace_layout.argtypes = [ctypes.POINTER(StepDesc), ctypes.POINTER(sz), ctypes.POINTER(sz),
+                                              ctypes.POINTER(sz)]
     _lib = L
     return L
 
@@ -318,6 +375,179 @@ class Sweep:
     def close(self):
         if self._handle:
             _check(lib().w4_decode_linear_sweep_destroy(self._handle), "w4_decode_linear_sweep_destroy")
+            self._handle = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def embed(table, token, h, stream=None):
+    """h[hidden] (fp32) = table[*token] for an fp16 table [vocab, hidden] and a
+    device int32 token of one element."""
+    import torch
+    vocab, hidden = table.shape
+    _check(lib().w4_embed(_dev_ptr(table, "table", torch.float16), vocab, hidden,
+                          _dev_ptr(token, "token", torch.int32, 1),
+                          _dev_ptr(h, "h", torch.float32, hidden), _stream(stream)), "w4_embed")
+
+
+def add_rmsnorm(h, y, gamma, eps: float, x, stream=None):
+    """h += y (when y is given), then x (fp16) = rmsnorm(h) * gamma."""
+    import torch
+    n = h.numel()
+    _check(lib().w4_add_rmsnorm(_dev_ptr(h, "h", torch.float32, n), _dev_ptr(y, "y", torch.float32, n),
+                                _dev_ptr(gamma, "gamma", torch.float16, n), n, float(eps),
+                                _dev_ptr(x, "x", torch.float16, n), _stream(stream)), "w4_add_rmsnorm")
+
+
+def rope_kv_append(qkv, bias, pos, n_heads: int, n_kv_heads: int, theta: float, q_out, k_cache, v_cache,
+                   page_table, max_ctx: int, ctx_len=None, stream=None):
+    """Rotate q and k of the fused projection output at device position *pos,
+    write q (fp16) to q_out and k, v to the paged caches; ctx_len <- pos + 1."""
+    import torch
+    rows = (n_heads + 2 * n_kv_heads) * 128
+    num_pages, _, page_size, _ = k_cache.shape
+    _check(lib().w4_rope_kv_append(_dev_ptr(qkv, "qkv", torch.float32, rows),
+                                   _dev_ptr(bias, "bias", torch.float32, rows),
+                                   _dev_ptr(pos, "pos", torch.int32, 1), n_heads, n_kv_heads, 128, float(theta),
+                                   _dev_ptr(q_out, "q_out", torch.float16, n_heads * 128),
+                                   _dev_ptr(k_cache, "k_cache", torch.float16),
+                                   _dev_ptr(v_cache, "v_cache", torch.float16, k_cache.numel()),
+                                   _dev_ptr(page_table, "page_table", torch.int32, -(-max_ctx // page_size)),
+                                   num_pages, page_size, max_ctx, _dev_ptr(ctx_len, "ctx_len", torch.int32, 1),
+                                   _stream(stream)), "w4_rope_kv_append")
+
+
+@dataclass
+class StepLayer:
+    """Device tensors of one decoder layer (packed matrices as uint8)."""
+    attn_norm: object
+    qkv_w: object
+    qkv_s: object
+    o_w: object
+    o_s: object
+    mlp_norm: object
+    gateup_w: object
+    gateup_s: object
+    down_w: object
+    down_s: object
+    k_cache: object
+    v_cache: object
+    qkv_bias: object = None
+
+
+def trace_layout(desc: "StepDesc") -> tuple[list[int], int, int]:
+    """(field offsets, layer stride, total bytes) of a step's trace buffer."""
+    offs = (ctypes.c_size_t * len(TRACE_FIELDS))()
+    stride, total = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().w4_decode_step_trace_layout(ctypes.byref(desc), offs, ctypes.byref(stride), ctypes.byref(total)),
+           "w4_decode_step_trace_layout")
+    return list(offs), stride.value, total.value
+
+
+def step_trace_bytes(*, hidden, n_heads, n_kv_heads, inter, layers) -> int:
+    """Bytes of the trace buffer a DecodeStep with these dimensions fills."""
+    d = StepDesc()
+    d.layers, d.hidden, d.n_heads, d.n_kv_heads, d.inter = layers, hidden, n_heads, n_kv_heads, inter
+    return trace_layout(d)[2]
+
+
+class DecodeStep:
+    """One full greedy decode step (embedding .. argmax, position advance) as
+    eager launches or one captured HIP graph; token and pos are device int32
+    tensors of one element that the step reads and advances."""
+
+    def __init__(self, *, hidden, n_heads, n_kv_heads, inter, vocab, group, page_size, max_ctx, rms_eps,
+                 rope_theta, embed, layers: Sequence[StepLayer], final_norm, lm_w, lm_s, page_table, token, pos,
+                 logits, trace=None, use_graph=True):
+        import torch
+        self._keep = (embed, list(layers), final_norm, lm_w, lm_s, page_table, token, pos, logits, trace)
+        qkv_rows = (n_heads + 2 * n_kv_heads) * 128
+        arr = (LayerDesc * len(layers))()
+        num_pages = None
+        for i, L in enumerate(layers):
+            d = arr[i]
+            d.attn_norm = _dev_ptr(L.attn_norm, "attn_norm", torch.float16, hidden)
+            d.mlp_norm = _dev_ptr(L.mlp_norm, "mlp_norm", torch.float16, hidden)
+            for name, (n, k, lay) in (("qkv", (qkv_rows, hidden, "plain")), ("o", (hidden, n_heads * 128, "plain")),
+                                      ("gateup", (2 * inter, hidden, "gateup")), ("down", (hidden, inter, "plain"))):
+                wb, sb = packed_size(n, k, group, lay)
+                setattr(d, name + "_w", _dev_ptr(getattr(L, name + "_w"), name + "_w", torch.uint8, wb))
+                setattr(d, name + "_s", _dev_ptr(getattr(L, name + "_s"), name + "_s", torch.uint8, sb))
+            d.qkv_bias = _dev_ptr(L.qkv_bias, "qkv_bias", torch.float32, qkv_rows)
+            if tuple(L.k_cache.shape[1:]) != (n_kv_heads, page_size, 128) or L.v_cache.shape != L.k_cache.shape:
+                raise ValueError("caches must be fp16 [num_pages, n_kv_heads, page_size, 128]")
+            if num_pages is not None and L.k_cache.shape[0] != num_pages:
+                raise ValueError("every layer's cache must have the same number of pages")
+            num_pages = L.k_cache.shape[0]
+            d.k_cache = _dev_ptr(L.k_cache, "k_cache", torch.float16)
+            d.v_cache = _dev_ptr(L.v_cache, "v_cache", torch.float16)
+        desc = StepDesc()
+        desc.layers, desc.hidden, desc.n_heads, desc.n_kv_heads = len(layers), hidden, n_heads, n_kv_heads
+        desc.head_dim, desc.inter, desc.vocab, desc.group = 128, inter, vocab, group
+        desc.page_size, desc.num_pages, desc.max_ctx = page_size, num_pages or 0, max_ctx
+        desc.rms_eps, desc.rope_theta = float(rms_eps), float(rope_theta)
+        desc.embed = _dev_ptr(embed, "embed", torch.float16, vocab * hidden)
+        desc.layer = arr
+        desc.final_norm = _dev_ptr(final_norm, "final_norm", torch.float16, hidden)
+        wb, sb = packed_size(vocab, hidden, group, "plain")
+        desc.lm_w = _dev_ptr(lm_w, "lm_w", torch.uint8, wb)
+        desc.lm_s = _dev_ptr(lm_s, "lm_s", torch.uint8, sb)
+        desc.page_table = _dev_ptr(page_table, "page_table", torch.int32, -(-max_ctx // page_size))
+        desc.token = _dev_ptr(token, "token", torch.int32, 1)
+        desc.pos = _dev_ptr(pos, "pos", torch.int32, 1)
+        desc.logits = _dev_ptr(logits, "logits", torch.float32, vocab)
+        self.layout = trace_layout(desc)
+        desc.trace = _dev_ptr(trace, "trace", torch.uint8, self.layout[2] if trace is not None else None)
+        self.dims = dict(hidden=hidden, n_heads=n_heads, n_kv_heads=n_kv_heads, inter=inter,
+                         layers=len(layers))
+        self.trace = trace
+        handle = ctypes.c_void_p()
+        _check(lib().w4_decode_step_create(ctypes.byref(desc), int(bool(use_graph)), ctypes.byref(handle)),
+               "w4_decode_step_create")
+        self._handle = handle
+        self.use_graph = use_graph
+
+    def read_trace(self) -> list[dict]:
+        """Host copy of the trace: one dict per layer (fp32 fields as float32,
+        fp16 fields as uint16 bits), then {"h_in", "x1"} of the final record."""
+        import numpy as np
+        if self.trace is None:
+            raise RuntimeError("step built without a trace buffer")
+        raw = self.trace.cpu().numpy()
+        offs, stride, _ = self.layout
+        H, nh, nkv, inter = (self.dims[k] for k in ("hidden", "n_heads", "n_kv_heads", "inter"))
+        spec = {"h_in": (np.float32, H), "x1": (np.uint16, H), "qkv": (np.float32, (nh + 2 * nkv) * 128),
+                "q": (np.uint16, nh * 128), "attn": (np.uint16, nh * 128), "o": (np.float32, H),
+                "h_mid": (np.float32, H), "x2": (np.uint16, H), "m": (np.uint16, inter), "d": (np.float32, H)}
+        out = []
+        for l in range(self.dims["layers"] + 1):
+            rec = {}
+            for f, name in enumerate(TRACE_FIELDS):
+                if l == self.dims["layers"] and name not in ("h_in", "x1"):
+                    continue
+                dt, n = spec[name]
+                start = l * stride + offs[f]
+                rec[name] = raw[start:start + n * np.dtype(dt).itemsize].view(dt).copy()
+            out.append(rec)
+        return out
+
+    def launches(self) -> int:
+        n = ctypes.c_int32()
+        _check(lib().w4_decode_step_launches(self._handle, ctypes.byref(n)), "w4_decode_step_launches")
+        return n.value
+
+    def run(self, stream=None):
+        if not self._handle:
+            raise RuntimeError("decode step destroyed")
+        _check(lib().w4_decode_step(self._handle, _stream(stream)), "w4_decode_step")
+
+    def close(self):
+        if self._handle:
+            _check(lib().w4_decode_step_destroy(self._handle), "w4_decode_step_destroy")
             self._handle = ctypes.c_void_p()
 
     def __del__(self):

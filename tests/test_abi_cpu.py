@@ -233,6 +233,112 @@ def test_sweep_create_validation():
     assert L.w4_decode_linear_sweep(None, None) == w4.EINVAL
 
 
+def test_step_glue_validation_before_launch():
+    """Embedding, residual + RMSNorm and rotary/KV-append checks run before
+    any device call."""
+    L = w4.lib()
+    A = 1 << 20
+    assert L.w4_embed(None, 10, 64, A, A, None) == w4.EINVAL
+    assert L.w4_embed(A, 10, 0, A, A, None) == w4.ESHAPE
+    assert L.w4_embed(A, 0, 64, A, A, None) == w4.ESHAPE
+    assert L.w4_embed(A + 1, 10, 64, A, A, None) == w4.EALIGN
+    assert L.w4_embed(A, 10, 64, A + 2, A, None) == w4.EALIGN
+    assert L.w4_add_rmsnorm(A, None, A, 0, 1e-6, A, None) == w4.ESHAPE
+    assert L.w4_add_rmsnorm(A, None, A, 64, -1.0, A, None) == w4.EINVAL
+    assert L.w4_add_rmsnorm(A, None, A, 64, float("nan"), A, None) == w4.EINVAL
+    assert L.w4_add_rmsnorm(None, None, A, 64, 1e-6, A, None) == w4.EINVAL
+    assert L.w4_add_rmsnorm(A + 2, None, A, 64, 1e-6, A, None) == w4.EALIGN
+
+    def rope(qkv=A, bias=None, pos=A, nh=28, nkv=4, dim=128, theta=1e6, q=A, kc=A, vc=A, tab=A, npages=4,
+             page=16, max_ctx=64, ctx=A):
+        return L.w4_rope_kv_append(qkv, bias, pos, nh, nkv, dim, theta, q, kc, vc, tab, npages, page, max_ctx,
+                                   ctx, None)
+
+    assert rope(dim=64) == w4.ESHAPE
+    assert rope(nh=30) == w4.ESHAPE
+    assert rope(page=12) == w4.ESHAPE
+    assert rope(max_ctx=0) == w4.ESHAPE
+    assert rope(theta=0.0) == w4.EINVAL
+    assert rope(pos=None) == w4.EINVAL
+    assert rope(kc=None) == w4.EINVAL
+    assert rope(qkv=A + 2) == w4.EALIGN
+    assert rope(bias=A + 1) == w4.EALIGN
+
+
+def _step_desc(layers_arr, **kw):
+    A = 1 << 20
+    d = w4.StepDesc()
+    vals = dict(layers=len(layers_arr), hidden=256, n_heads=2, n_kv_heads=1, head_dim=128, inter=512, vocab=300,
+                group=64, page_size=16, num_pages=4, max_ctx=64, rms_eps=1e-6, rope_theta=1e6)
+    vals.update(kw)
+    for k, v in vals.items():
+        setattr(d, k, v)
+    d.layer = layers_arr
+    for name in ("embed", "final_norm", "lm_w", "lm_s", "page_table", "token", "pos", "logits"):
+        setattr(d, name, A)
+    return d
+
+
+def _layer_arr(n):
+    A = 1 << 20
+    arr = (w4.LayerDesc * n)()
+    for L in arr:
+        for name, _ in w4.LayerDesc._fields_:
+            setattr(L, name, A)
+        L.qkv_bias = None
+    return arr
+
+
+def test_decode_step_create_validation():
+    """Every descriptor rule is checked before anything is allocated."""
+    L = w4.lib()
+    handle = ctypes.c_void_p()
+
+    def create(d):
+        return L.w4_decode_step_create(ctypes.byref(d), 1, ctypes.byref(handle))
+
+    arr = _layer_arr(2)
+    assert L.w4_decode_step_create(None, 1, ctypes.byref(handle)) == w4.EINVAL
+    assert create(_step_desc(arr, layers=0)) == w4.EINVAL
+    assert create(_step_desc(arr, head_dim=64)) == w4.ESHAPE
+    assert create(_step_desc(arr, n_heads=3, n_kv_heads=2)) == w4.ESHAPE
+    assert create(_step_desc(arr, rms_eps=-1.0)) == w4.EINVAL
+    assert create(_step_desc(arr, rope_theta=0.0)) == w4.EINVAL
+    assert create(_step_desc(arr, hidden=200)) == w4.ESHAPE        # k % G for qkv
+    assert "layer 0 qkv" in w4.last_error()
+    assert create(_step_desc(arr, inter=500)) == w4.ESHAPE         # k % G for down
+    assert "down" in w4.last_error()
+    d = _step_desc(arr)
+    d.token = None
+    assert create(d) == w4.EINVAL
+    d = _step_desc(arr)
+    d.trace = (1 << 20) + 16
+    assert create(d) == w4.EALIGN
+    bad = _layer_arr(2)
+    bad[1].k_cache = None
+    assert create(_step_desc(bad)) == w4.EINVAL
+    assert "layer 1" in w4.last_error()
+    bad = _layer_arr(2)
+    bad[1].gateup_w = (1 << 20) + 8
+    assert create(_step_desc(bad)) == w4.EALIGN
+    assert not handle.value
+    assert L.w4_decode_step(None, None) == w4.EINVAL
+    assert L.w4_decode_step_destroy(None) == w4.OK
+
+
+def test_decode_step_trace_layout():
+    d = _step_desc(_layer_arr(3), hidden=512, n_heads=4, n_kv_heads=2, inter=1024)
+    offs, stride, total = w4.trace_layout(d)
+    sizes = [4 * 512, 2 * 512, 4 * 1024, 2 * 512, 2 * 512, 4 * 512, 4 * 512, 2 * 512, 2 * 1024, 4 * 512]
+    expect, o = [], 0
+    for b in sizes:
+        expect.append(o)
+        o += -(-b // 256) * 256
+    assert offs == expect and stride == o
+    assert total == 3 * stride + expect[2]
+    assert w4.step_trace_bytes(hidden=512, n_heads=4, n_kv_heads=2, inter=1024, layers=3) == total
+
+
 def test_launch_without_device_reports_hip_error():
     """With no GPU present, a validated call fails with W4_EHIP (no launch)."""
     import torch
