@@ -18,6 +18,14 @@ the CPU oracle timed on a bounded sample on the host.
 times 28 layers' decode attention over a paged fp16 KV cache at a
 4096-token context (GB/s against the HBM peak).
 
+    python bench.py --workload step [--steps 128] [--warmup 5]
+
+times the full batch-1 decode step (embedding, 28 pre-norm decoder layers
+with RMSNorm, the INT4 projections, RoPE + paged KV append and attention,
+final norm, lm_head + greedy argmax, position advance) as one captured HIP
+graph per token, for tokens 512..512+steps-1 after a 512-token prompt (the
+pages' pp512/tg128 protocol), and the same step as eager launches.
+
     python bench.py --workload prefill [--steps 10] [--warmup 2]
 
 times the prefill counterpart instead: the 28 layers' four INT4 products for
@@ -47,6 +55,7 @@ MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 matrix-core peak
 METRIC = "achieved HBM GB/s (% of peak) and ms per 28-layer+lm_head INT4 linear sweep"
 PREFILL_METRIC = "prefill TFLOP/s (% of fp16 MFMA peak) and ms per 28-layer 512-token INT4 linear sweep"
 ATTN_METRIC = "decode attention GB/s (% of HBM peak) and ms per 28-layer paged-KV attention at 4096-token context"
+STEP_METRIC = "batch-1 decode tokens/s and ms per full 28-layer decode step (hipGraph), tokens 512..639"
 ATTN_HEADS, ATTN_KV_HEADS, ATTN_PAGE, ATTN_CTX = 28, 4, 16, 4096
 KERNEL_SRC = os.path.join(ROOT, "int4_weight_only_04_amd", "csrc", "w4_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gateup_silu_37888x3584.json")
@@ -477,20 +486,302 @@ def run_attention(args) -> int:
     return 0
 
 
+def build_step(layers: int, device: str = "cuda"):
+    """Device model of the full decode step: the sweep's packed weights (same
+    seeds), seeded RMSNorm weights, an fp16 embedding table of uniform random
+    magnitudes in [0.25, 0.5), and per layer a paged fp16 KV cache of
+    4096 tokens (pages of 16) filled with N(0, 1) values standing in for the
+    prompt, one shared permuted page table.  No qkv bias (the pages give none)."""
+    import torch
+    from int4_weight_only_04_amd import w4
+    H, V = synthetic.HIDDEN, synthetic.VOCAB
+    nkv, page, max_ctx = synthetic.KV_HEADS, synthetic.PAGE, synthetic.MAX_CTX
+    num_pages = max_ctx // page
+    specs = synthetic.sweep_projections(layers)
+
+    def packed(p):
+        layout = "gateup" if p.kind == "gateup" else "plain"
+        wb, sb = w4.packed_size(p.n, p.k, p.group, layout)
+        pw, ps, _ = synthetic.packed_random(p.seed, wb, sb // 2, p.k)
+        return torch.from_numpy(pw).to(device), torch.from_numpy(ps).to(device)
+
+    def f16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device).view(torch.float16)
+
+    g = torch.Generator(device="cpu").manual_seed(5000)
+    step_layers = []
+    for l in range(layers):
+        pq, po, pg, pd = specs[4 * l: 4 * l + 4]
+        (qw, qs), (ow, os_), (gw, gs), (dw, ds) = packed(pq), packed(po), packed(pg), packed(pd)
+        shape = (num_pages, nkv, page, 128)
+        kc = torch.randn(shape, generator=g).to(torch.float16).to(device)
+        vc = torch.randn(shape, generator=g).to(torch.float16).to(device)
+        step_layers.append(w4.StepLayer(
+            attn_norm=f16(synthetic.norm_weights(6000 + 10 * l, H)), qkv_w=qw, qkv_s=qs, o_w=ow, o_s=os_,
+            mlp_norm=f16(synthetic.norm_weights(6001 + 10 * l, H)), gateup_w=gw, gateup_s=gs, down_w=dw,
+            down_s=ds, k_cache=kc, v_cache=vc))
+    lw, ls = packed(specs[-1])
+    embed = f16(synthetic.half_bits_uniform(6900, V * H, lo_exp=13)).view(V, H)
+    model = dict(
+        layers=step_layers, embed=embed, final_norm=f16(synthetic.norm_weights(6901, H)), lm_w=lw, lm_s=ls,
+        page_table=torch.from_numpy(synthetic.page_table(6902, num_pages, num_pages)).to(device),
+        token=torch.zeros(1, dtype=torch.int32, device=device),
+        pos=torch.zeros(1, dtype=torch.int32, device=device),
+        logits=torch.empty(V, dtype=torch.float32, device=device))
+    return specs, model
+
+
+def make_step(model, use_graph: bool):
+    from int4_weight_only_04_amd import w4
+    return w4.DecodeStep(hidden=synthetic.HIDDEN, n_heads=synthetic.HEADS, n_kv_heads=synthetic.KV_HEADS,
+                         inter=synthetic.MLP, vocab=synthetic.VOCAB, group=synthetic.GROUP,
+                         page_size=synthetic.PAGE, max_ctx=synthetic.MAX_CTX, rms_eps=1e-6, rope_theta=1e6,
+                         use_graph=use_graph, **model)
+
+
+def step_bytes(specs, layers: int, ctx: int) -> int:
+    """Algorithmic bytes of one decode step at context ctx: the 113 INT4
+    products (as in the sweep), each layer's attention over ctx cached tokens,
+    the embedding row, the norm weights and the residual traffic."""
+    H = synthetic.HIDDEN
+    glue = 2 * H + (2 * layers + 1) * (2 * H + 4 * H * 3)  # embedding row; per norm: gamma, h, y, h
+    return sweep_bytes(specs) + layers * attn_bytes(ctx) + glue
+
+
+def run_steps(step, model, stream, start_token: int, start_pos: int, n: int, record: bool = False):
+    """Run n steps from (start_token, start_pos); return the tokens if record."""
+    import torch
+    model["token"].fill_(start_token)
+    model["pos"].fill_(start_pos)
+    torch.cuda.synchronize()
+    toks = []
+    for _ in range(n):
+        step.run(stream)
+        if record:
+            stream.synchronize()
+            toks.append(int(model["token"].item()))
+    return toks
+
+
+class PyEagerStep:
+    """The same decode step issued op by op from Python through the per-op C
+    ABI (w4_embed, w4_add_rmsnorm, w4_gemv, w4_rope_kv_append, w4_attn_decode,
+    w4_gemv_gateup_silu): what a host-driven eager loop costs."""
+
+    def __init__(self, model):
+        import torch
+        from int4_weight_only_04_amd import w4
+        H, I = synthetic.HIDDEN, synthetic.MLP
+        nh, nkv = synthetic.HEADS, synthetic.KV_HEADS
+        self.m, self.w4 = model, w4
+        dev = "cuda"
+        self.h = torch.empty(H, dtype=torch.float32, device=dev)
+        self.y = torch.empty(H, dtype=torch.float32, device=dev)
+        self.x = torch.empty(H, dtype=torch.float16, device=dev)
+        self.qkv = torch.empty((nh + 2 * nkv) * 128, dtype=torch.float32, device=dev)
+        self.q = torch.empty((nh, 128), dtype=torch.float16, device=dev)
+        self.ao = torch.empty((nh, 128), dtype=torch.float16, device=dev)
+        self.mh = torch.empty(I, dtype=torch.float16, device=dev)
+        self.ctx = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.attn_ws = torch.empty(w4.attn_decode_workspace_size(nh, synthetic.MAX_CTX), dtype=torch.uint8,
+                                   device=dev)
+        self.lm_ws = torch.empty(w4.gemv_workspace_size(synthetic.VOCAB, H, synthetic.GROUP, True),
+                                 dtype=torch.uint8, device=dev)
+        self.scale = 1.0 / float(np.sqrt(128.0))
+
+    def run(self, stream):
+        w4, m = self.w4, self.m
+        H, I, G = synthetic.HIDDEN, synthetic.MLP, synthetic.GROUP
+        nh, nkv = synthetic.HEADS, synthetic.KV_HEADS
+        rows = (nh + 2 * nkv) * 128
+        w4.embed(m["embed"], m["token"], self.h, stream=stream)
+        for l, L in enumerate(m["layers"]):
+            w4.add_rmsnorm(self.h, None if l == 0 else self.y, L.attn_norm, 1e-6, self.x, stream=stream)
+            w4.gemv(L.qkv_w, L.qkv_s, self.x, self.qkv, rows, H, G, stream=stream)
+            w4.rope_kv_append(self.qkv, L.qkv_bias, m["pos"], nh, nkv, 1e6, self.q, L.k_cache, L.v_cache,
+                              m["page_table"], synthetic.MAX_CTX, self.ctx, stream=stream)
+            w4.attn_decode(self.q, L.k_cache, L.v_cache, m["page_table"], self.ctx, synthetic.MAX_CTX, self.ao,
+                           nkv, synthetic.PAGE, self.scale, self.attn_ws, stream=stream)
+            w4.gemv(L.o_w, L.o_s, self.ao, self.y, H, nh * 128, G, stream=stream)
+            w4.add_rmsnorm(self.h, self.y, L.mlp_norm, 1e-6, self.x, stream=stream)
+            w4.gemv_gateup_silu(L.gateup_w, L.gateup_s, self.x, self.mh, 2 * I, H, G, stream=stream)
+            w4.gemv(L.down_w, L.down_s, self.mh, self.y, H, I, G, stream=stream)
+        w4.add_rmsnorm(self.h, self.y, m["final_norm"], 1e-6, self.x, stream=stream)
+        w4.gemv(m["lm_w"], m["lm_s"], self.x, m["logits"], synthetic.VOCAB, H, G, argmax=m["token"],
+                workspace=self.lm_ws, stream=stream)
+        import torch
+        with torch.cuda.stream(stream):
+            m["pos"].add_(1)
+
+
+def step_cpu_baseline(ctx: int):
+    """The oracle's decode step (single thread, fp64) on a bounded sample: one
+    full-width layer at context ctx and the lm_head, scaled to 28 layers."""
+    import oracle
+    from oracle import step as ostep
+    H, I, V, G = synthetic.HIDDEN, synthetic.MLP, synthetic.VOCAB, synthetic.GROUP
+    nh, nkv, page = synthetic.HEADS, synthetic.KV_HEADS, synthetic.PAGE
+    m = synthetic.step_model(6100, hidden=H, n_heads=nh, n_kv=nkv, inter=I, vocab=V, group=G, layers=1,
+                             embed=False)
+    L = m["layers"][0]
+    lay = ostep.Layer(attn_norm=L["attn_norm"], qkv=ostep.Proj(*L["qkv"]), o=ostep.Proj(*L["o"]),
+                      mlp_norm=L["mlp_norm"], gateup=ostep.Proj(*L["gateup"]), down=ostep.Proj(*L["down"]))
+    cfg = ostep.Config(hidden=H, n_heads=nh, n_kv=nkv, inter=I, group=G, page=page, eps=1e-6, theta=1e6)
+    pages = -(-(ctx + 1) // page)
+    kc, vc = synthetic.kv_prefix(6101, pages, nkv, page)
+    table = np.arange(pages, dtype=np.int32)
+    h = np.random.default_rng(6102).standard_normal(H)
+    oracle.default()
+    t0 = time.perf_counter()
+    r = ostep.decoder_layer(h, lay, cfg, ctx, kc, vc, table)
+    t_layer = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    ostep.final_logits(r.h_out, m["final_norm"], ostep.Proj(*m["lm"]), cfg)
+    t_lm = time.perf_counter() - t0
+    per_token = synthetic.LAYERS * t_layer + t_lm
+    return {
+        "value": 1.0 / per_token,
+        "unit": "tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"one full-width decoder layer at context {ctx + 1} ({t_layer:.2f} s) and the lm_head with "
+                   f"argmax ({t_lm:.2f} s), single-threaded fp64, scaled to {synthetic.LAYERS} layers"),
+        "seconds": t_layer + t_lm,
+    }
+
+
+def run_step(args) -> int:
+    """The full decode step, graph and eager, on the 7B-class shapes."""
+    import torch
+    layers = args.layers
+    prompt = synthetic.PROMPT
+    steps, warmup = args.steps, args.warmup
+    if prompt + steps > synthetic.MAX_CTX or warmup > prompt:
+        print("bench.py: prompt + steps must stay within the 4096-token context", file=sys.stderr)
+        return 2
+    print(f"[bench] building the decode-step model ({layers} layers)", file=sys.stderr, flush=True)
+    specs, model = build_step(layers)
+    stream = torch.cuda.Stream()
+    graph = make_step(model, True)
+    eager = make_step(model, False)
+    launches = graph.launches()
+
+    print("[bench] graph vs eager token check", file=sys.stderr, flush=True)
+    check_n = 12
+    toks_graph = run_steps(graph, model, stream, 1234, prompt, check_n, record=True)
+    toks_eager = run_steps(eager, model, stream, 1234, prompt, check_n, record=True)
+    pyeager = PyEagerStep(model)
+    toks_py = run_steps(pyeager, model, stream, 1234, prompt, check_n, record=True)
+
+    def timed(step, n_warm, n):
+        run_steps(step, model, stream, 1234, prompt - n_warm, n_warm)
+        stream.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        a.record(stream)
+        for _ in range(n):
+            step.run(stream)
+        b.record(stream)
+        stream.synchronize()
+        return a.elapsed_time(b) / n, (time.perf_counter() - t0) * 1e3 / n
+
+    print(f"[bench] graph: {warmup} warmup + {steps} timed tokens", file=sys.stderr, flush=True)
+    ms, wall_ms = timed(graph, warmup, steps)
+    print(f"[bench] eager: 2 warmup + {args.eager_steps} timed tokens", file=sys.stderr, flush=True)
+    eager_ms, eager_wall = timed(eager, 2, args.eager_steps)
+    print(f"[bench] python-driven eager: 2 warmup + {args.eager_steps} timed tokens", file=sys.stderr, flush=True)
+    py_ms, py_wall = timed(pyeager, 2, args.eager_steps)
+
+    print("[bench] dominant kernel", file=sys.stderr, flush=True)
+    from int4_weight_only_04_amd import w4
+    x = torch.zeros(synthetic.HIDDEN, dtype=torch.float16, device="cuda")
+    hbuf = torch.empty(synthetic.MLP, dtype=torch.float16, device="cuda")
+    gu = [w4.Proj(w4.PROJ_GATEUP_SILU, 2 * synthetic.MLP, synthetic.HIDDEN, synthetic.GROUP, L.gateup_w, L.gateup_s,
+                  x, hbuf) for L in model["layers"]]
+    gu_mean_ms, gu_launches = time_dominant_kernel(gu, stream)
+    gu_bytes = algorithmic_bytes("gateup", 2 * synthetic.MLP, synthetic.HIDDEN, synthetic.GROUP)
+    gu_gbs = gu_bytes / (gu_mean_ms * 1e-3) / 1e9
+    graph.close()
+    eager.close()
+
+    mid_ctx = prompt + steps // 2
+    nbytes = step_bytes(specs, layers, mid_ctx)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    out = {
+        "metric": STEP_METRIC,
+        "value": round(1000.0 / ms, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"batch-1 greedy decode, one hipGraph per token: embedding, {layers} pre-norm decoder "
+                         "layers (RMSNorm, INT4 qkv 3584->4608, RoPE + paged fp16 KV append, attention with 28 "
+                         "query / 4 KV heads, INT4 o_proj, RMSNorm, INT4 gate/up 3584->2x18944 + silu, INT4 down "
+                         "18944->3584, fp32 residual), final RMSNorm, INT4 lm_head 3584->152064 + argmax, "
+                         f"tokens {prompt}..{prompt + steps - 1} after a {prompt}-token prompt"),
+            "kernels_per_step": launches,
+            "algorithmic_bytes_per_step_at_mid_context": nbytes,
+            "achieved_gbs": round(gbs, 1),
+            "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+            "wall_ms_per_step": round(wall_ms, 4),
+            "eager_ms_per_step": round(eager_ms, 4),
+            "eager_wall_ms_per_step": round(eager_wall, 4),
+            "graph_speedup_vs_eager": round(eager_ms / ms, 3),
+            "graph_eager_tokens_equal": toks_graph == toks_eager,
+            "python_eager_ms_per_step": round(py_ms, 4),
+            "python_eager_wall_ms_per_step": round(py_wall, 4),
+            "graph_speedup_vs_python_eager": round(py_wall / wall_ms, 3),
+            "python_eager_tokens_equal": toks_graph == toks_py,
+            "pages_context_h100": {"runtime_ms_per_token": 16.7, "eager_ms_per_token": 119,
+                                   "llama_cpp_q4_k_m_ms_per_token": 4.95},
+        },
+        "roofline": {
+            "kernel": "gemv_w4_kernel<2, gate/up+silu> 37888x3584 g128",
+            "bound": "hbm",
+            "achieved": round(gu_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
+            "traffic": read_traffic(gu_bytes),
+            "algorithmic_bytes_per_launch": gu_bytes,
+            "avg_launch_us": round(gu_mean_ms * 1e3, 3),
+            "launches_timed": gu_launches,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle decode step)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = step_cpu_baseline(mid_ctx)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 50; 128 for --workload step, the pages' tg128)")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--layers", type=int, default=synthetic.LAYERS)
     ap.add_argument("--eager-steps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", choices=("decode", "prefill", "attention"), default="decode",
+    ap.add_argument("--workload", choices=("decode", "prefill", "attention", "step"), default="decode",
                     help="decode: the per-token GEMV sweep (default); prefill: the 512-token GEMM sweep; "
-                         "attention: 28 layers' paged-KV decode attention at a 4096-token context")
+                         "attention: 28 layers' paged-KV decode attention at a 4096-token context; "
+                         "step: the full decode step (tokens 512.. after a 512-token prompt)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args(argv)
+    if args.steps is None:
+        args.steps = 128 if args.workload == "step" else 50
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the INT4 decode GEMV sweep is a single-GPU path here; "
@@ -518,6 +809,8 @@ def main(argv=None):
         return run_prefill(args)
     if args.workload == "attention":
         return run_attention(args)
+    if args.workload == "step":
+        return run_step(args)
 
     print(f"[bench] building sweep ({args.layers} layers)", file=sys.stderr, flush=True)
     specs, projs = build_sweep(args.layers)

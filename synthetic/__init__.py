@@ -137,14 +137,20 @@ PAGE = 16
 MAX_CTX = 4096
 
 
+def norm_weights(seed: int, n: int) -> np.ndarray:
+    """RMSNorm weights: U[0.5, 1.5] drawn in float32, rounded to fp16 (bits)."""
+    return _scales(_rng(seed), n, 0.5, 1.5)
+
+
 def step_model(seed: int, *, hidden: int, n_heads: int, n_kv: int, inter: int, vocab: int, group: int,
-               layers: int, bias: bool = False, s_lo: float = 0.001, s_hi: float = 0.02) -> dict:
+               layers: int, bias: bool = False, s_lo: float = 0.001, s_hi: float = 0.02,
+               embed: bool = True) -> dict:
     """Logical weights of a small decoder for the full-step tests.
 
     Layer l draws from seed * 1000 + 10 * l + p with p = 0 qkv, 1 o_proj,
     2 gate/up, 3 down (nibbles then scales, as `logical`), 4 attention norm,
     5 MLP norm, 6 qkv bias; the embedding table, final norm and lm_head use
-    seed * 1000 + 900, 901, 902.  Norm weights ~ U[0.5, 1.5] and embeddings
+    seed * 1000 + 900, 901, 902 (embed=False skips the table).  Norm weights ~ U[0.5, 1.5] and embeddings
     ~ N(0, 1) (float32 draws rounded to fp16); biases ~ N(0, 0.5) in float32.
     Returns plain arrays: {"embed", "final_norm", "lm": (q, s), "layers":
     [{"attn_norm", "qkv", "qkv_bias", "o", "mlp_norm", "gateup", "down"}]}."""
@@ -155,7 +161,7 @@ def step_model(seed: int, *, hidden: int, n_heads: int, n_kv: int, inter: int, v
         return q, s
 
     def norm(sd, n):
-        return _scales(_rng(sd), n, 0.5, 1.5)
+        return norm_weights(sd, n)
 
     base = seed * 1000
     qkv_rows = (n_heads + 2 * n_kv) * 128
@@ -172,7 +178,7 @@ def step_model(seed: int, *, hidden: int, n_heads: int, n_kv: int, inter: int, v
             "qkv_bias": (_rng(b + 6).standard_normal(qkv_rows, dtype=np.float32) * np.float32(0.5)) if bias else None,
         }
         out["layers"].append(layer)
-    out["embed"] = _acts(_rng(base + 900), vocab * hidden).reshape(vocab, hidden)
+    out["embed"] = _acts(_rng(base + 900), vocab * hidden).reshape(vocab, hidden) if embed else None
     out["final_norm"] = norm(base + 901, hidden)
     out["lm"] = proj(base + 902, vocab, hidden)
     return out
