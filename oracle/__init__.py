@@ -17,6 +17,8 @@ inputs per row are the workload definition's format, the pages being silent):
     A[n]    = sum_k |w[n, k] * x[k]|
     h[j]    = silu(y[j]) * y[I + j],  silu(t) = t / (1 + exp(-t))
     argmax  = lowest index of max y
+    W4A8:   c[k] = rint(x[k] * 127 / amax_g), s_g = amax_g / 127 (binary32),
+            y[n] = sum_k w[n, k] * c[k] * s_g
 """
 from __future__ import annotations
 
@@ -81,6 +83,14 @@ class Oracle:
         lib.oracle_silu_gate.argtypes = [p, i64, p]
         lib.oracle_argmax.restype = i64
         lib.oracle_argmax.argtypes = [p, i64]
+        lib.oracle_quantize_act8.restype = None
+        lib.oracle_quantize_act8.argtypes = [p, i64, i32, p, p]
+        lib.oracle_act8_block_order.restype = None
+        lib.oracle_act8_block_order.argtypes = [p, i64, p]
+        lib.oracle_gemv_a8_rows.restype = None
+        lib.oracle_gemv_a8_rows.argtypes = [p, p, p, p, i64, i64, i32, p, i64, p, p]
+        lib.oracle_gemv_a8_packed_rows.restype = None
+        lib.oracle_gemv_a8_packed_rows.argtypes = [p, p, p, p, i64, i64, i32, i32, p, i64, p, p]
         self.lib = lib
         self.path = path
 
@@ -242,6 +252,57 @@ class Oracle:
         y = np.ascontiguousarray(y, dtype=np.float64)
         return int(self.lib.oracle_argmax(_ptr(y), y.size))
 
+    def quantize_act8(self, x_bits: np.ndarray, group: int):
+        """(codes int8 [k] in logical order, scales float32 [k/G]) of fp16 x."""
+        x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+        k = x_bits.size
+        assert k % group == 0
+        codes = np.empty(k, np.int8)
+        scales = np.empty(k // group, np.float32)
+        self.lib.oracle_quantize_act8(_ptr(x_bits), k, group, _ptr(codes), _ptr(scales))
+        return codes, scales
+
+    def act8_block_order(self, codes: np.ndarray) -> np.ndarray:
+        """The codes in the W4T4 byte order of the GEMV's activation buffer."""
+        codes = np.ascontiguousarray(codes, dtype=np.int8)
+        assert codes.size % 8 == 0
+        out = np.empty_like(codes)
+        self.lib.oracle_act8_block_order(_ptr(codes), codes.size, _ptr(out))
+        return out
+
+    def gemv_a8(self, q: np.ndarray, s_bits: np.ndarray, codes: np.ndarray, act_scales: np.ndarray, group: int,
+                rows=None):
+        """W4A8 (y, A) float64 for all rows, or for the listed rows."""
+        q = np.ascontiguousarray(q, dtype=np.uint8)
+        s_bits = np.ascontiguousarray(s_bits, dtype=np.uint16)
+        codes = np.ascontiguousarray(codes, dtype=np.int8)
+        act_scales = np.ascontiguousarray(act_scales, dtype=np.float32)
+        n, k = q.shape
+        assert s_bits.shape == (n, k // group) and codes.shape == (k,) and act_scales.shape == (k // group,)
+        rows = np.arange(n, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+        y = np.empty(rows.size, np.float64)
+        a = np.empty(rows.size, np.float64)
+        self.lib.oracle_gemv_a8_rows(_ptr(q), _ptr(s_bits), _ptr(codes), _ptr(act_scales), n, k, group,
+                                     _ptr(rows), rows.size, _ptr(y), _ptr(a))
+        return y, a
+
+    def gemv_a8_packed(self, pw, ps, codes, act_scales, n: int, k: int, group: int, gateup: bool = False,
+                       rows=None):
+        """W4A8 (y, A) for the listed rows (default: all) from the packed buffers."""
+        pw = np.ascontiguousarray(pw, dtype=np.uint8)
+        ps = np.ascontiguousarray(ps, dtype=np.uint8)
+        codes = np.ascontiguousarray(codes, dtype=np.int8)
+        act_scales = np.ascontiguousarray(act_scales, dtype=np.float32)
+        wb, sb = self.packed_sizes(n, k, group, gateup)
+        assert pw.size >= wb and ps.size >= sb and codes.shape == (k,) and act_scales.shape == (k // group,)
+        rows = np.arange(n, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+        assert rows.size == 0 or (rows.min() >= 0 and rows.max() < n)
+        y = np.empty(rows.size, np.float64)
+        a = np.empty(rows.size, np.float64)
+        self.lib.oracle_gemv_a8_packed_rows(_ptr(pw), _ptr(ps), _ptr(codes), _ptr(act_scales), n, k, group,
+                                            int(gateup), _ptr(rows), rows.size, _ptr(y), _ptr(a))
+        return y, a
+
 
 def _ptr(a: np.ndarray) -> int:
     assert a.flags["C_CONTIGUOUS"]
@@ -315,3 +376,19 @@ def silu_gate(y):
 
 def argmax(y):
     return default().argmax(y)
+
+
+def quantize_act8(x_bits, group):
+    return default().quantize_act8(x_bits, group)
+
+
+def act8_block_order(codes):
+    return default().act8_block_order(codes)
+
+
+def gemv_a8(q, s_bits, codes, act_scales, group, rows=None):
+    return default().gemv_a8(q, s_bits, codes, act_scales, group, rows)
+
+
+def gemv_a8_packed(pw, ps, codes, act_scales, n, k, group, gateup=False, rows=None):
+    return default().gemv_a8_packed(pw, ps, codes, act_scales, n, k, group, gateup, rows)

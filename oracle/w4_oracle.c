@@ -389,3 +389,115 @@ int64_t oracle_argmax(const double* y, int64_t n)
     }
     return best;
 }
+
+/* ------------------------------------------------------------------ W4A8
+ * The INT8-activation variant the pages' runtime built and then removed
+ * ("Tutorial: como construir seu proprio runtime de LLM do zero",
+ * noticiai.com.br, "As tres licoes", lesson 3; "How To Build Your Own LLM
+ * Runtime From Scratch", aitrending.vip, "Technical Details", low-level
+ * pitfalls bullet).  The pages give no quantization rule; the reading is a
+ * symmetric int8 code per activation with one fp32 scale per group of G
+ * consecutive inputs (the weights' G), every step in binary32 with
+ * round-to-nearest-even:
+ *
+ *     amax_g  = max_{k in g} |x[k]|
+ *     inv_g   = 127 / amax_g            (binary32 division)
+ *     c[k]    = clamp(rint(x[k] * inv_g), -127, 127)   (binary32 product)
+ *     s_g     = amax_g / 127            (binary32 division)
+ *     (amax_g == 0: c = 0 and s_g = 0)
+ *
+ * and the product uses the dequantized activation x^[k] = c[k] * s_g:
+ *
+ *     y[n] = sum_k (q[n][k] - 8) * s[n][g] * c[k] * s_g
+ *
+ * Each term is exact in double ((q - 8) c has at most 10 bits, s 11, s_g
+ * 24), so y is the exact sum up to the rounding of a plain fp64 sum. */
+
+/* codes (logical order) and per-group scales of an fp16 vector x[k] */
+void oracle_quantize_act8(const uint16_t* x, int64_t k, int32_t group, int8_t* codes, float* scales)
+{
+    for (int64_t g = 0; g < k / group; ++g) {
+        float amax = 0.0f;
+        for (int64_t kk = g * group; kk < (g + 1) * group; ++kk) {
+            float v = (float)fabs(oracle_half_to_double(x[kk]));
+            if (v > amax) amax = v;
+        }
+        if (amax == 0.0f) {
+            for (int64_t kk = g * group; kk < (g + 1) * group; ++kk) codes[kk] = 0;
+            scales[g] = 0.0f;
+            continue;
+        }
+        volatile float inv = 127.0f / amax;
+        for (int64_t kk = g * group; kk < (g + 1) * group; ++kk) {
+            volatile float prod = (float)oracle_half_to_double(x[kk]) * inv;
+            float r = rintf(prod);
+            if (r > 127.0f) r = 127.0f;
+            if (r < -127.0f) r = -127.0f;
+            codes[kk] = (int8_t)r;
+        }
+        volatile float sg = amax / 127.0f;
+        scales[g] = sg;
+    }
+}
+
+/* The W4T4 byte order of the codes: for each block of 8 inputs 8j..8j+7, the
+ * bytes at 8j..8j+7 hold inputs 8j + (0, 4, 1, 5, 2, 6, 3, 7), which is the
+ * order of the nibbles of a packed word taken as the bytes of
+ * (word & 0x0F0F0F0F) followed by the bytes of ((word >> 4) & 0x0F0F0F0F). */
+void oracle_act8_block_order(const int8_t* codes, int64_t k, int8_t* out)
+{
+    static const int order[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+    for (int64_t j = 0; j < k / 8; ++j)
+        for (int b = 0; b < 8; ++b) out[8 * j + b] = codes[8 * j + order[b]];
+}
+
+/* W4A8 dot products for the listed rows (rows == NULL: all), logical inputs,
+ * codes in logical order. */
+void oracle_gemv_a8_rows(const uint8_t* q, const uint16_t* s, const int8_t* codes, const float* act_scales,
+                         int64_t n, int64_t k, int32_t group, const int64_t* rows, int64_t nrows, double* y,
+                         double* a)
+{
+    int64_t ngroups = k / group;
+    (void)n;
+    for (int64_t i = 0; i < nrows; ++i) {
+        int64_t row = rows ? rows[i] : i;
+        double acc = 0.0, mag = 0.0;
+        for (int64_t kk = 0; kk < k; ++kk) {
+            double w = ((double)q[row * k + kk] - 8.0) * oracle_half_to_double(s[row * ngroups + kk / group]);
+            double p = w * ((double)codes[kk] * (double)act_scales[kk / group]);
+            acc += p;
+            mag += fabs(p);
+        }
+        y[i] = acc;
+        a[i] = mag;
+    }
+}
+
+/* The same from the packed weight buffers (W4T4 layout rules above). */
+void oracle_gemv_a8_packed_rows(const uint8_t* pw, const uint8_t* ps, const int8_t* codes,
+                                const float* act_scales, int64_t n, int64_t k, int32_t group, int32_t gateup,
+                                const int64_t* rows, int64_t nrows, double* y, double* a)
+{
+    int64_t nblocks = k / 8;
+    int64_t ngroups = k / group;
+    for (int64_t i = 0; i < nrows; ++i) {
+        int64_t row = rows ? rows[i] : i;
+        int64_t t;
+        int r;
+        place_row(row, n, gateup, &t, &r);
+        double acc = 0.0, mag = 0.0;
+        for (int64_t kk = 0; kk < k; ++kk) {
+            const uint8_t* src = pw + (t * nblocks + kk / 8) * 16 + 4 * r;
+            uint32_t word = (uint32_t)src[0] | ((uint32_t)src[1] << 8) |
+                            ((uint32_t)src[2] << 16) | ((uint32_t)src[3] << 24);
+            int qv = (int)((word >> (4 * slot_of_offset((int)(kk % 8)))) & 0xfu);
+            const uint8_t* sp = ps + (t * ngroups + kk / group) * 8 + 2 * r;
+            double sv = oracle_half_to_double((uint16_t)(sp[0] | (sp[1] << 8)));
+            double p = ((double)qv - 8.0) * sv * ((double)codes[kk] * (double)act_scales[kk / group]);
+            acc += p;
+            mag += fabs(p);
+        }
+        y[i] = acc;
+        a[i] = mag;
+    }
+}

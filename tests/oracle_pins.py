@@ -456,4 +456,109 @@ def pin_rope(orc):
     assert abs(d1 - d2) < 1e-9
 
 
+def pin_act8_hand_examples(orc):
+    """Codes worked by hand.  Group 0 has amax 1, so inv = 127 exactly and
+    c = rint(127 x): 0.5 -> 63.5 -> 64 (tie to even), -0.25 -> -31.75 -> -32,
+    0.125 -> 15.875 -> 16, 0.75 -> 95.25 -> 95, fp16(0.3) = 0.2998046875 ->
+    38.075 -> 38.  Group 1 has amax 2, inv = 63.5: 1 -> 63.5 -> 64,
+    -0.5 -> -31.75 -> -32, 1.5 -> 95.25 -> 95, 0.25 -> 15.875 -> 16."""
+    x = _h([1.0, 0.5, -0.25, 0.0, 0.125, -1.0, 0.75, 0.3, 2.0, 1.0, -0.5, 0.0, 1.5, -2.0, 0.25, 0.0])
+    c, sc = orc.quantize_act8(x, 8)
+    assert c.tolist() == [127, 64, -32, 0, 16, -127, 95, 38, 127, 64, -32, 0, 95, -127, 16, 0]
+    assert sc[0] == np.float32(1.0) / np.float32(127.0) and sc[1] == np.float32(2.0) / np.float32(127.0)
+    c0, s0 = orc.quantize_act8(np.zeros(16, np.uint16), 8)
+    assert not c0.any() and not s0.any()
+
+
+def pin_act8_properties(orc):
+    """Bounded codes; each group's largest |x| maps to +-127; the
+    dequantization error is at most half a step; sign symmetry; doubling x
+    doubles the scales and keeps the codes (every step is exact under a
+    power-of-two scaling)."""
+    rng = np.random.default_rng(61)
+    k, g = 512, 64
+    xf = rng.standard_normal(k) * 2.0
+    x = _h(xf)
+    xv = x.view(np.float16).astype(np.float64)
+    c, sc = orc.quantize_act8(x, g)
+    assert np.abs(c.astype(int)).max() <= 127
+    for j in range(k // g):
+        seg = slice(j * g, (j + 1) * g)
+        i = int(np.argmax(np.abs(xv[seg])))
+        assert abs(int(c[seg][i])) == 127
+        err = np.abs(xv[seg] - c[seg].astype(np.float64) * float(sc[j]))
+        assert np.all(err <= 0.5 * float(sc[j]) * (1 + 1e-6))
+    cn, sn = orc.quantize_act8(_h(-xv), g)
+    assert np.array_equal(cn, -c) and np.array_equal(sn, sc)
+    c2, s2 = orc.quantize_act8(_h(2.0 * xv), g)
+    assert np.array_equal(c2, c) and np.array_equal(s2, 2.0 * sc)
+
+
+def pin_act8_block_order(orc):
+    """The byte order of the codes is the packed nibble order: for a row whose
+    8 weights are q = 0..7, the bytes of (word & 0x0F0F0F0F) and of
+    ((word >> 4) & 0x0F0F0F0F) list the inputs in the order the codes use."""
+    q = np.zeros((4, 8), np.uint8)
+    q[0] = np.arange(8)
+    s = np.full((4, 1), 0x3C00, np.uint16)
+    pw, _ = orc.pack(q, s, 8)
+    word = int.from_bytes(bytes(pw[:4]), "little")
+    order = [(word >> (8 * b)) & 0xF for b in range(4)] + [(word >> (8 * b + 4)) & 0xF for b in range(4)]
+    assert order == [0, 4, 1, 5, 2, 6, 3, 7]
+    assert orc.act8_block_order(np.arange(16, dtype=np.int8)).tolist() == order + [8 + v for v in order]
+
+
+def pin_gemv_a8_vs_numpy(orc):
+    rng = np.random.default_rng(67)
+    n, k, g = 37, 256, 64
+    q = rng.integers(0, 16, (n, k), dtype=np.uint8)
+    s = _h(rng.uniform(0.001, 0.02, (n, k // g)))
+    c, sc = orc.quantize_act8(_h(rng.standard_normal(k)), g)
+    xhat = c.astype(np.float64) * np.repeat(sc.astype(np.float64), g)
+    w = _dequant_numpy(q, s, g)
+    y, a = orc.gemv_a8(q, s, c, sc, g)
+    assert np.allclose(y, w @ xhat, rtol=1e-12, atol=1e-15)
+    assert np.allclose(a, np.abs(w * xhat).sum(axis=1), rtol=1e-12, atol=1e-15)
+    rows = np.array([36, 0, 5], np.int64)
+    y2, _ = orc.gemv_a8(q, s, c, sc, g, rows=rows)
+    assert np.array_equal(y2, y[rows])
+
+
+def pin_gemv_a8_closed_forms(orc):
+    """q = 8 gives 0; unit weights (q = 9, s = 1) give sum_k c[k] s_g exactly;
+    a one-hot activation v e_k gives (q - 8) s (+-127 * fl(|v| / 127))."""
+    rng = np.random.default_rng(71)
+    n, k, g = 8, 128, 32
+    c, sc = orc.quantize_act8(_h(rng.standard_normal(k)), g)
+    ones = np.full((n, k // g), 0x3C00, np.uint16)
+    y0, _ = orc.gemv_a8(np.full((n, k), 8, np.uint8), ones, c, sc, g)
+    assert np.array_equal(y0, np.zeros(n))
+    y1, _ = orc.gemv_a8(np.full((n, k), 9, np.uint8), ones, c, sc, g)
+    exact = sum(int(c[i]) * float(sc[i // g]) for i in range(k))
+    assert np.all(y1 == exact)
+    x = np.zeros(k, np.uint16)
+    x[77] = _h([-0.375])[0]
+    c1, s1 = orc.quantize_act8(x, g)
+    assert c1[77] == -127 and s1[77 // g] == np.float32(0.375) / np.float32(127.0)
+    q = rng.integers(0, 16, (n, k), dtype=np.uint8)
+    s = _h(rng.uniform(0.001, 0.02, (n, k // g)))
+    y, _ = orc.gemv_a8(q, s, c1, s1, g)
+    ref = (q[:, 77].astype(np.float64) - 8) * s[:, 77 // g].view(np.float16).astype(np.float64) * (
+        -127.0 * float(s1[77 // g]))
+    assert np.array_equal(y, ref)
+
+
+def pin_gemv_a8_packed_matches_logical(orc):
+    rng = np.random.default_rng(73)
+    k, g = 192, 64
+    c, sc = orc.quantize_act8(_h(rng.standard_normal(k)), g)
+    for n, gateup in ((13, False), (10, True)):
+        q = rng.integers(0, 16, (n, k), dtype=np.uint8)
+        s = _h(rng.uniform(0.001, 0.02, (n, k // g)))
+        pw, ps = orc.pack(q, s, g, gateup)
+        y1, a1 = orc.gemv_a8(q, s, c, sc, g)
+        y2, a2 = orc.gemv_a8_packed(pw, ps, c, sc, n, k, g, gateup)
+        assert np.array_equal(y1, y2) and np.array_equal(a1, a2)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

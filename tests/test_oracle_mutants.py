@@ -53,6 +53,15 @@ MUTANTS = [
     ("rmsnorm_gamma_dropped", "out[i] = h[i] * r * oracle_half_to_double(gamma[i]);", "out[i] = h[i] * r;", None),
     ("rope_sign", "out[i] = x[i] * c - x[i + half] * sn;", "out[i] = x[i] * c + x[i + half] * sn;", None),
     ("rope_freq", "pow(theta, -2.0 * (double)i / (double)dim)", "pow(theta, -(double)i / (double)dim)", None),
+    ("act8_truncate", "float r = rintf(prod);", "float r = truncf(prod);", None),
+    ("act8_fixed_inverse", "(float)oracle_half_to_double(x[kk]) * inv;", "(float)oracle_half_to_double(x[kk]) * 127.0f;", None),
+    ("act8_signed_max", "float v = (float)fabs(oracle_half_to_double(x[kk]));", "float v = (float)oracle_half_to_double(x[kk]);", None),
+    ("act8_scale_inverted", "volatile float sg = amax / 127.0f;", "volatile float sg = 127.0f / amax;", None),
+    ("act8_block_order_identity", "{0, 4, 1, 5, 2, 6, 3, 7}", "{0, 1, 2, 3, 4, 5, 6, 7}", None),
+    ("a8_act_scale_dropped", "double p = w * ((double)codes[kk] * (double)act_scales[kk / group]);",
+     "double p = w * (double)codes[kk];", None),
+    ("a8_packed_act_group", "((double)codes[kk] * (double)act_scales[kk / group]);\n            acc",
+     "((double)codes[kk] * (double)act_scales[0]);\n            acc", None),
     ("gemm_packed_x_row_fixed", "oracle_gemv_packed_rows(pw, ps, xm + m * k,", "oracle_gemv_packed_rows(pw, ps, xm,", None),
 ]
 
