@@ -26,6 +26,13 @@ final norm, lm_head + greedy argmax, position advance) as one captured HIP
 graph per token, for tokens 512..512+steps-1 after a 512-token prompt (the
 pages' pp512/tg128 protocol), and the same step as eager launches.
 
+    python bench.py --workload w4a8
+
+times the W4A8 variant of the linear sweep (int8 activations, integer
+dot products): each projection's fp16 x is quantized per group of 128 and the
+GEMV reads the codes; reported next to the W4A16 sweep of the same weights,
+with and without the quantization launches.
+
     python bench.py --workload prefill [--steps 10] [--warmup 2]
 
 times the prefill counterpart instead: the 28 layers' four INT4 products for
@@ -55,6 +62,7 @@ MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 matrix-core peak
 METRIC = "achieved HBM GB/s (% of peak) and ms per 28-layer+lm_head INT4 linear sweep"
 PREFILL_METRIC = "prefill TFLOP/s (% of fp16 MFMA peak) and ms per 28-layer 512-token INT4 linear sweep"
 ATTN_METRIC = "decode attention GB/s (% of HBM peak) and ms per 28-layer paged-KV attention at 4096-token context"
+W4A8_METRIC = "W4A8 achieved HBM GB/s (% of peak) and ms per 28-layer+lm_head INT4 linear sweep with int8 activations"
 STEP_METRIC = "batch-1 decode tokens/s and ms per full 28-layer decode step (hipGraph), tokens 512..639"
 ATTN_HEADS, ATTN_KV_HEADS, ATTN_PAGE, ATTN_CTX = 28, 4, 16, 4096
 KERNEL_SRC = os.path.join(ROOT, "int4_weight_only_04_amd", "csrc", "w4_kernels.hip")
@@ -764,6 +772,157 @@ def run_step(args) -> int:
     return 0
 
 
+def a8_bytes(kind: str, n: int, k: int, group: int) -> int:
+    """Bytes of one W4A8 GEMV: the W4A16 GEMV's with int8 codes (k bytes) and
+    fp32 group scales in place of the fp16 x."""
+    return algorithmic_bytes(kind, n, k, group) - 2 * k + k + 4 * (k // group)
+
+
+def quant_bytes(k: int, group: int) -> int:
+    """Bytes of one activation quantization: fp16 x in, codes and scales out."""
+    return 2 * k + k + 4 * (k // group)
+
+
+def w4a8_cpu_baseline():
+    """The oracle's W4A8 product (single thread, fp64) on layer 0's four
+    projections, all rows, plus the oracle's quantization of their inputs."""
+    import oracle
+    from int4_weight_only_04_amd import w4
+    total, t_total = 0, 0.0
+    for p in synthetic.sweep_projections(1):
+        layout = "gateup" if p.kind == "gateup" else "plain"
+        wb, sb = w4.packed_size(p.n, p.k, p.group, layout)
+        pw, ps, x = synthetic.packed_random(p.seed, wb, sb // 2, p.k)
+        t0 = time.perf_counter()
+        c, sc = oracle.quantize_act8(x, p.group)
+        y, _ = oracle.gemv_a8_packed(pw, ps, c, sc, p.n, p.k, p.group, gateup=(layout == "gateup"))
+        if p.kind == "gateup":
+            oracle.silu_gate(y)
+        t_total += time.perf_counter() - t0
+        total += a8_bytes(p.kind, p.n, p.k, p.group) + quant_bytes(p.k, p.group)
+    return {
+        "value": total / t_total / 1e9,
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"layer 0 of the W4A8 sweep (quantize + qkv, o_proj, gate/up+silu, down), all rows, {total} "
+                  f"algorithmic bytes in {t_total:.1f} s, single-threaded fp64 C",
+        "seconds": t_total,
+    }
+
+
+def run_w4a8(args) -> int:
+    """The linear sweep with int8 activations, next to the W4A16 sweep."""
+    import torch
+    from int4_weight_only_04_amd import w4
+    print(f"[bench] building sweep ({args.layers} layers)", file=sys.stderr, flush=True)
+    specs, projs = build_sweep(args.layers)
+    stream = torch.cuda.Stream()
+    bufs = []
+    for p, pr in zip(specs, projs):
+        codes = torch.empty(p.k, dtype=torch.int8, device="cuda")
+        scales = torch.empty(p.k // p.group, dtype=torch.float32, device="cuda")
+        bufs.append((p, pr, codes, scales))
+
+    def launch(s, quant: bool, only=None):
+        for p, pr, codes, scales in bufs:
+            if only is not None and p.kind != only:
+                continue
+            if quant:
+                w4.quantize_act8(pr.x, p.group, codes, scales, stream=s)
+            if p.kind == "gateup":
+                w4.gemv_gateup_silu_a8(pr.packed_w, pr.packed_s, codes, scales, pr.out, p.n, p.k, p.group, stream=s)
+            elif p.kind == "lmhead":
+                w4.gemv_a8(pr.packed_w, pr.packed_s, codes, scales, pr.out, p.n, p.k, p.group, argmax=pr.argmax,
+                           workspace=pr.workspace, stream=s)
+            else:
+                w4.gemv_a8(pr.packed_w, pr.packed_s, codes, scales, pr.out, p.n, p.k, p.group, stream=s)
+
+    with torch.cuda.stream(stream):
+        launch(stream, True)   # fill the codes once for the GEMV-only graph
+    stream.synchronize()
+    print("[bench] W4A8 sweep with quantization (graph)", file=sys.stderr, flush=True)
+    g_q = capture(lambda s: launch(s, True), stream)
+    ms_q = replay_ms(g_q, stream, args.steps, args.warmup)
+    print("[bench] W4A8 sweep, GEMVs only (graph)", file=sys.stderr, flush=True)
+    g_g = capture(lambda s: launch(s, False), stream)
+    ms_g = replay_ms(g_g, stream, args.steps, args.warmup)
+    print("[bench] W4A16 sweep (graph)", file=sys.stderr, flush=True)
+    sweep16 = w4.Sweep(projs, use_graph=True)
+    ms16, _ = time_graph(sweep16, stream, args.steps, args.warmup)
+    sweep16.close()
+
+    print("[bench] dominant kernel (W4A8 gate/up)", file=sys.stderr, flush=True)
+    g_gu = capture(lambda s: launch(s, False, only="gateup"), stream)
+    with torch.cuda.stream(stream):
+        g_gu.replay()
+    stream.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    replays = 4
+    with torch.cuda.stream(stream):
+        a.record(stream)
+        for _ in range(replays):
+            g_gu.replay()
+        b.record(stream)
+    stream.synchronize()
+    n_gu = sum(1 for p in specs if p.kind == "gateup")
+    gu_ms = a.elapsed_time(b) / (replays * n_gu)
+    gp = next(p for p in specs if p.kind == "gateup")
+    gu_bytes = a8_bytes("gateup", gp.n, gp.k, gp.group)
+    gu_gbs = gu_bytes / (gu_ms * 1e-3) / 1e9
+
+    bytes_q = sum(a8_bytes(p.kind, p.n, p.k, p.group) + quant_bytes(p.k, p.group) for p in specs)
+    bytes_g = sum(a8_bytes(p.kind, p.n, p.k, p.group) for p in specs)
+    value = bytes_q / (ms_q * 1e-3) / 1e9
+    out = {
+        "metric": W4A8_METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_q, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8xi4->i32, f32",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"batch-1 decode-step INT4 linear sweep with int8 activations, hipGraph: {args.layers} x "
+                         "(quantize x + qkv 3584->4608, o_proj, gate/up 3584->2x18944 + silu, down 18944->3584) + "
+                         "lm_head 3584->152064 + argmax; activations per group of 128 (symmetric int8, fp32 scale), "
+                         "integer 8-input block sums, fp32 accumulation"),
+            "algorithmic_bytes_per_step": bytes_q,
+            "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+            "gemv_only_ms_per_step": round(ms_g, 4),
+            "gemv_only_gbs": round(bytes_g / (ms_g * 1e-3) / 1e9, 1),
+            "w4a16_ms_per_step": round(ms16, 4),
+            "w4a16_gbs": round(sweep_bytes(specs) / (ms16 * 1e-3) / 1e9, 1),
+            "w4a8_vs_w4a16_time_ratio": round(ms_q / ms16, 3),
+            "w4a8_gemv_only_vs_w4a16_time_ratio": round(ms_g / ms16, 3),
+        },
+        "roofline": {
+            "kernel": "gemv_w4_kernel<2, gate/up+silu, A8> 37888x3584 g128",
+            "bound": "hbm",
+            "achieved": round(gu_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": gu_bytes,
+            "avg_launch_us": round(gu_ms * 1e3, 3),
+            "launches_timed": replays * n_gu,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle W4A8)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = w4a8_cpu_baseline()
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -773,10 +932,11 @@ def main(argv=None):
     ap.add_argument("--layers", type=int, default=synthetic.LAYERS)
     ap.add_argument("--eager-steps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", choices=("decode", "prefill", "attention", "step"), default="decode",
+    ap.add_argument("--workload", choices=("decode", "prefill", "attention", "step", "w4a8"), default="decode",
                     help="decode: the per-token GEMV sweep (default); prefill: the 512-token GEMM sweep; "
                          "attention: 28 layers' paged-KV decode attention at a 4096-token context; "
-                         "step: the full decode step (tokens 512.. after a 512-token prompt)")
+                         "step: the full decode step (tokens 512.. after a 512-token prompt); "
+                         "w4a8: the sweep with int8 activations")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args(argv)
@@ -811,6 +971,8 @@ def main(argv=None):
         return run_attention(args)
     if args.workload == "step":
         return run_step(args)
+    if args.workload == "w4a8":
+        return run_w4a8(args)
 
     print(f"[bench] building sweep ({args.layers} layers)", file=sys.stderr, flush=True)
     specs, projs = build_sweep(args.layers)

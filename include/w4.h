@@ -184,6 +184,44 @@ w4_status w4_gemm_gateup_silu(const void* packed_w, const void* packed_s, const 
                               void* stream);
 
 /*
+ * W4A8: the INT8-activation variant of the GEMV, the path the pages' runtime
+ * implemented, tested and removed ("Tutorial: como construir seu proprio
+ * runtime de LLM do zero", noticiai.com.br, "As tres licoes", lesson 3;
+ * "How To Build Your Own LLM Runtime From Scratch", aitrending.vip,
+ * "Technical Details", low-level pitfalls bullet).  The pages give no
+ * quantization rule; this library quantizes x per group of G inputs (the
+ * weights' G), symmetric, in binary32 with round-to-nearest-even:
+ *     amax = max |x| over the group, inv = 127 / amax,
+ *     c[k] = clamp(rint(x[k] * inv), -127, 127),  s_g = amax / 127
+ *     (amax == 0: c = 0, s_g = 0)
+ * and computes y[n] = sum_k (q[n][k] - 8) * s[n][g] * c[k] * s_g, each
+ * 8-input block's integer sum exact (v_dot4_i32_i8), fp32 accumulation.
+ *
+ * w4_quantize_act8: codes and scales of one fp16 vector.  Device, async.
+ *   x       device fp16 [k], 16-byte aligned;
+ *   codes   device int8 [k], 8-byte aligned, in W4T4 block order: the bytes
+ *           8j..8j+7 hold inputs 8j + (0, 4, 1, 5, 2, 6, 3, 7) (the order
+ *           of the nibbles in (word & 0x0F0F0F0F) then ((word >> 4) &
+ *           0x0F0F0F0F) of a packed weight word);
+ *   scales  device fp32 [k / group].
+ * Shape rules as for w4_gemv (k, group).
+ */
+w4_status w4_quantize_act8(const uint16_t* x, int64_t k, int32_t group, int8_t* codes, float* scales,
+                           void* stream);
+
+/* w4_gemv with int8 activation codes and per-group scales from
+ * w4_quantize_act8 (same group) in place of fp16 x; the same outputs,
+ * argmax option, workspace and rules (codes 16-byte aligned). */
+w4_status w4_gemv_a8(const void* packed_w, const void* packed_s, const int8_t* codes, const float* act_scales,
+                     float* y, int32_t* argmax, void* workspace, size_t workspace_bytes, int64_t n, int64_t k,
+                     int32_t group, void* stream);
+
+/* w4_gemv_gateup_silu with int8 activation codes (see w4_gemv_a8). */
+w4_status w4_gemv_gateup_silu_a8(const void* packed_w, const void* packed_s, const int8_t* codes,
+                                 const float* act_scales, uint16_t* h, int64_t n_total, int64_t k, int32_t group,
+                                 void* stream);
+
+/*
  * Workspace bytes w4_attn_decode needs: (130 x 4) bytes per query head per
  * 64-token chunk of max_ctx (about 0.9 MB for 28 heads at 4096).  Host only.
  */

@@ -264,6 +264,64 @@ w4_status w4_gemv_gateup_silu(const void* packed_w, const void* packed_s, const 
     }
 }
 
+w4_status w4_quantize_act8(const uint16_t* x, int64_t k, int32_t group, int8_t* codes, float* scales, void* stream)
+{
+    try {
+        const char* who = "w4_quantize_act8";
+        if (!x || !codes || !scales) return fail(W4_EINVAL, "%s: null pointer", who);
+        w4_status st = check_shape(1, k, group, false, who);
+        if (st != W4_OK) return st;
+        if (!aligned16(x) || !aligned_to(codes, 8) || !aligned_to(scales, 4))
+            return fail(W4_EALIGN, "%s: x must be 16-byte, codes 8-byte, scales 4-byte aligned", who);
+        hipError_t err = launch_act8_quantize(x, k, group, codes, scales, static_cast<hipStream_t>(stream));
+        if (err != hipSuccess) return hip_fail(err, "w4_quantize_act8 launch");
+        return ok();
+    } catch (...) {
+        return fail(W4_EINVAL, "w4_quantize_act8: internal exception");
+    }
+}
+
+w4_status w4_gemv_a8(const void* packed_w, const void* packed_s, const int8_t* codes, const float* act_scales,
+                     float* y, int32_t* argmax, void* workspace, size_t workspace_bytes, int64_t n, int64_t k,
+                     int32_t group, void* stream)
+{
+    try {
+        GemvCall c{packed_w, packed_s, codes, y, argmax, workspace, n, k, group, argmax ? kEpiArgmax : kEpiPlain,
+                   act_scales};
+        w4_status st = validate_gemv(c, "w4_gemv_a8");
+        if (st != W4_OK) return st;
+        if (!act_scales) return fail(W4_EINVAL, "w4_gemv_a8: null act_scales");
+        if (!aligned_to(act_scales, 4)) return fail(W4_EALIGN, "w4_gemv_a8: act_scales must be 4-byte aligned");
+        if (argmax && workspace_bytes < argmax_workspace_bytes(launch_grid(c)))
+            return fail(W4_EINVAL, "w4_gemv_a8: workspace of %zu bytes, need %zu", workspace_bytes,
+                        argmax_workspace_bytes(launch_grid(c)));
+        hipError_t err = launch_gemv(c, static_cast<hipStream_t>(stream));
+        if (err != hipSuccess) return hip_fail(err, "w4_gemv_a8 launch");
+        return ok();
+    } catch (...) {
+        return fail(W4_EINVAL, "w4_gemv_a8: internal exception");
+    }
+}
+
+w4_status w4_gemv_gateup_silu_a8(const void* packed_w, const void* packed_s, const int8_t* codes,
+                                 const float* act_scales, uint16_t* h, int64_t n_total, int64_t k, int32_t group,
+                                 void* stream)
+{
+    try {
+        GemvCall c{packed_w, packed_s, codes, h, nullptr, nullptr, n_total, k, group, kEpiGateUp, act_scales};
+        w4_status st = validate_gemv(c, "w4_gemv_gateup_silu_a8");
+        if (st != W4_OK) return st;
+        if (!act_scales) return fail(W4_EINVAL, "w4_gemv_gateup_silu_a8: null act_scales");
+        if (!aligned_to(act_scales, 4))
+            return fail(W4_EALIGN, "w4_gemv_gateup_silu_a8: act_scales must be 4-byte aligned");
+        hipError_t err = launch_gemv(c, static_cast<hipStream_t>(stream));
+        if (err != hipSuccess) return hip_fail(err, "w4_gemv_gateup_silu_a8 launch");
+        return ok();
+    } catch (...) {
+        return fail(W4_EINVAL, "w4_gemv_gateup_silu_a8: internal exception");
+    }
+}
+
 w4_status w4_gemm_workspace_size(int64_t m, int64_t n, int64_t k, int32_t group, size_t* bytes)
 {
     try {

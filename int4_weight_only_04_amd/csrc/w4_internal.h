@@ -30,7 +30,13 @@ struct GemvCall {
     int64_t k;
     int32_t group;
     int32_t epi;
+    const float* xs;     // W4A8: x holds int8 codes (W4T4 block order), xs the per-group scales; null: fp16 x
 };
+
+// Per-group int8 quantization of fp16 x for the W4A8 GEMV (codes in W4T4
+// block order, one fp32 scale per group).
+hipError_t launch_act8_quantize(const uint16_t* x, int64_t k, int32_t group, int8_t* codes, float* scales,
+                                hipStream_t stream);
 
 // Prefill GEMM: y[m][n] = sum_k x[m][k] * w[n][k] for a block of token rows
 // (x fp16 [m][k] row-major; y fp32 [m][n], or h fp16 [m][n/2] for gate/up).

@@ -55,7 +55,8 @@ typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 struct KernelArgs {
     const uint4* pw;
     const uint2* ps;
-    const uint4* x;
+    const uint4* x;      // fp16 x, or (W4A8) int8 codes as uint2 per 8-input block
+    const float* xs;     // W4A8: activation scale per group
     void* out;
     float* part_v;       // argmax: per-workgroup best value
     int32_t* part_i;     // argmax: per-workgroup best row
@@ -111,6 +112,25 @@ __device__ __forceinline__ float dot8(uint32_t d, const uint4& xv, uint32_t magi
     p = __builtin_amdgcn_fdot2(vc, as_h2(xv.z), p, false);
     p = __builtin_amdgcn_fdot2(ve, as_h2(xv.w), p, false);
     return p;
+}
+
+// W4A8: sum over the 8 inputs of one block of (q - 8) * c as an exact
+// integer.  The nibbles of (d & 0x0F0F0F0F) and ((d >> 4) & 0x0F0F0F0F) are
+// bytes 0..15 (non-negative as int8), in the byte order the activation codes
+// are stored in, so two v_dot4_i32_i8 give sum q c; neg8cs = -8 sum c of the
+// block (shared by every row) removes the zero point.
+__device__ __forceinline__ int idot8(uint32_t d, const uint2& c, int neg8cs)
+{
+    const int lo = (int)(d & 0x0F0F0F0Fu);
+    const int hi = (int)((d >> 4) & 0x0F0F0F0Fu);
+    const int t = __builtin_amdgcn_sdot4(lo, (int)c.x, neg8cs, false);
+    return __builtin_amdgcn_sdot4(hi, (int)c.y, t, false);
+}
+
+__device__ __forceinline__ int neg8_code_sum(const uint2& c)
+{
+    const int t = __builtin_amdgcn_sdot4((int)c.x, 0x01010101, 0, false);
+    return -8 * __builtin_amdgcn_sdot4((int)c.y, 0x01010101, t, false);
 }
 
 __device__ __forceinline__ float half_lo(uint32_t v) { return (float)as_h2(v)[0]; }
@@ -183,15 +203,17 @@ __device__ __forceinline__ bool better(float v, int32_t i, float bv, int32_t bi)
 // wait counters are exact, so iteration d waits only for its own three
 // loads and its math overlaps the loads still in flight (with branches it
 // falls back to waiting for every load before any math).
-template <int C, int U>
+template <int C, int U, bool A8>
 __device__ __forceinline__ void accumulate_exact(float (&acc)[U][4], const uint4* const (&wp)[U],
                                                  const uint2* const (&sp)[U], const bool (&tile_ok)[U],
-                                                 const uint4* __restrict__ x, int i0, int lane, int gshift,
-                                                 uint32_t magic)
+                                                 const uint4* __restrict__ x, const float* __restrict__ xs, int i0,
+                                                 int lane, int gshift, uint32_t magic)
 {
     uint4 w[C][U];
     uint2 s[C][U];
     uint4 xr[C];
+    uint2 cr[C];
+    float sx[C];
 #pragma unroll
     for (int d = 0; d < C; ++d) {
         const int j = (i0 + d) * 64 + lane;
@@ -200,10 +222,17 @@ __device__ __forceinline__ void accumulate_exact(float (&acc)[U][4], const uint4
             w[d][u] = ld_stream(wp[u] + j);
             s[d][u] = ld_stream(sp[u] + (j >> gshift));
         }
-        xr[d] = x[j];
+        if constexpr (A8) {
+            cr[d] = reinterpret_cast<const uint2*>(x)[j];
+            sx[d] = xs[j >> gshift];
+        } else {
+            xr[d] = x[j];
+        }
     }
 #pragma unroll
     for (int d = 0; d < C; ++d) {
+        int n8 = 0;
+        if constexpr (A8) n8 = neg8_code_sum(cr[d]);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             // a unit's missing second tile reads tile 0 (in bounds) with its
@@ -211,10 +240,17 @@ __device__ __forceinline__ void accumulate_exact(float (&acc)[U][4], const uint4
             // stays unconditional and in issue order)
             const uint32_t keep = 0u - (uint32_t)tile_ok[u];
             const uint2 sc = make_uint2(s[d][u].x & keep, s[d][u].y & keep);
-            acc[u][0] = __builtin_fmaf(dot8(w[d][u].x, xr[d], magic), half_lo(sc.x), acc[u][0]);
-            acc[u][1] = __builtin_fmaf(dot8(w[d][u].y, xr[d], magic), half_hi(sc.x), acc[u][1]);
-            acc[u][2] = __builtin_fmaf(dot8(w[d][u].z, xr[d], magic), half_lo(sc.y), acc[u][2]);
-            acc[u][3] = __builtin_fmaf(dot8(w[d][u].w, xr[d], magic), half_hi(sc.y), acc[u][3]);
+            if constexpr (A8) {
+                acc[u][0] = __builtin_fmaf((float)idot8(w[d][u].x, cr[d], n8), half_lo(sc.x) * sx[d], acc[u][0]);
+                acc[u][1] = __builtin_fmaf((float)idot8(w[d][u].y, cr[d], n8), half_hi(sc.x) * sx[d], acc[u][1]);
+                acc[u][2] = __builtin_fmaf((float)idot8(w[d][u].z, cr[d], n8), half_lo(sc.y) * sx[d], acc[u][2]);
+                acc[u][3] = __builtin_fmaf((float)idot8(w[d][u].w, cr[d], n8), half_hi(sc.y) * sx[d], acc[u][3]);
+            } else {
+                acc[u][0] = __builtin_fmaf(dot8(w[d][u].x, xr[d], magic), half_lo(sc.x), acc[u][0]);
+                acc[u][1] = __builtin_fmaf(dot8(w[d][u].y, xr[d], magic), half_hi(sc.x), acc[u][1]);
+                acc[u][2] = __builtin_fmaf(dot8(w[d][u].z, xr[d], magic), half_lo(sc.y), acc[u][2]);
+                acc[u][3] = __builtin_fmaf(dot8(w[d][u].w, xr[d], magic), half_hi(sc.y), acc[u][3]);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -223,8 +259,9 @@ __device__ __forceinline__ void accumulate_exact(float (&acc)[U][4], const uint4
 constexpr int waves_for(int split) { return split < 4 ? 4 : split; }
 
 // U tiles per unit, epilogue EPI, SPLIT waves per unit, D iterations per load
-// round, FULL: k/8 is a multiple of 64 (no lane masking).
-template <int U, int EPI, int SPLIT, int D, bool FULL>
+// round, FULL: k/8 is a multiple of 64 (no lane masking), A8: int8
+// activation codes with per-group scales instead of fp16 x.
+template <int U, int EPI, int SPLIT, int D, bool FULL, bool A8>
 __global__ void __launch_bounds__(waves_for(SPLIT) * 64) gemv_w4_kernel(KernelArgs a)
 {
     constexpr int WAVES = waves_for(SPLIT);
@@ -272,9 +309,9 @@ __global__ void __launch_bounds__(waves_for(SPLIT) * 64) gemv_w4_kernel(KernelAr
             sp[u] = a.ps + t * a.ng;
         }
         if (count == D)
-            accumulate_exact<D, U>(acc, wp, sp, tile_ok, a.x, it0, lane, a.gshift, magic);
+            accumulate_exact<D, U, A8>(acc, wp, sp, tile_ok, a.x, a.xs, it0, lane, a.gshift, magic);
         else if constexpr (D > 1)
-            accumulate_exact<D - 1, U>(acc, wp, sp, tile_ok, a.x, it0, lane, a.gshift, magic);
+            accumulate_exact<D - 1, U, A8>(acc, wp, sp, tile_ok, a.x, a.xs, it0, lane, a.gshift, magic);
     } else if (live) {
         const uint4* wp[U];
         const uint2* sp[U];
@@ -287,6 +324,8 @@ __global__ void __launch_bounds__(waves_for(SPLIT) * 64) gemv_w4_kernel(KernelAr
             uint4 w[D][U];
             uint2 s[D][U];
             uint4 xr[D];
+            uint2 cr[D];
+            float sx[D];
 #pragma unroll
             for (int d = 0; d < D; ++d) {
                 const int j = (i0 + d) * 64 + lane;
@@ -301,19 +340,39 @@ __global__ void __launch_bounds__(waves_for(SPLIT) * 64) gemv_w4_kernel(KernelAr
                             s[d][u] = make_uint2(0, 0);
                         }
                     }
-                    xr[d] = a.x[j];
+                    if constexpr (A8) {
+                        cr[d] = reinterpret_cast<const uint2*>(a.x)[j];
+                        sx[d] = a.xs[j >> a.gshift];
+                    } else {
+                        xr[d] = a.x[j];
+                    }
                 }
             }
 #pragma unroll
             for (int d = 0; d < D; ++d) {
                 const int j = (i0 + d) * 64 + lane;
                 if ((i0 + d < it1) && (FULL || j < a.kb)) {
+                    if constexpr (A8) {
+                        const int n8 = neg8_code_sum(cr[d]);
 #pragma unroll
-                    for (int u = 0; u < U; ++u) {
-                        acc[u][0] = __builtin_fmaf(dot8(w[d][u].x, xr[d], magic), half_lo(s[d][u].x), acc[u][0]);
-                        acc[u][1] = __builtin_fmaf(dot8(w[d][u].y, xr[d], magic), half_hi(s[d][u].x), acc[u][1]);
-                        acc[u][2] = __builtin_fmaf(dot8(w[d][u].z, xr[d], magic), half_lo(s[d][u].y), acc[u][2]);
-                        acc[u][3] = __builtin_fmaf(dot8(w[d][u].w, xr[d], magic), half_hi(s[d][u].y), acc[u][3]);
+                        for (int u = 0; u < U; ++u) {
+                            acc[u][0] = __builtin_fmaf((float)idot8(w[d][u].x, cr[d], n8), half_lo(s[d][u].x) * sx[d],
+                                                       acc[u][0]);
+                            acc[u][1] = __builtin_fmaf((float)idot8(w[d][u].y, cr[d], n8), half_hi(s[d][u].x) * sx[d],
+                                                       acc[u][1]);
+                            acc[u][2] = __builtin_fmaf((float)idot8(w[d][u].z, cr[d], n8), half_lo(s[d][u].y) * sx[d],
+                                                       acc[u][2]);
+                            acc[u][3] = __builtin_fmaf((float)idot8(w[d][u].w, cr[d], n8), half_hi(s[d][u].y) * sx[d],
+                                                       acc[u][3]);
+                        }
+                    } else {
+#pragma unroll
+                        for (int u = 0; u < U; ++u) {
+                            acc[u][0] = __builtin_fmaf(dot8(w[d][u].x, xr[d], magic), half_lo(s[d][u].x), acc[u][0]);
+                            acc[u][1] = __builtin_fmaf(dot8(w[d][u].y, xr[d], magic), half_hi(s[d][u].x), acc[u][1]);
+                            acc[u][2] = __builtin_fmaf(dot8(w[d][u].z, xr[d], magic), half_lo(s[d][u].y), acc[u][2]);
+                            acc[u][3] = __builtin_fmaf(dot8(w[d][u].w, xr[d], magic), half_hi(s[d][u].y), acc[u][3]);
+                        }
                     }
                 }
             }
@@ -456,13 +515,13 @@ argmax_finalize_kernel(const float* __restrict__ part_v, const int32_t* __restri
 
 // Instantiated (split, depth) pairs: depth is the number of k iterations a
 // wave loads per round before computing.
-template <int U, int EPI>
+template <int U, int EPI, bool A8>
 const void* pick(int split, int depth, bool full)
 {
-#define W4_CASE(S, D)                                                                     \
-    if (split == S && depth == D)                                                         \
-        return full ? reinterpret_cast<const void*>(&gemv_w4_kernel<U, EPI, S, D, true>) \
-                    : reinterpret_cast<const void*>(&gemv_w4_kernel<U, EPI, S, D, false>);
+#define W4_CASE(S, D)                                                                         \
+    if (split == S && depth == D)                                                             \
+        return full ? reinterpret_cast<const void*>(&gemv_w4_kernel<U, EPI, S, D, true, A8>) \
+                    : reinterpret_cast<const void*>(&gemv_w4_kernel<U, EPI, S, D, false, A8>);
     if constexpr (U == 1 || EPI == kEpiGateUp) {
         W4_CASE(1, 2)
         W4_CASE(1, 4)
@@ -481,6 +540,19 @@ const void* pick(int split, int depth, bool full)
     return nullptr;
 }
 
+template <bool A8>
+const void* pick_epi(int32_t epi, const LaunchConfig& cfg, bool full)
+{
+    if (epi == kEpiGateUp) return pick<2, kEpiGateUp, A8>(cfg.split, cfg.depth, full);
+    if (epi == kEpiPlain)
+        return cfg.tiles == 2 ? pick<2, kEpiPlain, A8>(cfg.split, cfg.depth, full)
+                              : pick<1, kEpiPlain, A8>(cfg.split, cfg.depth, full);
+    if (epi == kEpiArgmax)
+        return cfg.tiles == 2 ? pick<2, kEpiArgmax, A8>(cfg.split, cfg.depth, full)
+                              : pick<1, kEpiArgmax, A8>(cfg.split, cfg.depth, full);
+    return nullptr;
+}
+
 struct Plan {
     const void* fn;
     int threads;
@@ -496,6 +568,7 @@ Plan make_plan(const GemvCall& c)
     a.pw = static_cast<const uint4*>(c.pw);
     a.ps = static_cast<const uint2*>(c.ps);
     a.x = static_cast<const uint4*>(c.x);
+    a.xs = c.xs;
     a.out = c.out;
     a.n = c.n;
     a.kb = (int32_t)(c.k / 8);
@@ -509,15 +582,7 @@ Plan make_plan(const GemvCall& c)
     const LaunchConfig cfg = choose_config(c.epi, gateup ? a.tiles / 2 : a.tiles, a.iters);
     a.units = gateup ? a.tiles / 2 : (a.tiles + cfg.tiles - 1) / cfg.tiles;
     const bool full = (a.kb % 64) == 0;
-    p.fn = nullptr;
-    if (c.epi == kEpiGateUp)
-        p.fn = pick<2, kEpiGateUp>(cfg.split, cfg.depth, full);
-    else if (c.epi == kEpiPlain)
-        p.fn = cfg.tiles == 2 ? pick<2, kEpiPlain>(cfg.split, cfg.depth, full)
-                              : pick<1, kEpiPlain>(cfg.split, cfg.depth, full);
-    else if (c.epi == kEpiArgmax)
-        p.fn = cfg.tiles == 2 ? pick<2, kEpiArgmax>(cfg.split, cfg.depth, full)
-                              : pick<1, kEpiArgmax>(cfg.split, cfg.depth, full);
+    p.fn = c.xs ? pick_epi<true>(c.epi, cfg, full) : pick_epi<false>(c.epi, cfg, full);
     const int waves = waves_for(cfg.split);
     const int slots = waves / cfg.split;
     p.threads = waves * 64;

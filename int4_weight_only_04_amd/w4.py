@@ -28,6 +28,7 @@ EXPORTED = (
     "w4_embed", "w4_add_rmsnorm", "w4_rope_kv_append",
     "w4_decode_step_create", "w4_decode_step", "w4_decode_step_launches", "w4_decode_step_destroy",
     "w4_decode_step_trace_layout",
+    "w4_quantize_act8", "w4_gemv_a8", "w4_gemv_gateup_silu_a8",
 )
 
 TRACE_FIELDS = ("h_in", "x1", "qkv", "q", "attn", "o", "h_mid", "x2", "m", "d")
@@ -150,6 +151,12 @@ def lib():
     L.w4_decode_step_launches.argtypes = [vp, ctypes.POINTER(i32)]
     L.w4_decode_step_destroy.restype = i32
     L.w4_decode_step_destroy.argtypes = [vp]
+    L.w4_quantize_act8.restype = i32
+    L.w4_quantize_act8.argtypes = [vp, i64, i32, vp, vp, vp]
+    L.w4_gemv_a8.restype = i32
+    L.w4_gemv_a8.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i32, vp]
+    L.w4_gemv_gateup_silu_a8.restype = i32
+    L.w4_gemv_gateup_silu_a8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, vp]
     L.w4_decode_step_trace_layout.restype = i32
     L.w4_decode_step_trace_layout.argtypes = [ctypes.POINTER(StepDesc), ctypes.POINTER(sz), ctypes.POINTER(sz),
                                               ctypes.POINTER(sz)]
@@ -259,6 +266,42 @@ def gemv_gateup_silu(packed_w, packed_s, x, h, n_total: int, k: int, group: int,
                                      _dev_ptr(x, "x", torch.float16, k),
                                      _dev_ptr(h, "h", torch.float16, n_total // 2),
                                      n_total, k, group, _stream(stream)), "w4_gemv_gateup_silu")
+
+
+def quantize_act8(x, group: int, codes, scales, stream=None):
+    """codes int8 [k] (W4T4 block order) and scales fp32 [k/group] of fp16 x."""
+    import torch
+    k = x.numel()
+    _check(lib().w4_quantize_act8(_dev_ptr(x, "x", torch.float16, k), k, group,
+                                  _dev_ptr(codes, "codes", torch.int8, k),
+                                  _dev_ptr(scales, "scales", torch.float32, k // group), _stream(stream)),
+           "w4_quantize_act8")
+
+
+def gemv_a8(packed_w, packed_s, codes, act_scales, y, n: int, k: int, group: int, argmax=None, workspace=None,
+            stream=None):
+    """W4A8 y[n] (fp32) from int8 codes and per-group scales (quantize_act8)."""
+    import torch
+    wb, sb = packed_size(n, k, group, "plain")
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().w4_gemv_a8(_dev_ptr(packed_w, "packed_w", torch.uint8, wb),
+                            _dev_ptr(packed_s, "packed_s", torch.uint8, sb),
+                            _dev_ptr(codes, "codes", torch.int8, k),
+                            _dev_ptr(act_scales, "act_scales", torch.float32, k // group),
+                            _dev_ptr(y, "y", torch.float32, n), _dev_ptr(argmax, "argmax", torch.int32, 1),
+                            _dev_ptr(workspace, "workspace"), ws_bytes, n, k, group, _stream(stream)), "w4_gemv_a8")
+
+
+def gemv_gateup_silu_a8(packed_w, packed_s, codes, act_scales, h, n_total: int, k: int, group: int, stream=None):
+    """W4A8 h[n_total/2] (fp16) = silu(gate) * up."""
+    import torch
+    wb, sb = packed_size(n_total, k, group, "gateup")
+    _check(lib().w4_gemv_gateup_silu_a8(_dev_ptr(packed_w, "packed_w", torch.uint8, wb),
+                                        _dev_ptr(packed_s, "packed_s", torch.uint8, sb),
+                                        _dev_ptr(codes, "codes", torch.int8, k),
+                                        _dev_ptr(act_scales, "act_scales", torch.float32, k // group),
+                                        _dev_ptr(h, "h", torch.float16, n_total // 2), n_total, k, group,
+                                        _stream(stream)), "w4_gemv_gateup_silu_a8")
 
 
 def gemm_workspace_size(m: int, n: int, k: int, group: int) -> int:

@@ -265,6 +265,22 @@ def test_step_glue_validation_before_launch():
     assert rope(bias=A + 1) == w4.EALIGN
 
 
+def test_w4a8_validation_before_launch():
+    L = w4.lib()
+    A = 1 << 20
+    assert L.w4_quantize_act8(None, 256, 64, A, A, None) == w4.EINVAL
+    assert L.w4_quantize_act8(A, 250, 64, A, A, None) == w4.ESHAPE      # k % G
+    assert L.w4_quantize_act8(A, 256, 48, A, A, None) == w4.ESHAPE      # G not a power of two
+    assert L.w4_quantize_act8(A + 8, 256, 64, A, A, None) == w4.EALIGN  # x not 16-byte aligned
+    assert L.w4_quantize_act8(A, 256, 64, A + 4, A, None) == w4.EALIGN  # codes not 8-byte aligned
+    assert L.w4_gemv_a8(A, A, A, None, A, None, None, 0, 4, 64, 32, None) == w4.EINVAL
+    assert L.w4_gemv_a8(A, A, A, A + 2, A, None, None, 0, 4, 64, 32, None) == w4.EALIGN
+    assert L.w4_gemv_a8(A, A, A + 8, A, A, None, None, 0, 4, 64, 32, None) == w4.EALIGN
+    assert L.w4_gemv_a8(A, A, A, A, A, A, A, 16, 4, 64, 32, None) == w4.EINVAL   # argmax workspace too small
+    assert L.w4_gemv_gateup_silu_a8(A, A, A, A, A, 7, 64, 32, None) == w4.ESHAPE
+    assert L.w4_gemv_gateup_silu_a8(A, A, A, None, A, 8, 64, 32, None) == w4.EINVAL
+
+
 def _step_desc(layers_arr, **kw):
     A = 1 << 20
     d = w4.StepDesc()
