@@ -69,6 +69,7 @@ KERNEL_SRC = os.path.join(ROOT, "int4_weight_only_04_amd", "csrc", "w4_kernels.h
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gateup_silu_37888x3584.json")
 GEMM_SRC = os.path.join(ROOT, "int4_weight_only_04_amd", "csrc", "w4_gemm.hip")
 GEMM_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_gateup_512x37888x3584.json")
+A8_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gateup_silu_a8_37888x3584.json")
 
 
 def algorithmic_bytes(kind: str, n: int, k: int, group: int) -> int:
@@ -909,7 +910,7 @@ def run_w4a8(args) -> int:
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": read_traffic(gu_bytes, A8_TRAFFIC_FILE),
             "algorithmic_bytes_per_launch": gu_bytes,
             "avg_launch_us": round(gu_ms * 1e3, 3),
             "launches_timed": replays * n_gu,
