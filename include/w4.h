@@ -442,16 +442,19 @@ typedef struct w4_step w4_step;
  *                h += (silu(x Wgate) * (x Wup)) Wdown
  *     x = rmsnorm(h) final_norm;  logits = x Wlm;  token = argmax(logits);
  *     pos += 1
- * with the library's kernels (w4_embed, w4_add_rmsnorm, w4_gemv,
- * w4_rope_kv_append, w4_attn_decode, w4_gemv_gateup_silu; each residual add
- * is fused into the following norm).  Attention scale 1/sqrt(128).  Because
+ * with the library's kernels: the embedding lookup fused with the first
+ * norm, w4_gemv, w4_add_rmsnorm (each residual add fused into the following
+ * norm), w4_attn_decode with the rotary embedding and KV append fused into
+ * its first kernel (q and the new token's k, v taken from the fp32 QKV
+ * output, cos/sin from a per-position table built at create), and
+ * w4_gemv_gateup_silu.  Attention scale 1/sqrt(128).  Because
  * token and pos are read and advanced on the device, one call of
  * w4_decode_step per token continues the greedy decode with no host work;
  * use_graph != 0 captures the whole step as one HIP graph (one submission per
  * token, the pages' "CUDA Graph Optimization" bullet), use_graph == 0 keeps
  * eager launches for the comparison.  The handle allocates its activation
- * buffers and workspaces (device, at create, about 1 MB for the 7B shapes)
- * and frees them at destroy; every pointer in the descriptor is baked in and
+ * buffers, workspaces and the rotary table (device, at create: about 3 MB
+ * for the 7B shapes at max_ctx 4096) and frees them at destroy; every pointer in the descriptor is baked in and
  * must stay valid until destroy.  pos must stay below max_ctx (at max_ctx - 1
  * the last cache slot is overwritten).  The handle is not thread-safe.
  * Rules: shapes as for the individual calls; hidden, n_heads * 128, inter

@@ -32,7 +32,7 @@ constexpr int kChunk = 64;         // tokens per workgroup
 constexpr int kAttnThreads = 256;  // 4 waves
 
 struct AttnArgs {
-    const uint4* q;          // fp16 [n_heads][128], 16 per head
+    const uint4* q;          // fp16 [n_heads][128], 16 per head (not used with the fused rotary embedding)
     const uint4* kc;         // fp16 cache, 16 uint4 per token row
     const uint32_t* vc;      // fp16 cache, 64 words per token row
     const int32_t* table;    // page table
@@ -46,6 +46,17 @@ struct AttnArgs {
     int32_t n_kv;
     int32_t page_shift;
     int32_t num_pages;
+    // fused rotary embedding + KV append (ROPE kernels): q and the new
+    // token's k, v come from the fp32 QKV projection at position *pos
+    const float* qkv;        // [(n_heads + 2 n_kv) * 128]: q heads, k heads, v heads
+    const float* bias;       // same length, or null
+    const int32_t* pos;
+    int32_t* ctx_out;        // <- pos + 1 (the combine kernel's context length)
+    uint16_t* q_out;         // fp16 [n_heads][128] or null (written by the chunk-0 workgroups)
+    uint4* kc_w;             // the caches, written at the new token's slot
+    uint32_t* vc_w;
+    double theta;
+    const float2* rope_cs;   // (cos, sin) per (position, pair)
 };
 
 __device__ __forceinline__ int clamp_ctx(const AttnArgs& a)
@@ -99,14 +110,39 @@ __device__ __forceinline__ float wave_sum(float v)
     return v;
 }
 
-// GQ query heads per KV head (1..8).
-template <int GQ>
+__device__ __forceinline__ float round_half(float v) { return (float)(_Float16)v; }
+
+// Rotary embedding of the pair (i, i + 64) of the 128-wide head starting at
+// row `base` of the QKV projection (plus bias), at position pos, with the
+// (cos, sin) table of launch_rope_table (double-precision angles rounded to
+// fp32, as the standalone rotary kernel computes them); rotation in fp32.
+__device__ __forceinline__ void rope_pair(const AttnArgs& a, int64_t base, int i, int pos, float& r0, float& r1)
+{
+    float x0 = a.qkv[base + i], x1 = a.qkv[base + i + 64];
+    if (a.bias) {
+        x0 += a.bias[base + i];
+        x1 += a.bias[base + i + 64];
+    }
+    const float2 t = a.rope_cs[(int64_t)pos * 64 + i];
+    r0 = x0 * t.x - x1 * t.y;
+    r1 = x1 * t.x + x0 * t.y;
+}
+
+// GQ query heads per KV head (1..8).  ROPE: the query heads and the new
+// token's key are rotated here from the QKV projection (fp16-rounded, as the
+// stored q and cache are), and the new token's k and v are appended to the
+// cache by the workgroup whose chunk holds it; that workgroup uses them
+// directly, and no other workgroup reads that slot.
+template <int GQ, bool ROPE>
 __global__ void __launch_bounds__(kAttnThreads) attn_partial_kernel(AttnArgs a)
 {
     __shared__ float s_sc[GQ][kChunk];
     __shared__ float s_o[4][GQ][kDim];
     __shared__ float s_m[GQ];
     __shared__ float s_l[GQ];
+    __shared__ float s_q[ROPE ? GQ : 1][kDim];
+    __shared__ float s_knew[ROPE ? kDim : 1];
+    __shared__ uint32_t s_vnew[ROPE ? kDim / 2 : 1];
 
     const int chunk = blockIdx.x;
     const int g = blockIdx.y;
@@ -121,12 +157,21 @@ __global__ void __launch_bounds__(kAttnThreads) attn_partial_kernel(AttnArgs a)
     // context length: q, this lane's 4 K row slices and its 16 V words (rows
     // of tokens past max_ctx are read from the last one; past the context
     // they are masked below)
-    const int ctx = clamp_ctx(a);
+    int ctx, pos = -1;
+    if constexpr (ROPE) {
+        pos = *a.pos;
+        pos = pos < 0 ? 0 : (pos >= a.max_ctx ? a.max_ctx - 1 : pos);
+        ctx = pos + 1;
+    } else {
+        ctx = clamp_ctx(a);
+    }
     const int dpart = lane & 15;
     const int tq = lane >> 4;
-    uint4 qv[GQ];
+    uint4 qv[ROPE ? 1 : GQ];
+    if constexpr (!ROPE) {
 #pragma unroll
-    for (int h = 0; h < GQ; ++h) qv[h] = a.q[(int64_t)(g * GQ + h) * (kDim / 8) + dpart];
+        for (int h = 0; h < GQ; ++h) qv[h] = a.q[(int64_t)(g * GQ + h) * (kDim / 8) + dpart];
+    }
     uint4 kv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -141,6 +186,77 @@ __global__ void __launch_bounds__(kAttnThreads) attn_partial_kernel(AttnArgs a)
         const int64_t row = cache_row(a, t < a.max_ctx ? t : a.max_ctx - 1, g);
         vv[j] = a.vc[row * (kDim / 2) + lane];
     }
+    const bool has_new = ROPE && pos >= t0 && pos < t0 + kChunk;  // uniform per workgroup
+    if constexpr (ROPE) {
+        // rotate this workgroup's query heads (GQ x 64 pairs over 256
+        // threads) and, in the workgroup holding the new token, its k and v
+        if (t0 < ctx) {
+            // at most two pairs per thread (GQ <= 8): every load first, then the math
+            constexpr int kPairs = (GQ * 64 + kAttnThreads - 1) / kAttnThreads;
+            float x0[kPairs], x1[kPairs];
+            float2 cs[kPairs];
+#pragma unroll
+            for (int k = 0; k < kPairs; ++k) {
+                const int p = tid + k * kAttnThreads;
+                if (p < GQ * 64) {
+                    const int64_t base = (int64_t)(g * GQ + p / 64) * kDim;
+                    const int i = p % 64;
+                    x0[k] = a.qkv[base + i];
+                    x1[k] = a.qkv[base + i + 64];
+                    if (a.bias) {
+                        x0[k] += a.bias[base + i];
+                        x1[k] += a.bias[base + i + 64];
+                    }
+                    cs[k] = a.rope_cs[(int64_t)pos * 64 + i];
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < kPairs; ++k) {
+                const int p = tid + k * kAttnThreads;
+                if (p < GQ * 64) {
+                    const int h = p / 64, i = p % 64;
+                    s_q[h][i] = round_half(x0[k] * cs[k].x - x1[k] * cs[k].y);
+                    s_q[h][i + 64] = round_half(x1[k] * cs[k].x + x0[k] * cs[k].y);
+                }
+            }
+            if (has_new) {
+                if (tid < 64) {
+                    float r0, r1;
+                    rope_pair(a, (int64_t)(a.n_heads + g) * kDim, tid, pos, r0, r1);
+                    s_knew[tid] = round_half(r0);
+                    s_knew[tid + 64] = round_half(r1);
+                } else if (tid < 128) {
+                    const int w = tid - 64;  // dimensions 2w, 2w + 1
+                    const int64_t vb = (int64_t)(a.n_heads + a.n_kv + g) * kDim + 2 * w;
+                    float v0 = a.qkv[vb], v1 = a.qkv[vb + 1];
+                    if (a.bias) {
+                        v0 += a.bias[vb];
+                        v1 += a.bias[vb + 1];
+                    }
+                    s_vnew[w] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v0) |
+                                ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v1) << 16);
+                }
+            }
+        }
+        if (chunk == 0 && g == 0 && tid == 0 && a.ctx_out) *a.ctx_out = ctx;
+        __syncthreads();
+        if (has_new) {
+            // append the new token to the cache (the stale slot was loaded
+            // above; its registers are replaced below)
+            const int64_t row = cache_row(a, pos, g);
+            if (tid < 64) {
+                reinterpret_cast<uint32_t*>(a.kc_w)[row * (kDim / 2) + tid] =
+                    (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)s_knew[2 * tid]) |
+                    ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)s_knew[2 * tid + 1]) << 16);
+            } else if (tid < 128) {
+                a.vc_w[row * (kDim / 2) + (tid - 64)] = s_vnew[tid - 64];
+            }
+        }
+        if (chunk == 0 && a.q_out) {
+            for (int i = tid; i < GQ * kDim; i += kAttnThreads)
+                a.q_out[(int64_t)g * GQ * kDim + i] = __builtin_bit_cast(uint16_t, (_Float16)s_q[i / kDim][i % kDim]);
+        }
+    }
     if (t0 >= ctx) {  // whole workgroup: a chunk past the context is empty
         for (int i = tid; i < GQ * kDim; i += kAttnThreads) po[i] = 0.0f;
         if (tid < GQ) {
@@ -153,13 +269,24 @@ __global__ void __launch_bounds__(kAttnThreads) attn_partial_kernel(AttnArgs a)
     // ---- scores: 16 lanes per token, 8 dimensions per lane, 4 tokens per wave step
     float qr[GQ][8];
 #pragma unroll
-    for (int h = 0; h < GQ; ++h) half8_to_float(qv[h], qr[h]);
+    for (int h = 0; h < GQ; ++h) {
+        if constexpr (ROPE) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) qr[h][j] = s_q[h][8 * dpart + j];
+        } else {
+            half8_to_float(qv[h], qr[h]);
+        }
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int tl = wave * 16 + i * 4 + tq;
         const bool valid = t0 + tl < ctx;
         float kf[8];
         half8_to_float(kv[i], kf);
+        if (ROPE && t0 + tl == pos) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) kf[j] = s_knew[8 * dpart + j];
+        }
 #pragma unroll
         for (int h = 0; h < GQ; ++h) {
             float d = 0.0f;
@@ -195,8 +322,9 @@ __global__ void __launch_bounds__(kAttnThreads) attn_partial_kernel(AttnArgs a)
         // a token past the context (weight 0) contributes exactly 0, even if
         // the row it was read from holds an infinity
         const uint32_t keep = 0u - (uint32_t)(t0 + tl < ctx);
-        const float v0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(vv[j] & keep & 0xFFFFu));
-        const float v1 = (float)__builtin_bit_cast(_Float16, (uint16_t)((vv[j] & keep) >> 16));
+        const uint32_t vw = (ROPE && t0 + tl == pos) ? s_vnew[lane] : vv[j];
+        const float v0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(vw & keep & 0xFFFFu));
+        const float v1 = (float)__builtin_bit_cast(_Float16, (uint16_t)((vw & keep) >> 16));
 #pragma unroll
         for (int h = 0; h < GQ; ++h) {
             const float w = s_sc[h][tl];  // 0 for tokens past the context
@@ -315,6 +443,22 @@ size_t attn_workspace_bytes(int32_t n_heads, int32_t max_ctx)
     return (size_t)attn_chunks(max_ctx) * (size_t)n_heads * (kDim + 2) * sizeof(float);
 }
 
+template <bool ROPE>
+const void* partial_fn(int group)
+{
+    switch (group) {
+        case 1: return reinterpret_cast<const void*>(&attn_partial_kernel<1, ROPE>);
+        case 2: return reinterpret_cast<const void*>(&attn_partial_kernel<2, ROPE>);
+        case 3: return reinterpret_cast<const void*>(&attn_partial_kernel<3, ROPE>);
+        case 4: return reinterpret_cast<const void*>(&attn_partial_kernel<4, ROPE>);
+        case 5: return reinterpret_cast<const void*>(&attn_partial_kernel<5, ROPE>);
+        case 6: return reinterpret_cast<const void*>(&attn_partial_kernel<6, ROPE>);
+        case 7: return reinterpret_cast<const void*>(&attn_partial_kernel<7, ROPE>);
+        case 8: return reinterpret_cast<const void*>(&attn_partial_kernel<8, ROPE>);
+        default: return nullptr;
+    }
+}
+
 hipError_t launch_attn(const AttnCall& c, hipStream_t stream)
 {
     AttnArgs a{};
@@ -336,18 +480,22 @@ hipError_t launch_attn(const AttnCall& c, hipStream_t stream)
     a.page_shift = shift;
     a.num_pages = c.num_pages;
     const int group = c.n_heads / c.n_kv;
-    const void* fn = nullptr;
-    switch (group) {
-        case 1: fn = reinterpret_cast<const void*>(&attn_partial_kernel<1>); break;
-        case 2: fn = reinterpret_cast<const void*>(&attn_partial_kernel<2>); break;
-        case 3: fn = reinterpret_cast<const void*>(&attn_partial_kernel<3>); break;
-        case 4: fn = reinterpret_cast<const void*>(&attn_partial_kernel<4>); break;
-        case 5: fn = reinterpret_cast<const void*>(&attn_partial_kernel<5>); break;
-        case 6: fn = reinterpret_cast<const void*>(&attn_partial_kernel<6>); break;
-        case 7: fn = reinterpret_cast<const void*>(&attn_partial_kernel<7>); break;
-        case 8: fn = reinterpret_cast<const void*>(&attn_partial_kernel<8>); break;
-        default: return hipErrorInvalidValue;
+    if (c.rope) {
+        const RopeCall& r = *c.rope;
+        if (!r.table || !r.qkv || !r.pos || !r.k_cache || !r.v_cache || !r.ctx_out) return hipErrorInvalidValue;
+        a.qkv = r.qkv;
+        a.bias = r.bias;
+        a.pos = r.pos;
+        a.ctx_out = r.ctx_out;
+        a.q_out = r.q_out;
+        a.kc_w = reinterpret_cast<uint4*>(r.k_cache);
+        a.vc_w = reinterpret_cast<uint32_t*>(r.v_cache);
+        a.theta = r.theta;
+        a.rope_cs = r.table;
+        a.ctx_ptr = r.ctx_out;  // the combine kernel's context length
     }
+    const void* fn = c.rope ? partial_fn<true>(group) : partial_fn<false>(group);
+    if (!fn) return hipErrorInvalidValue;
     void* args[] = {&a};
     hipError_t err = hipLaunchKernel(fn, dim3((unsigned)chunks, (unsigned)c.n_kv), dim3(kAttnThreads), args, 0, stream);
     if (err != hipSuccess) return err;

@@ -110,6 +110,11 @@ struct AttnCall {
     int32_t n_kv;
     int32_t page_size;
     int32_t num_pages;
+    // Non-null: rotary embedding + KV append fused into the attention (q,
+    // k, v from rope->qkv at *rope->pos; q ignored, ctx_len = rope->ctx_out
+    // is written with pos + 1).  The RopeCall's caches, page table and sizes
+    // must match this call's.
+    const struct RopeCall* rope;
 };
 
 constexpr int32_t kAttnHeadDim = 128;
@@ -135,15 +140,26 @@ struct RopeCall {
     int32_t page_size;         // power of two
     int32_t num_pages;
     int32_t max_ctx;
+    // (cos, sin) of every (position < max_ctx, pair i < 64), fp32, from
+    // launch_rope_table; required by the fused attention, unused by
+    // launch_rope_append
+    const float2* table;
 };
 
 constexpr int64_t kMaxHidden = 1 << 20;
 
 hipError_t launch_embed(const uint16_t* table, int64_t vocab, int64_t hidden, const int32_t* token, float* h,
                         hipStream_t stream);
+// Embedding lookup fused with the first RMSNorm: h = table[token] (fp32),
+// x = fp16(h * gamma / sqrt(mean(h^2) + eps)); one workgroup.
+hipError_t launch_embed_rmsnorm(const uint16_t* table, int64_t vocab, int64_t hidden, const int32_t* token,
+                                const uint16_t* gamma, float eps, float* h, uint16_t* x, hipStream_t stream);
 hipError_t launch_add_rmsnorm(float* h, const float* y, const uint16_t* gamma, int64_t n, float eps, uint16_t* x,
                               hipStream_t stream);
 hipError_t launch_rope_append(const RopeCall& call, hipStream_t stream);
+// table[p * 64 + i] = (cos, sin) of p * theta^(-2i/128) for p < max_ctx,
+// evaluated in double and rounded to fp32 (the rotary kernels' arithmetic).
+hipError_t launch_rope_table(double theta, int32_t max_ctx, float2* table, hipStream_t stream);
 hipError_t launch_advance(int32_t* pos, hipStream_t stream);
 
 // Launch one GEMV on `stream` (shape already validated by the caller); the

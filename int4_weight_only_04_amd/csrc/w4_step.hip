@@ -66,6 +66,162 @@ __global__ void __launch_bounds__(kNormThreads) add_rmsnorm_kernel(float* __rest
 }
 
 
+// One workgroup: h = table[token] (fp16 -> fp32), then the first layer's
+// RMSNorm x = fp16(h * g / sqrt(mean(h^2) + eps)), the same reduction as
+// add_rmsnorm_kernel.
+__global__ void __launch_bounds__(kNormThreads) embed_rmsnorm_kernel(const uint16_t* __restrict__ table, int64_t vocab,
+                                                                     int64_t n, const int32_t* __restrict__ token,
+                                                                     const uint16_t* __restrict__ gamma, float eps,
+                                                                     float* __restrict__ h, uint16_t* __restrict__ x)
+{
+    __shared__ float red[kNormThreads / 64];
+    int64_t t = *token;
+    t = t < 0 ? 0 : (t >= vocab ? vocab - 1 : t);
+    const uint16_t* row = table + t * n;
+    const int tid = threadIdx.x;
+    float ss = 0.0f;
+    for (int64_t i = tid; i < n; i += kNormThreads) {
+        const float v = half_to_float(row[i]);
+        h[i] = v;
+        ss = __builtin_fmaf(v, v, ss);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+    if ((tid & 63) == 0) red[tid >> 6] = ss;
+    __syncthreads();
+    float tot = red[0];
+#pragma unroll
+    for (int w = 1; w < kNormThreads / 64; ++w) tot += red[w];
+    const float r = 1.0f / sqrtf(tot / (float)n + eps);
+    for (int64_t i = tid; i < n; i += kNormThreads) x[i] = float_to_half(h[i] * r * half_to_float(gamma[i]));
+}
+
+// Vector forms of the two norm kernels, used when n % 4 == 0 and
+// n <= 16 x kNormThreads with aligned buffers: each thread owns up to
+// kNormVec float4 of the vector, issues every load (h, y or the embedding
+// row, gamma) before any arithmetic, keeps the values in registers and
+// writes h and x once -- one memory round trip instead of one per strided
+// iteration.  The sum of squares is reduced in a fixed order.
+constexpr int kNormVec = 4;
+
+__device__ __forceinline__ float block_sum(float v, float* red)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    float tot = red[0];
+#pragma unroll
+    for (int w = 1; w < kNormThreads / 64; ++w) tot += red[w];
+    return tot;
+}
+
+__device__ __forceinline__ float4 f4_from_halves(uint2 g)
+{
+    return make_float4(half_to_float((uint16_t)(g.x & 0xFFFFu)), half_to_float((uint16_t)(g.x >> 16)),
+                       half_to_float((uint16_t)(g.y & 0xFFFFu)), half_to_float((uint16_t)(g.y >> 16)));
+}
+
+__device__ __forceinline__ uint2 halves_from_f4(float4 v)
+{
+    return make_uint2((uint32_t)float_to_half(v.x) | ((uint32_t)float_to_half(v.y) << 16),
+                      (uint32_t)float_to_half(v.z) | ((uint32_t)float_to_half(v.w) << 16));
+}
+
+// x = fp16(v * r * gamma) for this thread's float4s, r from the block sum of squares.
+__device__ __forceinline__ void finish_norm4(const float4 (&v)[kNormVec], const uint2 (&g)[kNormVec], float ss,
+                                             int32_t n4, float eps, uint2* __restrict__ x4, float* red)
+{
+    const float tot = block_sum(ss, red);
+    const float r = 1.0f / sqrtf(tot / (float)(4 * n4) + eps);
+#pragma unroll
+    for (int u = 0; u < kNormVec; ++u) {
+        const int i = u * kNormThreads + threadIdx.x;
+        if (i < n4) {
+            const float4 gv = f4_from_halves(g[u]);
+            x4[i] = halves_from_f4(make_float4(v[u].x * r * gv.x, v[u].y * r * gv.y, v[u].z * r * gv.z,
+                                               v[u].w * r * gv.w));
+        }
+    }
+}
+
+__global__ void __launch_bounds__(kNormThreads) add_rmsnorm4_kernel(float4* __restrict__ h, const float4* __restrict__ y,
+                                                                    const uint2* __restrict__ gamma, int32_t n4,
+                                                                    float eps, uint2* __restrict__ x)
+{
+    __shared__ float red[kNormThreads / 64];
+    float4 v[kNormVec], yv[kNormVec];
+    uint2 g[kNormVec];
+#pragma unroll
+    for (int u = 0; u < kNormVec; ++u) {
+        const int i = u * kNormThreads + threadIdx.x;
+        if (i < n4) {
+            v[u] = h[i];
+            if (y) yv[u] = y[i];
+            g[u] = gamma[i];
+        }
+    }
+    float ss = 0.0f;
+#pragma unroll
+    for (int u = 0; u < kNormVec; ++u) {
+        const int i = u * kNormThreads + threadIdx.x;
+        if (i < n4) {
+            if (y) {
+                v[u] = make_float4(v[u].x + yv[u].x, v[u].y + yv[u].y, v[u].z + yv[u].z, v[u].w + yv[u].w);
+                h[i] = v[u];
+            }
+            ss = __builtin_fmaf(v[u].x, v[u].x, ss);
+            ss = __builtin_fmaf(v[u].y, v[u].y, ss);
+            ss = __builtin_fmaf(v[u].z, v[u].z, ss);
+            ss = __builtin_fmaf(v[u].w, v[u].w, ss);
+        }
+    }
+    finish_norm4(v, g, ss, n4, eps, x, red);
+}
+
+__global__ void __launch_bounds__(kNormThreads) embed_rmsnorm4_kernel(const uint16_t* __restrict__ table, int64_t vocab,
+                                                                      const int32_t* __restrict__ token,
+                                                                      const uint2* __restrict__ gamma, int32_t n4,
+                                                                      float eps, float4* __restrict__ h,
+                                                                      uint2* __restrict__ x)
+{
+    __shared__ float red[kNormThreads / 64];
+    int64_t t = *token;
+    t = t < 0 ? 0 : (t >= vocab ? vocab - 1 : t);
+    const uint2* row = reinterpret_cast<const uint2*>(table + t * (int64_t)(4 * n4));
+    float4 v[kNormVec];
+    uint2 e[kNormVec], g[kNormVec];
+#pragma unroll
+    for (int u = 0; u < kNormVec; ++u) {
+        const int i = u * kNormThreads + threadIdx.x;
+        if (i < n4) {
+            e[u] = row[i];
+            g[u] = gamma[i];
+        }
+    }
+    float ss = 0.0f;
+#pragma unroll
+    for (int u = 0; u < kNormVec; ++u) {
+        const int i = u * kNormThreads + threadIdx.x;
+        if (i < n4) {
+            v[u] = f4_from_halves(e[u]);
+            h[i] = v[u];
+            ss = __builtin_fmaf(v[u].x, v[u].x, ss);
+            ss = __builtin_fmaf(v[u].y, v[u].y, ss);
+            ss = __builtin_fmaf(v[u].z, v[u].z, ss);
+            ss = __builtin_fmaf(v[u].w, v[u].w, ss);
+        }
+    }
+    finish_norm4(v, g, ss, n4, eps, x, red);
+}
+
+bool norm4_ok(int64_t n, const void* h, const void* y, const void* gamma, const void* x)
+{
+    auto al = [](const void* p, uintptr_t b) { return (reinterpret_cast<uintptr_t>(p) & (b - 1)) == 0; };
+    return n % 4 == 0 && n / 4 <= (int64_t)kNormVec * kNormThreads && al(h, 16) && (!y || al(y, 16)) &&
+           al(gamma, 8) && al(x, 8);
+}
+
 // One workgroup per head of q and k (v heads ride along with k); thread i < 64
 // rotates the pair (i, i + 64) by pos * theta^(-2i/128) after the optional
 // bias is added.  The angle and its sine and cosine are evaluated in double
@@ -111,6 +267,17 @@ __global__ void __launch_bounds__(64) rope_append_kernel(RopeCall a, int page_sh
     if (a.ctx_out && g == 0 && i == 0) *a.ctx_out = pos + 1;
 }
 
+__global__ void __launch_bounds__(256) rope_table_kernel(double theta, int32_t max_ctx, float2* table)
+{
+    const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (k >= (int64_t)max_ctx * 64) return;
+    const int pos = (int)(k / 64), i = (int)(k % 64);
+    const double ang = (double)pos * pow(theta, -2.0 * (double)i / 128.0);
+    double sn, cs;
+    sincos(ang, &sn, &cs);
+    table[k] = make_float2((float)cs, (float)sn);
+}
+
 __global__ void __launch_bounds__(64) advance_kernel(int32_t* pos)
 {
     if (threadIdx.x == 0) *pos = *pos + 1;
@@ -126,9 +293,29 @@ hipError_t launch_embed(const uint16_t* table, int64_t vocab, int64_t hidden, co
     return hipGetLastError();
 }
 
+hipError_t launch_embed_rmsnorm(const uint16_t* table, int64_t vocab, int64_t hidden, const int32_t* token,
+                                const uint16_t* gamma, float eps, float* h, uint16_t* x, hipStream_t stream)
+{
+    if (norm4_ok(hidden, h, nullptr, gamma, x) && (reinterpret_cast<uintptr_t>(table) & 7u) == 0) {
+        hipLaunchKernelGGL(embed_rmsnorm4_kernel, dim3(1), dim3(kNormThreads), 0, stream, table, vocab, token,
+                           reinterpret_cast<const uint2*>(gamma), (int32_t)(hidden / 4), eps,
+                           reinterpret_cast<float4*>(h), reinterpret_cast<uint2*>(x));
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(embed_rmsnorm_kernel, dim3(1), dim3(kNormThreads), 0, stream, table, vocab, hidden, token, gamma,
+                       eps, h, x);
+    return hipGetLastError();
+}
+
 hipError_t launch_add_rmsnorm(float* h, const float* y, const uint16_t* gamma, int64_t n, float eps, uint16_t* x,
                               hipStream_t stream)
 {
+    if (norm4_ok(n, h, y, gamma, x)) {
+        hipLaunchKernelGGL(add_rmsnorm4_kernel, dim3(1), dim3(kNormThreads), 0, stream, reinterpret_cast<float4*>(h),
+                           reinterpret_cast<const float4*>(y), reinterpret_cast<const uint2*>(gamma), (int32_t)(n / 4),
+                           eps, reinterpret_cast<uint2*>(x));
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(add_rmsnorm_kernel, dim3(1), dim3(kNormThreads), 0, stream, h, y, gamma, n, eps, x);
     return hipGetLastError();
 }
@@ -138,6 +325,13 @@ hipError_t launch_rope_append(const RopeCall& c, hipStream_t stream)
     int shift = 0;
     while ((1 << shift) < c.page_size) ++shift;
     hipLaunchKernelGGL(rope_append_kernel, dim3((unsigned)(c.n_heads + c.n_kv)), dim3(64), 0, stream, c, shift);
+    return hipGetLastError();
+}
+
+hipError_t launch_rope_table(double theta, int32_t max_ctx, float2* table, hipStream_t stream)
+{
+    const int64_t n = (int64_t)max_ctx * 64;
+    hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, theta, max_ctx, table);
     return hipGetLastError();
 }
 

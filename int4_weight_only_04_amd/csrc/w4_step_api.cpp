@@ -193,7 +193,8 @@ w4_status validate_step(const w4_step_desc& d)
 {
     const char* who = "w4_decode_step_create";
     if (d.layers < 1 || !d.layer) return fail(W4_EINVAL, "%s: need at least one layer", who);
-    if (d.hidden < 8 || d.hidden > kMaxHidden || d.inter < 8 || d.vocab < 1 || d.vocab > INT32_MAX - 1)
+    if (d.hidden < 8 || d.hidden > kMaxHidden || d.hidden % 8 != 0 || d.inter < 8 || d.vocab < 1 ||
+        d.vocab > INT32_MAX - 1)
         return fail(W4_ESHAPE, "%s: hidden=%d inter=%d vocab=%lld", who, d.hidden, d.inter, (long long)d.vocab);
     w4_status st = check_kv_shape(d.n_heads, d.n_kv_heads, d.head_dim, d.page_size, d.max_ctx, d.num_pages, who);
     if (st != W4_OK) return st;
@@ -203,7 +204,7 @@ w4_status validate_step(const w4_step_desc& d)
         return fail(W4_EINVAL, "%s: rope_theta=%g must be > 0", who, d.rope_theta);
     if (!d.embed || !d.final_norm || !d.page_table || !d.token || !d.pos || !d.logits)
         return fail(W4_EINVAL, "%s: null pointer in the descriptor", who);
-    if (!aligned_to(d.embed, 2) || !aligned_to(d.final_norm, 2) || !aligned_to(d.page_table, 4) ||
+    if (!aligned_to(d.embed, 2) || !aligned_to(d.final_norm, 8) || !aligned_to(d.page_table, 4) ||
         !aligned_to(d.token, 4) || !aligned_to(d.pos, 4) || !aligned_to(d.logits, 4) ||
         (d.trace && !aligned_to(d.trace, 256)))
         return fail(W4_EALIGN, "%s: descriptor pointers must be aligned to their element size (trace: 256)", who);
@@ -215,7 +216,7 @@ w4_status validate_step(const w4_step_desc& d)
         const w4_layer_desc& L = d.layer[l];
         if (!L.attn_norm || !L.mlp_norm || !L.k_cache || !L.v_cache)
             return fail(W4_EINVAL, "%s: layer %d: null norm or cache pointer", who, l);
-        if (!aligned_to(L.attn_norm, 2) || !aligned_to(L.mlp_norm, 2) || !aligned_to(L.k_cache, 2) ||
+        if (!aligned_to(L.attn_norm, 8) || !aligned_to(L.mlp_norm, 8) || !aligned_to(L.k_cache, 2) ||
             !aligned_to(L.v_cache, 2) || (L.qkv_bias && !aligned_to(L.qkv_bias, 4)))
             return fail(W4_EALIGN, "%s: layer %d: pointers must be aligned to their element size", who, l);
         const GemvCall calls[4] = {
@@ -275,9 +276,16 @@ w4_status w4_decode_step_create(const w4_step_desc* desc, int32_t use_graph, w4_
         int32_t* ctx = static_cast<int32_t*>(alloc(16));
         void* lm_ws = alloc(lm_ws_bytes);
         void* attn_ws = alloc(attn_workspace_bytes(d.n_heads, d.max_ctx));
-        if (!h || !y || !x || !qkv || !q || !ao || !mh || !ctx || !lm_ws || !attn_ws) {
+        float2* rope_cs = static_cast<float2*>(alloc((size_t)d.max_ctx * 64 * sizeof(float2)));
+        if (!h || !y || !x || !qkv || !q || !ao || !mh || !ctx || !lm_ws || !attn_ws || !rope_cs) {
             delete sp;
             return fail(W4_EHIP, "%s: hipMalloc of the step's activation buffers failed", who);
+        }
+        // rotary (cos, sin) of every position, once (the handle's constant)
+        if (launch_rope_table(d.rope_theta, d.max_ctx, rope_cs, nullptr) != hipSuccess ||
+            hipDeviceSynchronize() != hipSuccess) {
+            delete sp;
+            return fail(W4_EHIP, "%s: building the rotary table failed", who);
         }
         lm.x = x;
         lm.ws = lm_ws;
@@ -296,26 +304,36 @@ w4_status w4_decode_step_create(const w4_step_desc* desc, int32_t use_graph, w4_
                              },
                              1, what});
         };
-        s.ops.push_back({[=](hipStream_t st_) { return launch_embed(d.embed, d.vocab, H, d.token, h, st_); }, 1,
-                         "embed"});
+        // layer 0's attention norm runs with the embedding lookup; every later
+        // norm adds the producing GEMV's output to the residual stream first
+        const uint16_t* g0 = d.layer[0].attn_norm;
+        s.ops.push_back({[=](hipStream_t st_) {
+                             return launch_embed_rmsnorm(d.embed, d.vocab, H, d.token, g0, eps, h, x, st_);
+                         },
+                         1, "embed + norm"});
+        copy(0, W4_TRACE_H_IN, h, "trace h");
+        copy(0, W4_TRACE_X1, x, "trace x1");
         for (int32_t l = 0; l < d.layers; ++l) {
             const w4_layer_desc L = d.layer[l];
-            const float* resid = l == 0 ? nullptr : y;  // previous layer's down output
-            s.ops.push_back({[=](hipStream_t st_) { return launch_add_rmsnorm(h, resid, L.attn_norm, H, eps, x, st_); },
-                             1, "attn norm"});
-            copy(l, W4_TRACE_H_IN, h, "trace h");
-            copy(l, W4_TRACE_X1, x, "trace x1");
             const GemvCall qkv_call{L.qkv_w, L.qkv_s, x, qkv, nullptr, nullptr, qkv_rows, H, d.group, kEpiPlain};
             s.ops.push_back({[=](hipStream_t st_) { return launch_gemv(qkv_call, st_); }, 1, "qkv"});
             copy(l, W4_TRACE_QKV, qkv, "trace qkv");
-            const RopeCall rc{qkv, L.qkv_bias, d.pos, q, L.k_cache, L.v_cache, d.page_table, ctx, d.rope_theta,
-                              d.n_heads, d.n_kv_heads, d.page_size, d.num_pages, d.max_ctx};
-            s.ops.push_back({[=](hipStream_t st_) { return launch_rope_append(rc, st_); }, 1, "rope + kv append"});
-            copy(l, W4_TRACE_Q, q, "trace q");
+            // rotary embedding and the KV append run inside the attention's
+            // first kernel (q, and the new token's k and v, from the fp32 QKV
+            // output); it also writes q for the trace and ctx = pos + 1
+            const RopeCall rc{qkv,         L.qkv_bias,   d.pos,       q,           L.k_cache,
+                              L.v_cache,   d.page_table, ctx,         d.rope_theta, d.n_heads,
+                              d.n_kv_heads, d.page_size, d.num_pages, d.max_ctx,   rope_cs};
             const AttnCall ac{q, L.k_cache, L.v_cache, d.page_table, ctx, ao, attn_ws,
                               (float)(1.0 / sqrt((double)kAttnHeadDim)), d.max_ctx, d.n_heads, d.n_kv_heads,
-                              d.page_size, d.num_pages};
-            s.ops.push_back({[=](hipStream_t st_) { return launch_attn(ac, st_); }, 2, "attention"});
+                              d.page_size, d.num_pages, nullptr};
+            s.ops.push_back({[=](hipStream_t st_) {
+                                 AttnCall fused = ac;
+                                 fused.rope = &rc;
+                                 return launch_attn(fused, st_);
+                             },
+                             2, "rope + kv append + attention"});
+            copy(l, W4_TRACE_Q, q, "trace q");
             copy(l, W4_TRACE_ATTN, ao, "trace attn");
             const GemvCall o_call{L.o_w, L.o_s, ao, y, nullptr, nullptr, H, attn_dim, d.group, kEpiPlain};
             s.ops.push_back({[=](hipStream_t st_) { return launch_gemv(o_call, st_); }, 1, "o_proj"});
@@ -328,14 +346,15 @@ w4_status w4_decode_step_create(const w4_step_desc* desc, int32_t use_graph, w4_
                                    d.group, kEpiGateUp};
             s.ops.push_back({[=](hipStream_t st_) { return launch_gemv(gu_call, st_); }, 1, "gate/up"});
             copy(l, W4_TRACE_M, mh, "trace m");
+            const uint16_t* g_next = l + 1 < d.layers ? d.layer[l + 1].attn_norm : d.final_norm;
             const GemvCall dn_call{L.down_w, L.down_s, mh, y, nullptr, nullptr, H, d.inter, d.group, kEpiPlain};
             s.ops.push_back({[=](hipStream_t st_) { return launch_gemv(dn_call, st_); }, 1, "down"});
             copy(l, W4_TRACE_D, y, "trace d");
+            s.ops.push_back({[=](hipStream_t st_) { return launch_add_rmsnorm(h, y, g_next, H, eps, x, st_); },
+                             1, l + 1 < d.layers ? "attn norm" : "final norm"});
+            copy(l + 1, W4_TRACE_H_IN, h, "trace h");
+            copy(l + 1, W4_TRACE_X1, x, "trace x1");
         }
-        s.ops.push_back({[=](hipStream_t st_) { return launch_add_rmsnorm(h, y, d.final_norm, H, eps, x, st_); },
-                         1, "final norm"});
-        copy(d.layers, W4_TRACE_H_IN, h, "trace final h");
-        copy(d.layers, W4_TRACE_X1, x, "trace final x");
         s.ops.push_back({[=](hipStream_t st_) { return launch_gemv(lm, st_); }, 2, "lm_head + argmax"});
         int32_t* pos = d.pos;
         s.ops.push_back({[=](hipStream_t st_) { return launch_advance(pos, st_); }, 1, "advance"});
