@@ -210,8 +210,9 @@ class Model:
         self.m = m
         self.layers = []
         dev_layers = []
-        self.num_pages = max_ctx // page + 2
-        self.table = synthetic.page_table(seed + 1, self.num_pages, max_ctx // page)
+        entries = -(-max_ctx // page)  # logical pages covering max_ctx tokens
+        self.num_pages = entries + 2
+        self.table = synthetic.page_table(seed + 1, self.num_pages, entries)
         self.kc0, self.vc0 = [], []
         for l, L in enumerate(m["layers"]):
             lay = ostep.Layer(attn_norm=L["attn_norm"], qkv=ostep.Proj(*L["qkv"]), o=ostep.Proj(*L["o"]),
@@ -379,6 +380,30 @@ def test_step_first_position():
     st.run()
     torch.cuda.synchronize()
     check_step(model, st, 999, 0, before)
+
+
+@pytest.mark.parametrize("n_heads,n_kv,page,max_ctx,start", [
+    (2, 2, 1, 40, 37),      # one query head per KV head, one token per page
+    (8, 2, 64, 100, 97),    # the last chunk's reads past max_ctx are clamped onto the slot being appended
+    (6, 3, 16, 70, 63),     # steps across a chunk boundary (63 -> 64) into the ragged last chunk
+    (4, 1, 8, 129, 126),    # four query heads on one KV head; the new token ends at max_ctx - 1 = 128
+])
+def test_step_fused_attention_edges(n_heads, n_kv, page, max_ctx, start):
+    """The rotary + KV append fused into attention at the cache's edges:
+    every step teacher-forced, up to the last position of the cache."""
+    cfg = dict(hidden=256, n_heads=n_heads, n_kv=n_kv, inter=512, vocab=300, group=64, layers=2, page=page,
+               max_ctx=max_ctx)
+    model = Model(60 + n_heads + page, bias=True, **cfg)
+    st = model.step(True)
+    model.token.fill_(3)
+    model.pos.fill_(start)
+    torch.cuda.synchronize()
+    for _ in range(max_ctx - start):
+        token, pos = int(model.token.item()), int(model.pos.item())
+        before = model.caches()
+        st.run()
+        torch.cuda.synchronize()
+        check_step(model, st, token, pos, before)
 
 
 @pytest.mark.slow
