@@ -185,6 +185,37 @@ def time_dominant_kernel(projs, stream, replays: int = 4):
     return a.elapsed_time(b) / launches, launches
 
 
+def time_pure_read_sweep(specs, stream, steps: int, warmup: int):
+    """The ceiling of a sweep built from one kernel per projection: a graph of
+    113 launches of the library's read-only probe kernel (the GEMVs' 16-byte
+    non-temporal loads and nothing else), each over exactly the packed weight +
+    scale bytes of one projection, in sweep order, from one buffer.  Also one
+    1 GiB read, the streaming ceiling of the loads themselves."""
+    import torch
+    from int4_weight_only_04_amd import w4
+    sizes = []
+    for p in specs:
+        layout = "gateup" if p.kind == "gateup" else "plain"
+        wb, sb = w4.packed_size(p.n, p.k, p.group, layout)
+        sizes.append((wb + sb + 255) // 256 * 256)
+    total = sum(sizes)
+    buf = torch.empty(max(total, 1 << 30), dtype=torch.uint8, device="cuda")
+    buf[: 1 << 20].fill_(1)
+    sink = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    offs = np.concatenate([[0], np.cumsum(sizes)[:-1]]).astype(np.int64)
+
+    def launch(s):
+        for off, nb in zip(offs, sizes):
+            w4.read_probe(buf[int(off):], nb, sink, stream=s)
+
+    g = capture(launch, stream)
+    ms = replay_ms(g, stream, steps, warmup)
+    big = capture(lambda s: w4.read_probe(buf, 1 << 30, sink, stream=s), stream)
+    big_ms = replay_ms(big, stream, 10, 2)
+    del g, big
+    return ms, total, (1 << 30) / (big_ms * 1e-3) / 1e9
+
+
 def cpu_baseline():
     """The oracle as it stands (single thread, fp64) on a bounded sample: all
     rows of layer 0's four projections, inputs drawn exactly as in the sweep."""
@@ -991,6 +1022,8 @@ def main(argv=None):
 
     print("[bench] dominant kernel", file=sys.stderr, flush=True)
     gu_mean_ms, gu_launches = time_dominant_kernel(projs, stream)
+    print("[bench] pure-read ceiling (113 read-only launches)", file=sys.stderr, flush=True)
+    read_ms, read_bytes, stream_gbs = time_pure_read_sweep(specs, stream, args.steps, args.warmup)
     gp = next(p for p in specs if p.kind == "gateup")
     gu_bytes = algorithmic_bytes("gateup", gp.n, gp.k, gp.group)
     gu_gbs = gu_bytes / (gu_mean_ms * 1e-3) / 1e9
@@ -1021,6 +1054,10 @@ def main(argv=None):
             "wall_ms_per_step": round(wall_ms, 4),
             "eager_ms_per_step": round(eager_ms, 4),
             "graph_speedup_vs_eager": round(eager_ms / ev_ms, 3),
+            "pure_read_sweep_ms": round(read_ms, 4),
+            "pure_read_sweep_gbs": round(read_bytes / (read_ms * 1e-3) / 1e9, 1),
+            "sweep_time_vs_pure_read": round(ev_ms / read_ms, 3),
+            "stream_read_1gib_gbs": round(stream_gbs, 1),
         },
         "roofline": {
             "kernel": "gemv_w4_kernel<2, gate/up+silu> 37888x3584 g128",

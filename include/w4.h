@@ -184,6 +184,17 @@ w4_status w4_gemm_gateup_silu(const void* packed_w, const void* packed_s, const 
                               void* stream);
 
 /*
+ * Diagnostic, not part of the method: a kernel that only reads `bytes`
+ * (a positive multiple of 16) of device memory at `buf` (16-byte aligned)
+ * with the same 16-byte non-temporal loads as the GEMVs' weight stream, and
+ * stores a checksum word per workgroup into `sink` (device uint32 [1024],
+ * contents meaningless).  Launched once per matrix of a sweep, in the same
+ * order, it measures the practical ceiling of a sweep built from one kernel
+ * per projection.  Device, asynchronous.
+ */
+w4_status w4_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+
+/*
  * W4A8: the INT8-activation variant of the GEMV, the path the pages' runtime
  * implemented, tested and removed ("Tutorial: como construir seu proprio
  * runtime de LLM do zero", noticiai.com.br, "As tres licoes", lesson 3;

@@ -322,6 +322,22 @@ w4_status w4_gemv_gateup_silu_a8(const void* packed_w, const void* packed_s, con
     }
 }
 
+w4_status w4_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream)
+{
+    try {
+        const char* who = "w4_read_probe";
+        if (!buf || !sink) return fail(W4_EINVAL, "%s: null pointer", who);
+        if (bytes == 0 || bytes % 16 != 0 || bytes / 16 > ((size_t)1 << 40))
+            return fail(W4_ESHAPE, "%s: bytes=%zu must be a positive multiple of 16", who, bytes);
+        if (!aligned16(buf) || !aligned_to(sink, 4)) return fail(W4_EALIGN, "%s: buf must be 16-byte aligned", who);
+        hipError_t err = launch_read_probe(buf, bytes, sink, static_cast<hipStream_t>(stream));
+        if (err != hipSuccess) return hip_fail(err, "w4_read_probe launch");
+        return ok();
+    } catch (...) {
+        return fail(W4_EINVAL, "w4_read_probe: internal exception");
+    }
+}
+
 w4_status w4_gemm_workspace_size(int64_t m, int64_t n, int64_t k, int32_t group, size_t* bytes)
 {
     try {

@@ -162,6 +162,11 @@ hipError_t launch_rope_append(const RopeCall& call, hipStream_t stream);
 hipError_t launch_rope_table(double theta, int32_t max_ctx, float2* table, hipStream_t stream);
 hipError_t launch_advance(int32_t* pos, hipStream_t stream);
 
+// Read-only bandwidth probe: streams `bytes` (a multiple of 16, 16-byte
+// aligned) with 16-byte non-temporal loads; sink holds kProbeSinkWords words.
+constexpr int kProbeSinkWords = 1024;
+hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
+
 // Launch one GEMV on `stream` (shape already validated by the caller); the
 // argmax epilogue adds a one-workgroup finalize kernel on the same stream.
 hipError_t launch_gemv(const GemvCall& call, hipStream_t stream);

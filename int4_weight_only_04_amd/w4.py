@@ -28,7 +28,7 @@ EXPORTED = (
     "w4_embed", "w4_add_rmsnorm", "w4_rope_kv_append",
     "w4_decode_step_create", "w4_decode_step", "w4_decode_step_launches", "w4_decode_step_destroy",
     "w4_decode_step_trace_layout",
-    "w4_quantize_act8", "w4_gemv_a8", "w4_gemv_gateup_silu_a8",
+    "w4_quantize_act8", "w4_gemv_a8", "w4_gemv_gateup_silu_a8", "w4_read_probe",
 )
 
 TRACE_FIELDS = ("h_in", "x1", "qkv", "q", "attn", "o", "h_mid", "x2", "m", "d")
@@ -151,6 +151,8 @@ def lib():
     L.w4_decode_step_launches.argtypes = [vp, ctypes.POINTER(i32)]
     L.w4_decode_step_destroy.restype = i32
     L.w4_decode_step_destroy.argtypes = [vp]
+    L.w4_read_probe.restype = i32
+    L.w4_read_probe.argtypes = [vp, sz, vp, vp]
     L.w4_quantize_act8.restype = i32
     L.w4_quantize_act8.argtypes = [vp, i64, i32, vp, vp, vp]
     L.w4_gemv_a8.restype = i32
@@ -266,6 +268,16 @@ def gemv_gateup_silu(packed_w, packed_s, x, h, n_total: int, k: int, group: int,
                                      _dev_ptr(x, "x", torch.float16, k),
                                      _dev_ptr(h, "h", torch.float16, n_total // 2),
                                      n_total, k, group, _stream(stream)), "w4_gemv_gateup_silu")
+
+
+def read_probe(buf, nbytes: int, sink, stream=None):
+    """Diagnostic: stream nbytes of a device buffer with the GEMVs' loads
+    (sink: device int32/uint32 tensor of 1024 words)."""
+    import torch
+    if buf.numel() * buf.element_size() < nbytes:
+        raise ValueError("buffer smaller than nbytes")
+    _check(lib().w4_read_probe(_dev_ptr(buf, "buf"), nbytes, _dev_ptr(sink, "sink", None, 1024), _stream(stream)),
+           "w4_read_probe")
 
 
 def quantize_act8(x, group: int, codes, scales, stream=None):

@@ -265,6 +265,15 @@ def test_step_glue_validation_before_launch():
     assert rope(bias=A + 1) == w4.EALIGN
 
 
+def test_read_probe_validation_before_launch():
+    L = w4.lib()
+    A = 1 << 20
+    assert L.w4_read_probe(None, 1024, A, None) == w4.EINVAL
+    assert L.w4_read_probe(A, 0, A, None) == w4.ESHAPE
+    assert L.w4_read_probe(A, 1000, A, None) == w4.ESHAPE
+    assert L.w4_read_probe(A + 8, 1024, A, None) == w4.EALIGN
+
+
 def test_w4a8_validation_before_launch():
     L = w4.lib()
     A = 1 << 20
