@@ -14,7 +14,8 @@
 // and unnormalised fp32 output.  The second merges the chunks in chunk order
 // (deterministic).  The context length is read from device memory, so a
 // captured graph replays unchanged from token to token; the grid is sized for
-// max_ctx and chunks past the context write an empty partial.  A chunk's
+// max_ctx, and a chunk past the context exits before reading the cache (the
+// combine reads only the chunks below the context).  A chunk's
 // softmax covers every token in it, the page's tail included: all waves reach
 // every barrier, and tokens past the context are masked, never skipped with
 // an early exit (the barrier-in-a-branch mistake the pages describe corrupted
@@ -153,10 +154,25 @@ __global__ void __launch_bounds__(kAttnThreads) attn_partial_kernel(AttnArgs a)
     float* po = a.part_o + ((int64_t)chunk * a.n_heads + (int64_t)g * GQ) * kDim;
     float* pml = a.part_ml + ((int64_t)chunk * a.n_heads + (int64_t)g * GQ) * 2;
 
-    // ---- every load of the workgroup goes out first, none waiting for the
-    // context length: q, this lane's 4 K row slices and its 16 V words (rows
-    // of tokens past max_ctx are read from the last one; past the context
-    // they are masked below)
+    // ---- first round: the context length (or position) and the page-table
+    // entries of this lane's K and V rows; a chunk past the context ends
+    // here, before any K/V traffic (the combine never reads its partial).
+    // Second round: q and the K row slices and V words, all issued before any
+    // math (rows of tokens past max_ctx are read from the last one; past the
+    // context they are masked below).
+    const int dpart = lane & 15;
+    const int tq = lane >> 4;
+    int64_t krow[4], vrow[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int t = t0 + wave * 16 + i * 4 + tq;
+        krow[i] = cache_row(a, t < a.max_ctx ? t : a.max_ctx - 1, g);
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int t = t0 + wave * 16 + j;
+        vrow[j] = cache_row(a, t < a.max_ctx ? t : a.max_ctx - 1, g);
+    }
     int ctx, pos = -1;
     if constexpr (ROPE) {
         pos = *a.pos;
@@ -165,8 +181,7 @@ __global__ void __launch_bounds__(kAttnThreads) attn_partial_kernel(AttnArgs a)
     } else {
         ctx = clamp_ctx(a);
     }
-    const int dpart = lane & 15;
-    const int tq = lane >> 4;
+    if (t0 >= ctx) return;  // whole workgroup, before any barrier
     uint4 qv[ROPE ? 1 : GQ];
     if constexpr (!ROPE) {
 #pragma unroll
@@ -174,18 +189,10 @@ __global__ void __launch_bounds__(kAttnThreads) attn_partial_kernel(AttnArgs a)
     }
     uint4 kv[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int t = t0 + wave * 16 + i * 4 + tq;
-        const int64_t row = cache_row(a, t < a.max_ctx ? t : a.max_ctx - 1, g);
-        kv[i] = a.kc[row * (kDim / 8) + dpart];
-    }
+    for (int i = 0; i < 4; ++i) kv[i] = a.kc[krow[i] * (kDim / 8) + dpart];
     uint32_t vv[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        const int t = t0 + wave * 16 + j;
-        const int64_t row = cache_row(a, t < a.max_ctx ? t : a.max_ctx - 1, g);
-        vv[j] = a.vc[row * (kDim / 2) + lane];
-    }
+    for (int j = 0; j < 16; ++j) vv[j] = a.vc[vrow[j] * (kDim / 2) + lane];
     const bool has_new = ROPE && pos >= t0 && pos < t0 + kChunk;  // uniform per workgroup
     if constexpr (ROPE) {
         // rotate this workgroup's query heads (GQ x 64 pairs over 256
@@ -257,15 +264,6 @@ __global__ void __launch_bounds__(kAttnThreads) attn_partial_kernel(AttnArgs a)
                 a.q_out[(int64_t)g * GQ * kDim + i] = __builtin_bit_cast(uint16_t, (_Float16)s_q[i / kDim][i % kDim]);
         }
     }
-    if (t0 >= ctx) {  // whole workgroup: a chunk past the context is empty
-        for (int i = tid; i < GQ * kDim; i += kAttnThreads) po[i] = 0.0f;
-        if (tid < GQ) {
-            pml[2 * tid] = -__builtin_inff();
-            pml[2 * tid + 1] = 0.0f;
-        }
-        return;
-    }
-
     // ---- scores: 16 lanes per token, 8 dimensions per lane, 4 tokens per wave step
     float qr[GQ][8];
 #pragma unroll
