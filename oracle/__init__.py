@@ -75,6 +75,10 @@ class Oracle:
         lib.oracle_attn_decode.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, ctypes.c_double, p, p]
         lib.oracle_rmsnorm.restype = None
         lib.oracle_rmsnorm.argtypes = [p, i64, p, ctypes.c_double, p]
+        lib.oracle_rmsnorm_given.restype = None
+        lib.oracle_rmsnorm_given.argtypes = [p, i64, p, ctypes.c_double, ctypes.c_double, p]
+        lib.oracle_sumsq_blocks.restype = None
+        lib.oracle_sumsq_blocks.argtypes = [p, i64, i64, p]
         lib.oracle_rope.restype = None
         lib.oracle_rope.argtypes = [p, i32, i64, ctypes.c_double, p]
         lib.oracle_silu.restype = ctypes.c_double
@@ -229,6 +233,23 @@ class Oracle:
         self.lib.oracle_rmsnorm(_ptr(h), h.size, _ptr(gamma_bits), float(eps), _ptr(out))
         return out
 
+    def rmsnorm_given(self, h: np.ndarray, gamma_bits: np.ndarray, sumsq: float, eps: float) -> np.ndarray:
+        """h / sqrt(sumsq / n + eps) * gamma in float64, the sum of squares given."""
+        h = np.ascontiguousarray(h, dtype=np.float64)
+        gamma_bits = np.ascontiguousarray(gamma_bits, dtype=np.uint16)
+        assert gamma_bits.shape == h.shape and h.ndim == 1
+        out = np.empty_like(h)
+        self.lib.oracle_rmsnorm_given(_ptr(h), h.size, _ptr(gamma_bits), float(sumsq), float(eps), _ptr(out))
+        return out
+
+    def sumsq_blocks(self, h: np.ndarray, rows: int) -> np.ndarray:
+        """Sums of h^2 over consecutive blocks of `rows` values (the last may be short)."""
+        h = np.ascontiguousarray(h, dtype=np.float64)
+        assert h.ndim == 1 and rows >= 1
+        out = np.empty((h.size + rows - 1) // rows, np.float64)
+        self.lib.oracle_sumsq_blocks(_ptr(h), h.size, int(rows), _ptr(out))
+        return out
+
     def rope(self, x: np.ndarray, pos: int, theta: float) -> np.ndarray:
         """Rotary embedding of each row of x [heads, dim] at position pos."""
         x = np.ascontiguousarray(x, dtype=np.float64)
@@ -360,6 +381,14 @@ def attn_decode(q_bits, k_cache, v_cache, page_table, ctx, n_kv, page, scale):
 
 def rmsnorm(h, gamma_bits, eps):
     return default().rmsnorm(h, gamma_bits, eps)
+
+
+def rmsnorm_given(h, gamma_bits, sumsq, eps):
+    return default().rmsnorm_given(h, gamma_bits, sumsq, eps)
+
+
+def sumsq_blocks(h, rows):
+    return default().sumsq_blocks(h, rows)
 
 
 def rope(x, pos, theta):

@@ -352,6 +352,29 @@ void oracle_rmsnorm(const double* h, int64_t n, const uint16_t* gamma, double ep
     for (int64_t i = 0; i < n; ++i) out[i] = h[i] * r * oracle_half_to_double(gamma[i]);
 }
 
+/* The same normalization with the sum of squares supplied by the caller: the
+ * mean of h^2 is a sum divided by n, and that sum may have been accumulated
+ * in parts (for instance per block of rows of the projection that produced h).
+ *   out[i] = h[i] / sqrt(sumsq / n + eps) * gamma[i] */
+void oracle_rmsnorm_given(const double* h, int64_t n, const uint16_t* gamma, double sumsq, double eps,
+                          double* out)
+{
+    double r = 1.0 / sqrt(sumsq / (double)n + eps);
+    for (int64_t i = 0; i < n; ++i) out[i] = h[i] * r * oracle_half_to_double(gamma[i]);
+}
+
+/* Sum of squares of h in consecutive blocks of `rows` values:
+ *   out[u] = sum of h[i]^2 for u * rows <= i < min(n, (u + 1) * rows) */
+void oracle_sumsq_blocks(const double* h, int64_t n, int64_t rows, double* out)
+{
+    int64_t parts = (n + rows - 1) / rows;
+    for (int64_t u = 0; u < parts; ++u) {
+        double t = 0.0;
+        for (int64_t i = u * rows; i < n && i < (u + 1) * rows; ++i) t += h[i] * h[i];
+        out[u] = t;
+    }
+}
+
 /* Rotary embedding of one head of `dim` values at position pos, rotating the
  * pairs (i, i + dim/2) by pos * theta^(-2i/dim):
  *   out[i]         = x[i] cos a - x[i + dim/2] sin a

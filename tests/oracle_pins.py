@@ -432,6 +432,29 @@ def pin_rmsnorm(orc):
     assert np.allclose(o1 * np.sqrt(np.mean(h ** 2)), h, rtol=1e-13, atol=0)
 
 
+def pin_rmsnorm_given_and_sumsq_blocks(orc):
+    """The norm with its sum of squares given: a unit mean square with eps = 0
+    returns h * gamma exactly, a mean square of 4 halves it, and fed the sum of
+    the block sums it is the plain RMSNorm.  Block sums: rows = 1 gives the
+    squares, the blocks of a ragged length cover every value once, and a
+    hand-worked case."""
+    rng = np.random.default_rng(59)
+    n = 1000
+    h = rng.standard_normal(n) * 2.0
+    g = _h(rng.uniform(0.5, 1.5, n))
+    hg = h * g.view(np.float16).astype(np.float64)
+    assert np.array_equal(orc.rmsnorm_given(h, g, float(n), 0.0), hg)
+    assert np.array_equal(orc.rmsnorm_given(h, g, 4.0 * n, 0.0), hg / 2.0)
+    for rows in (1, 4, 7, 1000, 1024):
+        parts = orc.sumsq_blocks(h, rows)
+        assert parts.size == -(-n // rows)
+        assert np.allclose(orc.rmsnorm_given(h, g, float(np.sum(parts)), 1e-6), orc.rmsnorm(h, g, 1e-6),
+                           rtol=1e-13, atol=0)
+        assert abs(np.sum(parts) - np.sum(h ** 2)) <= 1e-12 * np.sum(h ** 2)
+    assert np.array_equal(orc.sumsq_blocks(h, 1), h * h)
+    assert np.array_equal(orc.sumsq_blocks(np.array([1.0, 2.0, 3.0, 4.0, 5.0]), 2), np.array([5.0, 25.0, 25.0]))
+
+
 def pin_rope(orc):
     """RoPE against the complex-number form (x_i + j x_{i+d/2}) e^{j a_i},
     identity at position 0, norm preservation, composition of positions and

@@ -51,6 +51,10 @@ MUTANTS = [
     ("attn_abs_dropped", "a[(int64_t)h * dim + d] += w * fabs(v);", "a[(int64_t)h * dim + d] += w * v;", None),
     ("rmsnorm_no_mean", "double r = 1.0 / sqrt(ss / (double)n + eps);", "double r = 1.0 / sqrt(ss + eps);", None),
     ("rmsnorm_gamma_dropped", "out[i] = h[i] * r * oracle_half_to_double(gamma[i]);", "out[i] = h[i] * r;", None),
+    ("rmsnorm_given_no_mean", "double r = 1.0 / sqrt(sumsq / (double)n + eps);", "double r = 1.0 / sqrt(sumsq + eps);",
+     None),
+    ("sumsq_blocks_overlap", "i < n && i < (u + 1) * rows;", "i < n && i <= (u + 1) * rows;", None),
+    ("sumsq_blocks_not_squared", "t += h[i] * h[i];", "t += h[i];", None),
     ("rope_sign", "out[i] = x[i] * c - x[i + half] * sn;", "out[i] = x[i] * c + x[i + half] * sn;", None),
     ("rope_freq", "pow(theta, -2.0 * (double)i / (double)dim)", "pow(theta, -(double)i / (double)dim)", None),
     ("act8_truncate", "float r = rintf(prod);", "float r = truncf(prod);", None),
