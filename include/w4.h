@@ -351,6 +351,61 @@ w4_status w4_add_rmsnorm(float* h, const float* y, const uint16_t* gamma, int64_
                          void* stream);
 
 /*
+ * The residual add and the RMSNorm above, folded into the projections on
+ * either side of them (the same decoder reading; the fold itself is this
+ * library's, not the pages').  A projection whose output feeds the residual
+ * stream (o_proj, down) adds it and emits partial sums of squares; the next
+ * projection (qkv, gate/up, lm_head) normalizes h itself from those partials,
+ * so no separate norm kernel runs between them.
+ *
+ * Number of partial sums w4_gemv_residual writes for an n x k projection
+ * (one per 4-row tile while n <= 65532; fewer for taller matrices).  Host only.
+ * Rules as for w4_gemv (W4_ESHAPE).
+ */
+w4_status w4_residual_parts(int64_t n, int64_t k, int32_t group, int64_t* parts);
+
+/*
+ * y = W x as w4_gemv (no argmax), then h_out[i] = h_in[i] + y[i] in fp32
+ * (i < n; h_out may be h_in) and ss_part[u] = the sum of h_out[i]^2 over the
+ * rows of partial u (fp32, a fixed order), for u < w4_residual_parts(n, k,
+ * group).  Device, asynchronous, one kernel.
+ *   x  device fp16 [k];  y, h_in, h_out  device fp32 [n];
+ *   ss_part  device fp32, 16-byte aligned, w4_residual_parts floats written.
+ * Rules as for w4_gemv; y, h_in and h_out 4-byte aligned (W4_EALIGN).
+ */
+w4_status w4_gemv_residual(const void* packed_w, const void* packed_s, const uint16_t* x, float* y,
+                           const float* h_in, float* h_out, float* ss_part, int64_t n, int64_t k, int32_t group,
+                           void* stream);
+
+/*
+ * RMSNorm folded into the GEMV input: with S = the sum of ss_part[0 .. parts)
+ * (fp32, a fixed order) and r = 1 / sqrt(S / k + eps),
+ *     x[i] = fp16( (h[i] * r) * gamma[i] )      (fp32 products, nearest even)
+ * and then y = W x exactly as w4_gemv, optionally with the argmax epilogue.
+ * Every workgroup computes the same x; the first also stores it to x_out
+ * when x_out != NULL.  Device, asynchronous (one kernel, two with argmax).
+ *   h  device fp32 [k];  gamma  device fp16 [k];  x_out  device fp16 [k] or
+ *   NULL;  ss_part  device fp32, parts values, readable up to the next
+ *   multiple of 4 floats (the values past parts are ignored);
+ *   y, argmax, workspace as for w4_gemv.
+ * Rules as for w4_gemv; 1 <= parts <= 1024 (W4_ESHAPE); eps >= 0 and finite
+ * (W4_EINVAL); h, gamma, ss_part and x_out 16-byte aligned (W4_EALIGN).
+ */
+w4_status w4_gemv_rmsnorm(const void* packed_w, const void* packed_s, const float* h, const uint16_t* gamma,
+                          const float* ss_part, int64_t parts, float eps, uint16_t* x_out, float* y,
+                          int32_t* argmax, void* workspace, size_t workspace_bytes, int64_t n, int64_t k,
+                          int32_t group, void* stream);
+
+/*
+ * w4_gemv_gateup_silu with its input normalized as in w4_gemv_rmsnorm.
+ *   h_mlp  device fp16 [n_total / 2], the SiLU-gated output.
+ */
+w4_status w4_gemv_gateup_silu_rmsnorm(const void* packed_w, const void* packed_s, const float* h,
+                                      const uint16_t* gamma, const float* ss_part, int64_t parts, float eps,
+                                      uint16_t* x_out, uint16_t* h_mlp, int64_t n_total, int64_t k, int32_t group,
+                                      void* stream);
+
+/*
  * Rotary embedding and KV-cache append for one new token at position
  * p = *pos (device int32, clamped into [0, max_ctx)).  qkv holds the fused
  * projection's output: n_heads query heads, then n_kv_heads key heads, then
@@ -454,11 +509,14 @@ typedef struct w4_step w4_step;
  *     x = rmsnorm(h) final_norm;  logits = x Wlm;  token = argmax(logits);
  *     pos += 1
  * with the library's kernels: the embedding lookup fused with the first
- * norm, w4_gemv, w4_add_rmsnorm (each residual add fused into the following
- * norm), w4_attn_decode with the rotary embedding and KV append fused into
- * its first kernel (q and the new token's k, v taken from the fp32 QKV
- * output, cos/sin from a per-position table built at create), and
- * w4_gemv_gateup_silu.  Attention scale 1/sqrt(128).  Because
+ * norm; w4_gemv, w4_gemv_gateup_silu and w4_add_rmsnorm (the residual add
+ * fused into the norm after o_proj, and into the final norm); from layer 1 on,
+ * while hidden <= 4096, the attention norm folded into the qkv projection
+ * (w4_gemv_residual for the down projection before it, w4_gemv_rmsnorm for
+ * qkv), otherwise w4_add_rmsnorm there too; and w4_attn_decode with the
+ * rotary embedding and KV append fused into its first kernel (q and the new
+ * token's k, v taken from the fp32 QKV output, cos/sin from a per-position
+ * table built at create).  Attention scale 1/sqrt(128).  Because
  * token and pos are read and advanced on the device, one call of
  * w4_decode_step per token continues the greedy decode with no host work;
  * use_graph != 0 captures the whole step as one HIP graph (one submission per
@@ -469,8 +527,8 @@ typedef struct w4_step w4_step;
  * must stay valid until destroy.  pos must stay below max_ctx (at max_ctx - 1
  * the last cache slot is overwritten).  The handle is not thread-safe.
  * Rules: shapes as for the individual calls; hidden, n_heads * 128, inter
- * multiples of G; W4_ESHAPE / W4_EINVAL / W4_EALIGN before anything is
- * allocated or launched.
+ * multiples of G; attn_norm 16-byte, mlp_norm and final_norm 8-byte aligned;
+ * W4_ESHAPE / W4_EINVAL / W4_EALIGN before anything is allocated or launched.
  */
 w4_status w4_decode_step_create(const w4_step_desc* desc, int32_t use_graph, w4_step** out);
 

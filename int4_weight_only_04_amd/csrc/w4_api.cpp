@@ -2,6 +2,7 @@
 // validation, error reporting, the host packer entry, single-GEMV launches
 // and the per-token sweep (eager launches or one captured HIP graph).
 #include <hip/hip_runtime_api.h>
+#include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -85,11 +86,29 @@ w4_status validate_gemv(const GemvCall& c, const char* who)
     const bool gateup = c.epi == kEpiGateUp;
     w4_status st = check_shape(c.n, c.k, c.group, gateup, who);
     if (st != W4_OK) return st;
-    if (!c.pw || !c.ps || !c.x || !c.out)
+    const void* in = c.norm_h ? static_cast<const void*>(c.norm_h) : c.x;
+    if (!c.pw || !c.ps || !in || !c.out)
         return fail(W4_EINVAL, "%s: null pointer (packed_w=%p packed_s=%p x=%p out=%p)", who, c.pw,
-                    c.ps, c.x, c.out);
-    if (!aligned16(c.pw) || !aligned16(c.ps) || !aligned16(c.x))
-        return fail(W4_EALIGN, "%s: packed_w, packed_s and x must be 16-byte aligned", who);
+                    c.ps, in, c.out);
+    if (!aligned16(c.pw) || !aligned16(c.ps) || !aligned16(in))
+        return fail(W4_EALIGN, "%s: packed_w, packed_s and x (or h) must be 16-byte aligned", who);
+    if (c.norm_h) {
+        if (c.xs) return fail(W4_EINVAL, "%s: the RMSNorm prologue takes fp16 activations only", who);
+        if (!c.norm_gamma || !c.norm_ss) return fail(W4_EINVAL, "%s: null gamma or ss_part", who);
+        if (!aligned16(c.norm_gamma) || !aligned16(c.norm_ss) || (c.x_out && !aligned16(c.x_out)))
+            return fail(W4_EALIGN, "%s: gamma, ss_part and x_out must be 16-byte aligned", who);
+        if (c.norm_parts < 1 || c.norm_parts > kMaxNormParts)
+            return fail(W4_ESHAPE, "%s: parts=%lld must be in [1, %lld]", who, (long long)c.norm_parts,
+                        (long long)kMaxNormParts);
+        if (!(c.norm_eps >= 0.0f) || !isfinite(c.norm_eps))
+            return fail(W4_EINVAL, "%s: eps=%g must be finite and >= 0", who, c.norm_eps);
+    }
+    if (c.h_out) {
+        if (c.epi != kEpiPlain) return fail(W4_EINVAL, "%s: the residual epilogue is for plain GEMVs", who);
+        if (!c.h_in || !c.ss_out) return fail(W4_EINVAL, "%s: null h_in or ss_part", who);
+        if (!aligned_to(c.h_in, 4) || !aligned_to(c.h_out, 4) || !aligned16(c.ss_out) || !aligned_to(c.out, 4))
+            return fail(W4_EALIGN, "%s: h_in, h_out and y must be 4-byte, ss_part 16-byte aligned", who);
+    }
     if (c.epi == kEpiArgmax) {
         if (!c.argmax || !c.ws)
             return fail(W4_EINVAL, "%s: argmax needs argmax and workspace pointers", who);
@@ -261,6 +280,93 @@ w4_status w4_gemv_gateup_silu(const void* packed_w, const void* packed_s, const 
         return ok();
     } catch (...) {
         return fail(W4_EINVAL, "w4_gemv_gateup_silu: internal exception");
+    }
+}
+
+w4_status w4_residual_parts(int64_t n, int64_t k, int32_t group, int64_t* parts)
+{
+    try {
+        if (!parts) return fail(W4_EINVAL, "w4_residual_parts: null output");
+        w4_status st = check_shape(n, k, group, false, "w4_residual_parts");
+        if (st != W4_OK) return st;
+        *parts = residual_parts(n, k, group);
+        return ok();
+    } catch (...) {
+        return fail(W4_EINVAL, "w4_residual_parts: internal exception");
+    }
+}
+
+w4_status w4_gemv_residual(const void* packed_w, const void* packed_s, const uint16_t* x, float* y,
+                           const float* h_in, float* h_out, float* ss_part, int64_t n, int64_t k, int32_t group,
+                           void* stream)
+{
+    try {
+        const char* who = "w4_gemv_residual";
+        if (!h_out) return fail(W4_EINVAL, "%s: null h_out", who);
+        GemvCall c{packed_w, packed_s, x, y, nullptr, nullptr, n, k, group, kEpiPlain};
+        c.h_in = h_in;
+        c.h_out = h_out;
+        c.ss_out = ss_part;
+        w4_status st = validate_gemv(c, who);
+        if (st != W4_OK) return st;
+        hipError_t err = launch_gemv(c, static_cast<hipStream_t>(stream));
+        if (err != hipSuccess) return hip_fail(err, "w4_gemv_residual launch");
+        return ok();
+    } catch (...) {
+        return fail(W4_EINVAL, "w4_gemv_residual: internal exception");
+    }
+}
+
+w4_status w4_gemv_rmsnorm(const void* packed_w, const void* packed_s, const float* h, const uint16_t* gamma,
+                          const float* ss_part, int64_t parts, float eps, uint16_t* x_out, float* y,
+                          int32_t* argmax, void* workspace, size_t workspace_bytes, int64_t n, int64_t k,
+                          int32_t group, void* stream)
+{
+    try {
+        const char* who = "w4_gemv_rmsnorm";
+        if (!h) return fail(W4_EINVAL, "%s: null h", who);
+        GemvCall c{packed_w, packed_s, nullptr, y, argmax, workspace, n, k, group, argmax ? kEpiArgmax : kEpiPlain};
+        c.norm_h = h;
+        c.norm_gamma = gamma;
+        c.norm_ss = ss_part;
+        c.norm_parts = parts;
+        c.norm_eps = eps;
+        c.x_out = x_out;
+        w4_status st = validate_gemv(c, who);
+        if (st != W4_OK) return st;
+        if (argmax && workspace_bytes < argmax_workspace_bytes(launch_grid(c)))
+            return fail(W4_EINVAL, "%s: workspace of %zu bytes, need %zu", who, workspace_bytes,
+                        argmax_workspace_bytes(launch_grid(c)));
+        hipError_t err = launch_gemv(c, static_cast<hipStream_t>(stream));
+        if (err != hipSuccess) return hip_fail(err, "w4_gemv_rmsnorm launch");
+        return ok();
+    } catch (...) {
+        return fail(W4_EINVAL, "w4_gemv_rmsnorm: internal exception");
+    }
+}
+
+w4_status w4_gemv_gateup_silu_rmsnorm(const void* packed_w, const void* packed_s, const float* h,
+                                      const uint16_t* gamma, const float* ss_part, int64_t parts, float eps,
+                                      uint16_t* x_out, uint16_t* h_mlp, int64_t n_total, int64_t k, int32_t group,
+                                      void* stream)
+{
+    try {
+        const char* who = "w4_gemv_gateup_silu_rmsnorm";
+        if (!h) return fail(W4_EINVAL, "%s: null h", who);
+        GemvCall c{packed_w, packed_s, nullptr, h_mlp, nullptr, nullptr, n_total, k, group, kEpiGateUp};
+        c.norm_h = h;
+        c.norm_gamma = gamma;
+        c.norm_ss = ss_part;
+        c.norm_parts = parts;
+        c.norm_eps = eps;
+        c.x_out = x_out;
+        w4_status st = validate_gemv(c, who);
+        if (st != W4_OK) return st;
+        hipError_t err = launch_gemv(c, static_cast<hipStream_t>(stream));
+        if (err != hipSuccess) return hip_fail(err, "w4_gemv_gateup_silu_rmsnorm launch");
+        return ok();
+    } catch (...) {
+        return fail(W4_EINVAL, "w4_gemv_gateup_silu_rmsnorm: internal exception");
     }
 }
 

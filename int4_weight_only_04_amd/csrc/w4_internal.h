@@ -31,7 +31,31 @@ struct GemvCall {
     int32_t group;
     int32_t epi;
     const float* xs;     // W4A8: x holds int8 codes (W4T4 block order), xs the per-group scales; null: fp16 x
+    // Residual epilogue (plain only; h_out non-null): h_out[i] = h_in[i] + y[i]
+    // for i < n (h_in may equal h_out), and ss_out[u] = sum of h_out^2 over the
+    // rows of unit u, for u < residual_parts(n, k, group).
+    const float* h_in;
+    float* h_out;
+    float* ss_out;
+    // RMSNorm prologue (norm_h non-null; x unused): the GEMV input is
+    // x = fp16(h * r * gamma) with r = 1 / sqrt(S / k + eps) and S the sum of
+    // norm_parts partial sums (<= kMaxNormParts, the buffer padded to a multiple
+    // of 4 floats); workgroup 0 also writes that x to x_out when non-null.
+    const float* norm_h;
+    const uint16_t* norm_gamma;
+    const float* norm_ss;
+    int64_t norm_parts;
+    float norm_eps;
+    uint16_t* x_out;
 };
+
+// The norm prologue reads its partial sums with four 16-byte loads per lane.
+constexpr int kNormPartLoads = 4;
+constexpr int64_t kMaxNormParts = 64 * 4 * kNormPartLoads;
+
+// Number of partial sums of squares the residual epilogue of a plain n x k
+// GEMV writes (one per unit of its launch shape).
+int64_t residual_parts(int64_t n, int64_t k, int32_t group);
 
 // Per-group int8 quantization of fp16 x for the W4A8 GEMV (codes in W4T4
 // block order, one fp32 scale per group).

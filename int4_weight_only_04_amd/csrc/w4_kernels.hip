@@ -68,7 +68,23 @@ struct KernelArgs {
     int32_t ng;          // k / G
     int32_t gshift;      // log2(G / 8)
     int32_t iters;       // ceil(kb / 64)
+    // residual epilogue (plain; h_out non-null): h_out = h_in + y, ss_out[unit] = sum of h_out^2 of the unit's rows
+    const float* h_in;
+    float* h_out;
+    float* ss_out;
+    // RMSNorm prologue (x mode kXNorm): x = fp16(h * r * gamma), r from the partial sums of squares
+    const float4* nh;    // h fp32 [k], two float4 per 8-input block
+    const uint4* ngamma; // gamma fp16 [k], one uint4 per 8-input block
+    const float4* nss;   // partial sums of squares, padded to whole float4
+    int32_t nparts;      // number of partial sums
+    float nk;            // k as fp32 (the mean's divisor)
+    float neps;
+    uint4* x_out;        // workgroup 0 writes the fp16 x it used (or null)
 };
+
+// Where a GEMV takes its input from: fp16 x, int8 codes with per-group scales
+// (W4A8), or fp32 h normalized on the fly (RMSNorm prologue).
+enum XMode : int { kXHalf = 0, kXCodes = 1, kXNorm = 2 };
 
 __device__ __forceinline__ h2_t as_h2(uint32_t v) { return __builtin_bit_cast(h2_t, v); }
 
@@ -197,42 +213,116 @@ __device__ __forceinline__ bool better(float v, int32_t i, float bv, int32_t bi)
     return v > bv || (v == bv && i < bi);
 }
 
+// RMSNorm prologue, step 1: lane l loads float4 l, l + 64, ... of the partial
+// sums of squares.  Indices past the last float4 are clamped to it (the buffer
+// is padded to whole float4, so every load is in bounds and unconditional);
+// reduce_parts masks what lies past nparts.
+__device__ __forceinline__ void load_parts(float4 (&pv)[kNormPartLoads], const float4* __restrict__ nss, int nparts,
+                                           int lane)
+{
+    const int last = ((nparts + 3) >> 2) - 1;
+#pragma unroll
+    for (int p = 0; p < kNormPartLoads; ++p) {
+        const int i = p * 64 + lane;
+        pv[p] = nss[i < last ? i : last];
+    }
+}
+
+// Step 2: r = 1 / sqrt(S / k + eps), S summed in a fixed order (each lane's 16
+// values in index order, then a butterfly across the wave, which leaves the
+// same sum in every lane), so every wave of every workgroup gets the same r.
+__device__ __forceinline__ float reduce_parts(const float4 (&pv)[kNormPartLoads], int nparts, int lane, float nk,
+                                              float eps)
+{
+    float t = 0.0f;
+#pragma unroll
+    for (int p = 0; p < kNormPartLoads; ++p) {
+        const int b = 4 * (p * 64 + lane);
+        t += b + 0 < nparts ? pv[p].x : 0.0f;
+        t += b + 1 < nparts ? pv[p].y : 0.0f;
+        t += b + 2 < nparts ? pv[p].z : 0.0f;
+        t += b + 3 < nparts ? pv[p].w : 0.0f;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) t += __shfl_xor(t, off);
+    return 1.0f / sqrtf(t / nk + eps);
+}
+
+__device__ __forceinline__ uint32_t half_pair(float a, float b)
+{
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
+}
+
+// Step 3: the 8 fp16 inputs of one block, x = fp16((h * r) * gamma).
+__device__ __forceinline__ uint4 normed_block(const float4& h0, const float4& h1, const uint4& g, float r)
+{
+    return make_uint4(half_pair(h0.x * r * half_lo(g.x), h0.y * r * half_hi(g.x)),
+                      half_pair(h0.z * r * half_lo(g.y), h0.w * r * half_hi(g.y)),
+                      half_pair(h1.x * r * half_lo(g.z), h1.y * r * half_hi(g.z)),
+                      half_pair(h1.z * r * half_lo(g.w), h1.w * r * half_hi(g.w)));
+}
+
 // Straight-line body for exactly C k iterations of one wave: all loads first
 // (weights and scales non-temporal, x through L1), then the math for each
 // iteration in order.  With no branches between the loads the compiler's
 // wait counters are exact, so iteration d waits only for its own three
 // loads and its math overlaps the loads still in flight (with branches it
 // falls back to waiting for every load before any math).
-template <int C, int U, bool A8>
+template <int C, int U, int XM>
 __device__ __forceinline__ void accumulate_exact(float (&acc)[U][4], const uint4* const (&wp)[U],
                                                  const uint2* const (&sp)[U], const bool (&tile_ok)[U],
-                                                 const uint4* __restrict__ x, const float* __restrict__ xs, int i0,
-                                                 int lane, int gshift, uint32_t magic)
+                                                 const KernelArgs& a, int i0, int lane, uint32_t magic, bool write_x)
 {
     uint4 w[C][U];
     uint2 s[C][U];
     uint4 xr[C];
     uint2 cr[C];
     float sx[C];
+    float4 hv[C][2];
+    uint4 gv[C];
+    float4 pv[kNormPartLoads];
+    // The callers branch between C = D and C = D - 1; the two bodies begin
+    // with the same loads, and the compiler would hoist those above the branch
+    // (keeping them live across it and reordering the waits).  An assembler
+    // comment that differs per C makes the bodies differ from the first
+    // instruction on.
+    asm volatile("; accumulate_exact %0 iterations" ::"n"(C));
+    // the norm's partial sums go first, so waiting for them does not wait
+    // for the weight stream issued after them
+    if constexpr (XM == kXNorm) load_parts(pv, a.nss, a.nparts, lane);
 #pragma unroll
     for (int d = 0; d < C; ++d) {
         const int j = (i0 + d) * 64 + lane;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             w[d][u] = ld_stream(wp[u] + j);
-            s[d][u] = ld_stream(sp[u] + (j >> gshift));
+            s[d][u] = ld_stream(sp[u] + (j >> a.gshift));
         }
-        if constexpr (A8) {
-            cr[d] = reinterpret_cast<const uint2*>(x)[j];
-            sx[d] = xs[j >> gshift];
+        if constexpr (XM == kXCodes) {
+            cr[d] = reinterpret_cast<const uint2*>(a.x)[j];
+            sx[d] = a.xs[j >> a.gshift];
+        } else if constexpr (XM == kXNorm) {
+            hv[d][0] = a.nh[2 * j];
+            hv[d][1] = a.nh[2 * j + 1];
+            gv[d] = a.ngamma[j];
         } else {
-            xr[d] = x[j];
+            xr[d] = a.x[j];
         }
+    }
+    float r = 0.0f;
+    if constexpr (XM == kXNorm) {
+        // keep every load above the reduction: it waits only for the partial
+        // sums, while the weight stream stays in flight
+        __builtin_amdgcn_sched_barrier(0);
+        r = reduce_parts(pv, a.nparts, lane, a.nk, a.neps);
     }
 #pragma unroll
     for (int d = 0; d < C; ++d) {
+        // iteration d's x from its own h and gamma loads only
+        if constexpr (XM == kXNorm) xr[d] = normed_block(hv[d][0], hv[d][1], gv[d], r);
         int n8 = 0;
-        if constexpr (A8) n8 = neg8_code_sum(cr[d]);
+        if constexpr (XM == kXCodes) n8 = neg8_code_sum(cr[d]);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             // a unit's missing second tile reads tile 0 (in bounds) with its
@@ -240,7 +330,7 @@ __device__ __forceinline__ void accumulate_exact(float (&acc)[U][4], const uint4
             // stays unconditional and in issue order)
             const uint32_t keep = 0u - (uint32_t)tile_ok[u];
             const uint2 sc = make_uint2(s[d][u].x & keep, s[d][u].y & keep);
-            if constexpr (A8) {
+            if constexpr (XM == kXCodes) {
                 acc[u][0] = __builtin_fmaf((float)idot8(w[d][u].x, cr[d], n8), half_lo(sc.x) * sx[d], acc[u][0]);
                 acc[u][1] = __builtin_fmaf((float)idot8(w[d][u].y, cr[d], n8), half_hi(sc.x) * sx[d], acc[u][1]);
                 acc[u][2] = __builtin_fmaf((float)idot8(w[d][u].z, cr[d], n8), half_lo(sc.y) * sx[d], acc[u][2]);
@@ -254,14 +344,21 @@ __device__ __forceinline__ void accumulate_exact(float (&acc)[U][4], const uint4
         }
         __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (XM == kXNorm) {
+        // after the math, so the branch does not split the load/math block
+        if (write_x) {
+#pragma unroll
+            for (int d = 0; d < C; ++d) a.x_out[(i0 + d) * 64 + lane] = xr[d];
+        }
+    }
 }
 
 constexpr int waves_for(int split) { return split < 4 ? 4 : split; }
 
 // U tiles per unit, epilogue EPI, SPLIT waves per unit, D iterations per load
-// round, FULL: k/8 is a multiple of 64 (no lane masking), A8: int8
-// activation codes with per-group scales instead of fp16 x.
-template <int U, int EPI, int SPLIT, int D, bool FULL, bool A8>
+// round, FULL: k/8 is a multiple of 64 (no lane masking), XM: where the input
+// comes from (fp16 x, int8 codes, or fp32 h through the RMSNorm prologue).
+template <int U, int EPI, int SPLIT, int D, bool FULL, int XM>
 __global__ void __launch_bounds__(waves_for(SPLIT) * 64) gemv_w4_kernel(KernelArgs a)
 {
     constexpr int WAVES = waves_for(SPLIT);
@@ -281,6 +378,8 @@ __global__ void __launch_bounds__(waves_for(SPLIT) * 64) gemv_w4_kernel(KernelAr
     const int it1 = (sub + 1) * a.iters / SPLIT;
     const bool writer = (lane & 15) == 0;   // one lane per reduced row
     const int row_in_tile = reduced_row(lane);
+    // workgroup 0's first slot covers every k iteration: it writes the normalized x
+    const bool write_x = XM == kXNorm && a.x_out != nullptr && blockIdx.x == 0 && slot == 0;
 
     // tiles of this unit (plain U == 2: tiles 2u and 2u+1, the second may be
     // past the end; gate/up: tile u and its up partner)
@@ -290,6 +389,21 @@ __global__ void __launch_bounds__(waves_for(SPLIT) * 64) gemv_w4_kernel(KernelAr
     for (int u = 0; u < U; ++u) {
         tile_of[u] = (EPI == kEpiGateUp) ? unit + u * a.tiles_half : unit * U + u;
         tile_ok[u] = live && (EPI == kEpiGateUp || tile_of[u] < a.tiles);
+    }
+
+    // residual epilogue: the owner wave fetches h_in of its rows up front (a
+    // clamped, in-bounds index; rows past n are masked at the end)
+    float hin[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) hin[u] = 0.0f;
+    if constexpr (EPI == kEpiPlain) {
+        if (a.h_out != nullptr && sub == 0) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t row = tile_of[u] * 4 + row_in_tile;
+                hin[u] = a.h_in[row < a.n ? row : a.n - 1];
+            }
+        }
     }
 
     float acc[U][4];
@@ -309,9 +423,9 @@ __global__ void __launch_bounds__(waves_for(SPLIT) * 64) gemv_w4_kernel(KernelAr
             sp[u] = a.ps + t * a.ng;
         }
         if (count == D)
-            accumulate_exact<D, U, A8>(acc, wp, sp, tile_ok, a.x, a.xs, it0, lane, a.gshift, magic);
+            accumulate_exact<D, U, XM>(acc, wp, sp, tile_ok, a, it0, lane, magic, write_x);
         else if constexpr (D > 1)
-            accumulate_exact<D - 1, U, A8>(acc, wp, sp, tile_ok, a.x, a.xs, it0, lane, a.gshift, magic);
+            accumulate_exact<D - 1, U, XM>(acc, wp, sp, tile_ok, a, it0, lane, magic, write_x);
     } else if (live) {
         const uint4* wp[U];
         const uint2* sp[U];
@@ -319,6 +433,14 @@ __global__ void __launch_bounds__(waves_for(SPLIT) * 64) gemv_w4_kernel(KernelAr
         for (int u = 0; u < U; ++u) {
             wp[u] = a.pw + tile_of[u] * a.kb;
             sp[u] = a.ps + tile_of[u] * a.ng;
+        }
+        float r = 0.0f;
+        if constexpr (XM == kXNorm) {
+            if (it0 < it1) {
+                float4 pv[kNormPartLoads];
+                load_parts(pv, a.nss, a.nparts, lane);
+                r = reduce_parts(pv, a.nparts, lane, a.nk, a.neps);
+            }
         }
         for (int i0 = it0; i0 < it1; i0 += D) {
             uint4 w[D][U];
@@ -340,9 +462,12 @@ __global__ void __launch_bounds__(waves_for(SPLIT) * 64) gemv_w4_kernel(KernelAr
                             s[d][u] = make_uint2(0, 0);
                         }
                     }
-                    if constexpr (A8) {
+                    if constexpr (XM == kXCodes) {
                         cr[d] = reinterpret_cast<const uint2*>(a.x)[j];
                         sx[d] = a.xs[j >> a.gshift];
+                    } else if constexpr (XM == kXNorm) {
+                        xr[d] = normed_block(a.nh[2 * j], a.nh[2 * j + 1], a.ngamma[j], r);
+                        if (write_x) a.x_out[j] = xr[d];
                     } else {
                         xr[d] = a.x[j];
                     }
@@ -352,7 +477,7 @@ __global__ void __launch_bounds__(waves_for(SPLIT) * 64) gemv_w4_kernel(KernelAr
             for (int d = 0; d < D; ++d) {
                 const int j = (i0 + d) * 64 + lane;
                 if ((i0 + d < it1) && (FULL || j < a.kb)) {
-                    if constexpr (A8) {
+                    if constexpr (XM == kXCodes) {
                         const int n8 = neg8_code_sum(cr[d]);
 #pragma unroll
                         for (int u = 0; u < U; ++u) {
@@ -421,6 +546,26 @@ __global__ void __launch_bounds__(waves_for(SPLIT) * 64) gemv_w4_kernel(KernelAr
                     bv = rv[u];
                     bi = (int32_t)row;
                 }
+            }
+        }
+        if constexpr (EPI == kEpiPlain) {
+            if (a.h_out != nullptr && owner) {
+                // h_out = h_in + y; the unit's sum of squares of h_out, its tile
+                // rows added as (r0 + r2) + (r1 + r3) (every lane of a 16-lane
+                // row holds that row's value), then its tiles in order
+                float ss = 0.0f;
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int64_t row = tile_of[u] * 4 + row_in_tile;
+                    const bool ok = row < a.n;
+                    const float hn = hin[u] + rv[u];
+                    if (ok && writer) a.h_out[row] = hn;
+                    float sq = ok ? hn * hn : 0.0f;
+                    sq += __shfl_xor(sq, 16);
+                    sq += __shfl_xor(sq, 32);
+                    ss += sq;
+                }
+                if (lane == 0) a.ss_out[unit] = ss;
             }
         }
         if constexpr (EPI == kEpiArgmax) {
@@ -515,17 +660,17 @@ argmax_finalize_kernel(const float* __restrict__ part_v, const int32_t* __restri
 
 // Instantiated (split, depth) pairs: depth is the number of k iterations a
 // wave loads per round before computing.
-template <int U, int EPI, bool A8>
+template <int U, int EPI, int XM>
 const void* pick(int split, int depth, bool full)
 {
 #define W4_CASE(S, D)                                                                         \
     if (split == S && depth == D)                                                             \
-        return full ? reinterpret_cast<const void*>(&gemv_w4_kernel<U, EPI, S, D, true, A8>) \
-                    : reinterpret_cast<const void*>(&gemv_w4_kernel<U, EPI, S, D, false, A8>);
+        return full ? reinterpret_cast<const void*>(&gemv_w4_kernel<U, EPI, S, D, true, XM>) \
+                    : reinterpret_cast<const void*>(&gemv_w4_kernel<U, EPI, S, D, false, XM>);
+    // split 1 happens only with a single k iteration (k <= 512), hence depth 2,
+    // for every unit size (tall matrices with short rows included)
+    W4_CASE(1, 2)
     if constexpr (U == 1 || EPI == kEpiGateUp) {
-        W4_CASE(1, 2)
-        W4_CASE(1, 4)
-        W4_CASE(1, 8)
         W4_CASE(4, 2)
         W4_CASE(4, 4)
         W4_CASE(4, 8)
@@ -540,16 +685,16 @@ const void* pick(int split, int depth, bool full)
     return nullptr;
 }
 
-template <bool A8>
+template <int XM>
 const void* pick_epi(int32_t epi, const LaunchConfig& cfg, bool full)
 {
-    if (epi == kEpiGateUp) return pick<2, kEpiGateUp, A8>(cfg.split, cfg.depth, full);
+    if (epi == kEpiGateUp) return pick<2, kEpiGateUp, XM>(cfg.split, cfg.depth, full);
     if (epi == kEpiPlain)
-        return cfg.tiles == 2 ? pick<2, kEpiPlain, A8>(cfg.split, cfg.depth, full)
-                              : pick<1, kEpiPlain, A8>(cfg.split, cfg.depth, full);
+        return cfg.tiles == 2 ? pick<2, kEpiPlain, XM>(cfg.split, cfg.depth, full)
+                              : pick<1, kEpiPlain, XM>(cfg.split, cfg.depth, full);
     if (epi == kEpiArgmax)
-        return cfg.tiles == 2 ? pick<2, kEpiArgmax, A8>(cfg.split, cfg.depth, full)
-                              : pick<1, kEpiArgmax, A8>(cfg.split, cfg.depth, full);
+        return cfg.tiles == 2 ? pick<2, kEpiArgmax, XM>(cfg.split, cfg.depth, full)
+                              : pick<1, kEpiArgmax, XM>(cfg.split, cfg.depth, full);
     return nullptr;
 }
 
@@ -582,7 +727,22 @@ Plan make_plan(const GemvCall& c)
     const LaunchConfig cfg = choose_config(c.epi, gateup ? a.tiles / 2 : a.tiles, a.iters);
     a.units = gateup ? a.tiles / 2 : (a.tiles + cfg.tiles - 1) / cfg.tiles;
     const bool full = (a.kb % 64) == 0;
-    p.fn = c.xs ? pick_epi<true>(c.epi, cfg, full) : pick_epi<false>(c.epi, cfg, full);
+    if (c.norm_h)
+        p.fn = pick_epi<kXNorm>(c.epi, cfg, full);
+    else if (c.xs)
+        p.fn = pick_epi<kXCodes>(c.epi, cfg, full);
+    else
+        p.fn = pick_epi<kXHalf>(c.epi, cfg, full);
+    a.h_in = c.h_in;
+    a.h_out = c.h_out;
+    a.ss_out = c.ss_out;
+    a.nh = reinterpret_cast<const float4*>(c.norm_h);
+    a.ngamma = reinterpret_cast<const uint4*>(c.norm_gamma);
+    a.nss = reinterpret_cast<const float4*>(c.norm_ss);
+    a.nparts = (int32_t)c.norm_parts;
+    a.nk = (float)c.k;
+    a.neps = c.norm_eps;
+    a.x_out = reinterpret_cast<uint4*>(c.x_out);
     const int waves = waves_for(cfg.split);
     const int slots = waves / cfg.split;
     p.threads = waves * 64;
@@ -600,6 +760,16 @@ Plan make_plan(const GemvCall& c)
 int64_t launch_grid(const GemvCall& c)
 {
     return make_plan(c).grid;
+}
+
+int64_t residual_parts(int64_t n, int64_t k, int32_t group)
+{
+    GemvCall c{};
+    c.n = n;
+    c.k = k;
+    c.group = group;
+    c.epi = kEpiPlain;
+    return make_plan(c).args.units;
 }
 
 hipError_t launch_gemv(const GemvCall& c, hipStream_t stream)

@@ -216,7 +216,7 @@ w4_status validate_step(const w4_step_desc& d)
         const w4_layer_desc& L = d.layer[l];
         if (!L.attn_norm || !L.mlp_norm || !L.k_cache || !L.v_cache)
             return fail(W4_EINVAL, "%s: layer %d: null norm or cache pointer", who, l);
-        if (!aligned_to(L.attn_norm, 8) || !aligned_to(L.mlp_norm, 8) || !aligned_to(L.k_cache, 2) ||
+        if (!aligned_to(L.attn_norm, 16) || !aligned_to(L.mlp_norm, 8) || !aligned_to(L.k_cache, 2) ||
             !aligned_to(L.v_cache, 2) || (L.qkv_bias && !aligned_to(L.qkv_bias, 4)))
             return fail(W4_EALIGN, "%s: layer %d: pointers must be aligned to their element size", who, l);
         const GemvCall calls[4] = {
@@ -266,7 +266,17 @@ w4_status w4_decode_step_create(const w4_step_desc* desc, int32_t use_graph, w4_
         const int64_t attn_dim = (int64_t)d.n_heads * 128;
         GemvCall lm{d.lm_w, d.lm_s, nullptr, d.logits, d.token, nullptr, d.vocab, d.hidden, d.group, kEpiArgmax};
         const size_t lm_ws_bytes = argmax_workspace_bytes(launch_grid(lm));
+        // The attention norm of layers 1.. is folded into their qkv projection
+        // (the down projection before it adds the residual and writes partial
+        // sums of squares) when those partials fit the norm prologue's one load
+        // round (hidden <= 4096).  The MLP and final norms stay separate
+        // kernels: folded into gate/up and lm_head they cost those kernels more
+        // (three times the input bytes per workgroup) than the norm kernel
+        // costs on its own.
+        const int64_t parts_down = residual_parts(d.hidden, d.inter, d.group);
+        const bool fuse_attn = d.layers > 1 && parts_down <= kMaxNormParts;
         float* h = static_cast<float*>(alloc((size_t)d.hidden * 4));
+        float* ss = fuse_attn ? static_cast<float*>(alloc((size_t)((parts_down + 3) & ~(int64_t)3) * 4)) : nullptr;
         float* y = static_cast<float*>(alloc((size_t)d.hidden * 4));
         uint16_t* x = static_cast<uint16_t*>(alloc((size_t)d.hidden * 2));
         float* qkv = static_cast<float*>(alloc((size_t)qkv_rows * 4));
@@ -277,7 +287,8 @@ w4_status w4_decode_step_create(const w4_step_desc* desc, int32_t use_graph, w4_
         void* lm_ws = alloc(lm_ws_bytes);
         void* attn_ws = alloc(attn_workspace_bytes(d.n_heads, d.max_ctx));
         float2* rope_cs = static_cast<float2*>(alloc((size_t)d.max_ctx * 64 * sizeof(float2)));
-        if (!h || !y || !x || !qkv || !q || !ao || !mh || !ctx || !lm_ws || !attn_ws || !rope_cs) {
+        if (!h || !y || !x || !qkv || !q || !ao || !mh || !ctx || !lm_ws || !attn_ws || !rope_cs ||
+            (fuse_attn && !ss)) {
             delete sp;
             return fail(W4_EHIP, "%s: hipMalloc of the step's activation buffers failed", who);
         }
@@ -292,6 +303,7 @@ w4_status w4_decode_step_create(const w4_step_desc* desc, int32_t use_graph, w4_
 
         const int64_t H = d.hidden;
         const float eps = d.rms_eps;
+
         const TraceLayout tl = trace_layout(d);
         uint8_t* trace = static_cast<uint8_t*>(d.trace);
         // Copy `bytes` from src into trace field f of record l (traced steps only).
@@ -304,8 +316,7 @@ w4_status w4_decode_step_create(const w4_step_desc* desc, int32_t use_graph, w4_
                              },
                              1, what});
         };
-        // layer 0's attention norm runs with the embedding lookup; every later
-        // norm adds the producing GEMV's output to the residual stream first
+        // layer 0's attention norm runs with the embedding lookup
         const uint16_t* g0 = d.layer[0].attn_norm;
         s.ops.push_back({[=](hipStream_t st_) {
                              return launch_embed_rmsnorm(d.embed, d.vocab, H, d.token, g0, eps, h, x, st_);
@@ -315,8 +326,21 @@ w4_status w4_decode_step_create(const w4_step_desc* desc, int32_t use_graph, w4_
         copy(0, W4_TRACE_X1, x, "trace x1");
         for (int32_t l = 0; l < d.layers; ++l) {
             const w4_layer_desc L = d.layer[l];
-            const GemvCall qkv_call{L.qkv_w, L.qkv_s, x, qkv, nullptr, nullptr, qkv_rows, H, d.group, kEpiPlain};
+            const bool qkv_normed = fuse_attn && l > 0;
+            GemvCall qkv_call{L.qkv_w, L.qkv_s, x, qkv, nullptr, nullptr, qkv_rows, H, d.group, kEpiPlain};
+            if (qkv_normed) {
+                // this layer's attention norm, from h and the down projection's
+                // partial sums; workgroup 0 writes the normalized x for the trace
+                qkv_call.x = nullptr;
+                qkv_call.norm_h = h;
+                qkv_call.norm_gamma = L.attn_norm;
+                qkv_call.norm_ss = ss;
+                qkv_call.norm_parts = parts_down;
+                qkv_call.norm_eps = eps;
+                qkv_call.x_out = x;
+            }
             s.ops.push_back({[=](hipStream_t st_) { return launch_gemv(qkv_call, st_); }, 1, "qkv"});
+            if (qkv_normed) copy(l, W4_TRACE_X1, x, "trace x1");
             copy(l, W4_TRACE_QKV, qkv, "trace qkv");
             // rotary embedding and the KV append run inside the attention's
             // first kernel (q, and the new token's k and v, from the fp32 QKV
@@ -346,14 +370,23 @@ w4_status w4_decode_step_create(const w4_step_desc* desc, int32_t use_graph, w4_
                                    d.group, kEpiGateUp};
             s.ops.push_back({[=](hipStream_t st_) { return launch_gemv(gu_call, st_); }, 1, "gate/up"});
             copy(l, W4_TRACE_M, mh, "trace m");
-            const uint16_t* g_next = l + 1 < d.layers ? d.layer[l + 1].attn_norm : d.final_norm;
-            const GemvCall dn_call{L.down_w, L.down_s, mh, y, nullptr, nullptr, H, d.inter, d.group, kEpiPlain};
+            GemvCall dn_call{L.down_w, L.down_s, mh, y, nullptr, nullptr, H, d.inter, d.group, kEpiPlain};
+            const bool next_normed = fuse_attn && l + 1 < d.layers;
+            if (next_normed) {
+                // h += y in place, with the partial sums of squares of the new h
+                dn_call.h_in = h;
+                dn_call.h_out = h;
+                dn_call.ss_out = ss;
+            }
             s.ops.push_back({[=](hipStream_t st_) { return launch_gemv(dn_call, st_); }, 1, "down"});
             copy(l, W4_TRACE_D, y, "trace d");
-            s.ops.push_back({[=](hipStream_t st_) { return launch_add_rmsnorm(h, y, g_next, H, eps, x, st_); },
-                             1, l + 1 < d.layers ? "attn norm" : "final norm"});
+            if (!next_normed) {
+                const uint16_t* g_next = l + 1 < d.layers ? d.layer[l + 1].attn_norm : d.final_norm;
+                s.ops.push_back({[=](hipStream_t st_) { return launch_add_rmsnorm(h, y, g_next, H, eps, x, st_); },
+                                 1, l + 1 < d.layers ? "attn norm" : "final norm"});
+            }
             copy(l + 1, W4_TRACE_H_IN, h, "trace h");
-            copy(l + 1, W4_TRACE_X1, x, "trace x1");
+            if (!next_normed) copy(l + 1, W4_TRACE_X1, x, "trace x1");
         }
         s.ops.push_back({[=](hipStream_t st_) { return launch_gemv(lm, st_); }, 2, "lm_head + argmax"});
         int32_t* pos = d.pos;

@@ -29,6 +29,7 @@ EXPORTED = (
     "w4_decode_step_create", "w4_decode_step", "w4_decode_step_launches", "w4_decode_step_destroy",
     "w4_decode_step_trace_layout",
     "w4_quantize_act8", "w4_gemv_a8", "w4_gemv_gateup_silu_a8", "w4_read_probe",
+    "w4_residual_parts", "w4_gemv_residual", "w4_gemv_rmsnorm", "w4_gemv_gateup_silu_rmsnorm",
 )
 
 TRACE_FIELDS = ("h_in", "x1", "qkv", "q", "attn", "o", "h_mid", "x2", "m", "d")
@@ -119,6 +120,14 @@ def lib():
     L.w4_gemv.argtypes = [vp, vp, vp, vp, vp, vp, sz, i64, i64, i32, vp]
     L.w4_gemv_gateup_silu.restype = i32
     L.w4_gemv_gateup_silu.argtypes = [vp, vp, vp, vp, i64, i64, i32, vp]
+    L.w4_residual_parts.restype = i32
+    L.w4_residual_parts.argtypes = [i64, i64, i32, ctypes.POINTER(i64)]
+    L.w4_gemv_residual.restype = i32
+    L.w4_gemv_residual.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, vp]
+    L.w4_gemv_rmsnorm.restype = i32
+    L.w4_gemv_rmsnorm.argtypes = [vp, vp, vp, vp, vp, i64, ctypes.c_float, vp, vp, vp, vp, sz, i64, i64, i32, vp]
+    L.w4_gemv_gateup_silu_rmsnorm.restype = i32
+    L.w4_gemv_gateup_silu_rmsnorm.argtypes = [vp, vp, vp, vp, vp, i64, ctypes.c_float, vp, vp, i64, i64, i32, vp]
     L.w4_gemm_workspace_size.restype = i32
     L.w4_gemm_workspace_size.argtypes = [i64, i64, i64, i32, ctypes.POINTER(sz)]
     L.w4_gemm.restype = i32
@@ -268,6 +277,65 @@ def gemv_gateup_silu(packed_w, packed_s, x, h, n_total: int, k: int, group: int,
                                      _dev_ptr(x, "x", torch.float16, k),
                                      _dev_ptr(h, "h", torch.float16, n_total // 2),
                                      n_total, k, group, _stream(stream)), "w4_gemv_gateup_silu")
+
+
+def residual_parts(n: int, k: int, group: int) -> int:
+    """Partial sums of squares gemv_residual writes for an n x k projection."""
+    out = ctypes.c_int64()
+    _check(lib().w4_residual_parts(n, k, group, ctypes.byref(out)), "w4_residual_parts")
+    return out.value
+
+
+def gemv_residual(packed_w, packed_s, x, y, h_in, h_out, ss_part, n: int, k: int, group: int, stream=None):
+    """y = W x, h_out = h_in + y (fp32, h_out may be h_in) and the partial
+    sums of squares of h_out (ss_part: fp32, residual_parts floats)."""
+    import torch
+    wb, sb = packed_size(n, k, group, "plain")
+    _check(lib().w4_gemv_residual(_dev_ptr(packed_w, "packed_w", torch.uint8, wb),
+                                  _dev_ptr(packed_s, "packed_s", torch.uint8, sb),
+                                  _dev_ptr(x, "x", torch.float16, k),
+                                  _dev_ptr(y, "y", torch.float32, n),
+                                  _dev_ptr(h_in, "h_in", torch.float32, n),
+                                  _dev_ptr(h_out, "h_out", torch.float32, n),
+                                  _dev_ptr(ss_part, "ss_part", torch.float32, residual_parts(n, k, group)),
+                                  n, k, group, _stream(stream)), "w4_gemv_residual")
+
+
+def _norm_args(h, gamma, ss_part, parts: int, eps: float, x_out, k: int):
+    import torch
+    return (_dev_ptr(h, "h", torch.float32, k), _dev_ptr(gamma, "gamma", torch.float16, k),
+            _dev_ptr(ss_part, "ss_part", torch.float32, (parts + 3) // 4 * 4), parts, float(eps),
+            _dev_ptr(x_out, "x_out", torch.float16, k))
+
+
+def gemv_rmsnorm(packed_w, packed_s, h, gamma, ss_part, parts: int, eps: float, y, n: int, k: int, group: int,
+                 x_out=None, argmax=None, workspace=None, stream=None):
+    """y = W x with x = fp16(h * gamma / sqrt(sum(ss_part[:parts]) / k + eps))
+    (ss_part padded to a multiple of 4 floats); x_out receives that x."""
+    import torch
+    wb, sb = packed_size(n, k, group, "plain")
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if argmax is not None and ws_bytes < gemv_workspace_size(n, k, group, True):
+        raise ValueError("workspace too small for the argmax epilogue")
+    _check(lib().w4_gemv_rmsnorm(_dev_ptr(packed_w, "packed_w", torch.uint8, wb),
+                                 _dev_ptr(packed_s, "packed_s", torch.uint8, sb),
+                                 *_norm_args(h, gamma, ss_part, parts, eps, x_out, k),
+                                 _dev_ptr(y, "y", torch.float32, n),
+                                 _dev_ptr(argmax, "argmax", torch.int32, 1),
+                                 _dev_ptr(workspace, "workspace"), ws_bytes, n, k, group,
+                                 _stream(stream)), "w4_gemv_rmsnorm")
+
+
+def gemv_gateup_silu_rmsnorm(packed_w, packed_s, h, gamma, ss_part, parts: int, eps: float, h_mlp, n_total: int,
+                             k: int, group: int, x_out=None, stream=None):
+    """gemv_gateup_silu with its input normalized as in gemv_rmsnorm."""
+    import torch
+    wb, sb = packed_size(n_total, k, group, "gateup")
+    _check(lib().w4_gemv_gateup_silu_rmsnorm(_dev_ptr(packed_w, "packed_w", torch.uint8, wb),
+                                             _dev_ptr(packed_s, "packed_s", torch.uint8, sb),
+                                             *_norm_args(h, gamma, ss_part, parts, eps, x_out, k),
+                                             _dev_ptr(h_mlp, "h_mlp", torch.float16, n_total // 2),
+                                             n_total, k, group, _stream(stream)), "w4_gemv_gateup_silu_rmsnorm")
 
 
 def read_probe(buf, nbytes: int, sink, stream=None):

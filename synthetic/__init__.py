@@ -204,3 +204,8 @@ def half_bits_uniform(seed: int, count: int, lo_exp: int = 14) -> np.ndarray:
     i.e. [0.5, 1) by default)."""
     raw = _rng(seed).bit_generator.random_raw((count + 3) // 4).view(np.uint16)[:count]
     return (raw & np.uint16(0x83FF)) | np.uint16(lo_exp << 10)
+
+
+def residual(seed: int, n: int, scale: float = 4.0) -> np.ndarray:
+    """A residual-stream vector: N(0, scale^2) drawn in float32."""
+    return (_rng(seed).standard_normal(n, dtype=np.float32) * np.float32(scale)).astype(np.float32)

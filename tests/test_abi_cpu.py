@@ -290,6 +290,45 @@ def test_w4a8_validation_before_launch():
     assert L.w4_gemv_gateup_silu_a8(A, A, A, None, A, 8, 64, 32, None) == w4.EINVAL
 
 
+def test_fused_norm_validation_before_launch():
+    """The residual and norm-prologue GEMVs reject bad calls on the host."""
+    L = w4.lib()
+    A = 1 << 20
+    f = ctypes.c_float
+    assert L.w4_gemv_residual(A, A, A, A, A, None, A, 64, 256, 64, None) == w4.EINVAL        # null h_out
+    assert L.w4_gemv_residual(A, A, A, A, None, A, A, 64, 256, 64, None) == w4.EINVAL        # null h_in
+    assert L.w4_gemv_residual(A, A, A, A, A, A, None, 64, 256, 64, None) == w4.EINVAL        # null ss_part
+    assert L.w4_gemv_residual(A, A, A, A, A, A, A + 4, 64, 256, 64, None) == w4.EALIGN       # ss_part 16-byte
+    assert L.w4_gemv_residual(A, A, A, A, A + 2, A, A, 64, 256, 64, None) == w4.EALIGN       # h_in 4-byte
+    assert L.w4_gemv_residual(A, A, A, A, A, A, A, 64, 250, 64, None) == w4.ESHAPE           # k % G
+    args = lambda **kw: [kw.get(k, v) for k, v in (
+        ("w", A), ("s", A), ("h", A), ("g", A), ("ss", A), ("parts", 4), ("eps", f(1e-6)), ("xo", None), ("y", A),
+        ("am", None), ("ws", None), ("wsb", 0), ("n", 64), ("k", 256), ("group", 64), ("st", None))]
+    assert L.w4_gemv_rmsnorm(*args(h=None)) == w4.EINVAL
+    assert L.w4_gemv_rmsnorm(*args(g=None)) == w4.EINVAL
+    assert L.w4_gemv_rmsnorm(*args(ss=None)) == w4.EINVAL
+    assert L.w4_gemv_rmsnorm(*args(parts=0)) == w4.ESHAPE
+    assert L.w4_gemv_rmsnorm(*args(parts=1025)) == w4.ESHAPE
+    assert L.w4_gemv_rmsnorm(*args(eps=f(-1.0))) == w4.EINVAL
+    assert L.w4_gemv_rmsnorm(*args(eps=f(float("inf")))) == w4.EINVAL
+    assert L.w4_gemv_rmsnorm(*args(h=A + 4)) == w4.EALIGN
+    assert L.w4_gemv_rmsnorm(*args(g=A + 8)) == w4.EALIGN
+    assert L.w4_gemv_rmsnorm(*args(ss=A + 4)) == w4.EALIGN
+    assert L.w4_gemv_rmsnorm(*args(xo=A + 8)) == w4.EALIGN
+    assert L.w4_gemv_rmsnorm(*args(am=A, ws=A, wsb=16)) == w4.EINVAL   # argmax workspace too small
+    assert L.w4_gemv_gateup_silu_rmsnorm(A, A, A, A, A, 4, f(1e-6), None, A, 63, 256, 64, None) == w4.ESHAPE
+    assert L.w4_gemv_gateup_silu_rmsnorm(A, A, A, A, A, 2000, f(1e-6), None, A, 64, 256, 64, None) == w4.ESHAPE
+    assert L.w4_gemv_gateup_silu_rmsnorm(A, A, None, A, A, 4, f(1e-6), None, A, 64, 256, 64, None) == w4.EINVAL
+
+
+@pytest.mark.parametrize("n,k,group,parts", [(3584, 3584, 128, 896), (3584, 18944, 128, 896), (37, 96, 32, 10),
+                                             (65536, 256, 64, 8192), (65540, 256, 64, 8193)])
+def test_residual_parts(n, k, group, parts):
+    """One partial per 4-row tile, or per pair of tiles once the matrix has
+    16384 tiles or more (the launch's two-tile units)."""
+    assert w4.residual_parts(n, k, group) == parts
+
+
 def _step_desc(layers_arr, **kw):
     A = 1 << 20
     d = w4.StepDesc()
@@ -346,6 +385,15 @@ def test_decode_step_create_validation():
     bad = _layer_arr(2)
     bad[1].gateup_w = (1 << 20) + 8
     assert create(_step_desc(bad)) == w4.EALIGN
+    bad = _layer_arr(2)
+    bad[1].attn_norm = (1 << 20) + 8         # read 16 bytes at a time by the qkv norm prologue
+    assert create(_step_desc(bad)) == w4.EALIGN
+    bad = _layer_arr(2)
+    bad[1].mlp_norm = (1 << 20) + 4
+    assert create(_step_desc(bad)) == w4.EALIGN
+    d = _step_desc(arr)
+    d.final_norm = (1 << 20) + 4
+    assert create(d) == w4.EALIGN
     assert not handle.value
     assert L.w4_decode_step(None, None) == w4.EINVAL
     assert L.w4_decode_step_destroy(None) == w4.OK

@@ -244,6 +244,20 @@ def test_lmhead_config():
         assert idx == oracle.argmax(y_ref)
 
 
+@pytest.mark.parametrize("n,k", [(65536, 256), (70001, 512), (65540, 8)])
+def test_tall_matrix_short_rows(n, k):
+    """16384 tiles or more run two tiles per unit; with k <= 512 there is one
+    k iteration and a single wave per unit (a launch shape of its own), with
+    and without the argmax epilogue."""
+    group = 8 if k == 8 else 64
+    q, s, x = synthetic.logical(n + k, n, k, group)
+    check_plain(run_plain(q, s, x, group), q, s, x, group)
+    y, idx, _ = run_plain(q, s, x, group, argmax=True)
+    y_ref, a_ref = check_plain(y, q, s, x, group)
+    assert idx == oracle.argmax(y)
+    assert idx in near_tie_set(y_ref, a_ref)
+
+
 def test_argmax_planted_and_ties():
     n, k, group = 4099, 256, 64
     q, s, x = synthetic.logical(55, n, k, group)

@@ -59,10 +59,12 @@ def _host16(t):
 
 
 def tol_rmsnorm(x_ref, n):
-    # t bounds the additions any square passes through in the fp32 sum of
-    # squares of both norm kernels (per-thread terms, 6 shuffle levels, the
-    # cross-wave sum): the single-workgroup kernel has ceil(n/1024) + 21, the
-    # GEMV's last-workgroup tail at most n/64 + 17
+    # t bounds the fp32 roundings any square passes through on its way into
+    # the sum of squares: the single-workgroup norm kernel has ceil(n/1024) +
+    # 21 (per-thread terms, 6 shuffle levels, the cross-wave sum); the norm
+    # folded into the qkv projection has the square, 3 additions in the down
+    # projection's part (up to 8 rows), 15 per-lane additions of the parts and
+    # 6 shuffle levels, i.e. 25
     t = n / 64 + 32
     return (2.0 ** -11 + (t / 2 + 8) * U) * np.abs(x_ref) + 2.0 ** -25
 
@@ -329,10 +331,12 @@ def test_step_teacher_forced_small(use_graph):
     growing), each checked stage by stage."""
     model = Model(21, bias=True, **SMALL)
     st = model.step(use_graph)
-    # 8 kernels per layer (qkv, rotary + append + attention x2, o_proj, norm,
-    # gate/up, down, norm) + embedding with the first norm, lm_head (2) and
-    # advance; the trace adds 10 copies per layer and 2 for the first record
-    assert st.launches() == 8 * 3 + 4 + 10 * 3 + 2
+    # 7 kernels per layer (qkv with the attention norm folded in from layer 1
+    # on, rotary + append + attention x2, o_proj, residual add + MLP norm,
+    # gate/up, down with the residual add) + embedding with the first norm, the
+    # last down's residual add + final norm, lm_head (2) and advance; the trace
+    # adds 10 copies per layer and 2 for the first record
+    assert st.launches() == 7 * 3 + 5 + 10 * 3 + 2
     model.token.fill_(5)
     model.pos.fill_(37)
     torch.cuda.synchronize()
@@ -399,6 +403,26 @@ def test_step_fused_attention_edges(n_heads, n_kv, page, max_ctx, start):
     model.pos.fill_(start)
     torch.cuda.synchronize()
     for _ in range(max_ctx - start):
+        token, pos = int(model.token.item()), int(model.pos.item())
+        before = model.caches()
+        st.run()
+        torch.cuda.synchronize()
+        check_step(model, st, token, pos, before)
+
+
+def test_step_separate_norms_above_4096():
+    """Hidden 4224 (33 heads over 11 KV heads): the partial sums of squares
+    would exceed the norm prologue's 1024, so the step runs a separate residual
+    + RMSNorm kernel before every qkv (8 kernels per layer); teacher-forced
+    like the rest."""
+    cfg = dict(hidden=4224, n_heads=33, n_kv=11, inter=256, vocab=500, group=64, layers=2, page=16, max_ctx=64)
+    model = Model(88, bias=True, **cfg)
+    st = model.step(True)
+    assert st.launches() == 8 * 2 + 4 + 10 * 2 + 2
+    model.token.fill_(7)
+    model.pos.fill_(30)
+    torch.cuda.synchronize()
+    for _ in range(2):
         token, pos = int(model.token.item()), int(model.pos.item())
         before = model.caches()
         st.run()
