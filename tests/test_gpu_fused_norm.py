@@ -113,7 +113,7 @@ def test_gemv_residual_vs_oracle(seed, n, k, group, in_place):
 
 PLAIN_NORM = [  # seed, n, k, group, rows per given part
     (1, 5, 512, 64, 512), (2, 37, 96, 32, 7), (3, 130, 448, 64, 4), (4, 4608, 3584, 128, 4),
-    (5, 200, 4096, 128, 4), (6, 3, 3584, 128, 4), (7, 260, 1024, 64, 1)]
+    (5, 200, 4096, 128, 4), (6, 3, 3584, 128, 4), (7, 260, 1024, 64, 1), (8, 8, 32768, 128, 32)]
 
 
 @pytest.mark.parametrize("seed,n,k,group,rows", PLAIN_NORM)
