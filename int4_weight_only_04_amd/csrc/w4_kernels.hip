@@ -4,8 +4,8 @@
 // aitrending.vip, "Technical Details" bullet 1: INT4 weights dequantized at
 // run time; noticiai.com.br, "As tres licoes" lesson 3: activations stay
 // floating point): y[n] = sum_k (q[n][k] - 8) * s[n][k/G] * x[k], with fp16
-// x and s, exact dequantization and fp32 accumulation, plus two fused
-// epilogues (SiLU-gated gate/up, lm_head argmax).
+// x and s, exact dequantization and fp32 accumulation, plus fused epilogues
+// (SiLU-gated gate/up, lm_head argmax, residual add) and an RMSNorm prologue.
 //
 // Design (one GEMV is a pure HBM stream: 0.52 bytes per weight against 2
 // flops, far below the chip's ridge point, so the kernel is shaped for
@@ -42,6 +42,14 @@
 //     workspace with plain stores and a one-workgroup second kernel reduces
 //     them in index order.  The kernel boundary orders the two, so there are
 //     no device-scope fences or atomics on the hot path.
+//   * Decode-step forms: the residual epilogue adds y into the fp32 residual
+//     stream and writes one sum of squares of the new rows per unit; the
+//     RMSNorm prologue (x mode kXNorm) takes h, gamma and those sums instead
+//     of x.  Every wave sums the partials in one fixed order, so every
+//     workgroup forms the same x = fp16((h * r) * gamma); the partials are
+//     loaded before the weights, and each iteration's x is made from its own
+//     h and gamma loads, so the weight stream is not held up.  The kernel
+//     boundary between producer and consumer orders the partial sums.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

@@ -303,7 +303,6 @@ w4_status w4_decode_step_create(const w4_step_desc* desc, int32_t use_graph, w4_
 
         const int64_t H = d.hidden;
         const float eps = d.rms_eps;
-
         const TraceLayout tl = trace_layout(d);
         uint8_t* trace = static_cast<uint8_t*>(d.trace);
         // Copy `bytes` from src into trace field f of record l (traced steps only).
