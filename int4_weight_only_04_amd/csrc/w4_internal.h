@@ -79,9 +79,11 @@ struct GemmCall {
 
 hipError_t launch_gemm(const GemmCall& call, hipStream_t stream);
 
-// Output tile of the prefill GEMM: 128 x 128, or 64 x 128 while 128-row
-// tiles would give fewer than two workgroups per CU of the 256.  Gate/up
-// tiles hold 64 gate rows and the matching 64 up rows.
+// Output tile of the prefill GEMM: 128 x 128 when the block has at least
+// 256 token rows or the 128-row tiles alone give two workgroups per CU of the
+// 256; 64 x 128 otherwise.  A 128 x 128 tile reads 2/3 of the LDS bytes per
+// flop of a 64 x 128 one (each wave multiplies 64 x 64 instead of 32 x 64).
+// Gate/up tiles hold 64 gate rows and the matching 64 up rows.
 struct GemmShape {
     int bm;
     int bn;
@@ -92,14 +94,15 @@ inline GemmShape choose_gemm_shape(int32_t epi, int64_t m, int64_t n)
     const int64_t cols = epi == kEpiGateUp ? n / 2 : n;
     const int64_t per_tile = epi == kEpiGateUp ? 64 : 128;
     const int64_t tiles128 = ((m + 127) / 128) * ((cols + per_tile - 1) / per_tile);
-    return tiles128 >= 512 ? GemmShape{128, 128} : GemmShape{64, 128};
+    return (m >= 256 || tiles128 >= 512) ? GemmShape{128, 128} : GemmShape{64, 128};
 }
 
-// Split-k factor: when the output tiles give fewer than 256 workgroups (one
-// per CU), the k range is split so the grid covers the chip, at most 8 ways
-// and at least one 64-input step per split; the partials are summed in a
-// fixed order by a second kernel.  Gate/up is never split (its SiLU needs the
-// full sums).
+// Split-k factor: when the output tiles give fewer than 256 workgroups, the k
+// range is split so the grid covers the chip in one round: for 128-row tiles
+// (two workgroups per CU) as many splits as fit in 512 workgroups, for 64-row
+// tiles enough to reach 256; at most 8 ways and at least one 64-input step per
+// split.  The partials are summed in a fixed order by a second kernel.
+// Gate/up is never split (its SiLU needs the full sums).
 inline int32_t gemm_splits(int32_t epi, int64_t m, int64_t n, int64_t k)
 {
     if (epi == kEpiGateUp) return 1;
@@ -107,7 +110,7 @@ inline int32_t gemm_splits(int32_t epi, int64_t m, int64_t n, int64_t k)
     const int64_t wgs = ((n + sh.bn - 1) / sh.bn) * ((m + sh.bm - 1) / sh.bm);
     if (wgs >= 256) return 1;
     const int64_t steps = (k / 8 + 7) / 8;
-    int64_t s = (256 + wgs - 1) / wgs;
+    int64_t s = sh.bm == 128 ? 512 / wgs : (256 + wgs - 1) / wgs;
     if (s > 8) s = 8;
     if (s > steps) s = steps;
     return (int32_t)(s < 1 ? 1 : s);

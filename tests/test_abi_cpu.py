@@ -176,10 +176,14 @@ def test_gemm_validation_before_launch():
 
 
 def test_gemm_workspace_sizes():
-    # split-k partials: splits x m x n fp32; no split once the grid covers the chip
-    assert w4.gemm_workspace_size(512, 4608, 3584, 128) == 0            # 288 tiles of 64 x 128
-    assert w4.gemm_workspace_size(512, 3584, 18944, 128) == 2 * 512 * 3584 * 4
-    assert w4.gemm_workspace_size(4096, 37888, 3584, 128) == 0
+    # split-k partials: splits x m x n fp32; no split once the grid covers the chip.
+    # From 256 token rows the tiles are 128 x 128, split to fit 512 workgroups:
+    assert w4.gemm_workspace_size(512, 4608, 3584, 128) == 3 * 512 * 4608 * 4    # 144 tiles, 3 splits
+    assert w4.gemm_workspace_size(512, 3584, 18944, 128) == 4 * 512 * 3584 * 4   # 112 tiles, 4 splits
+    assert w4.gemm_workspace_size(512, 3584, 3584, 128) == 4 * 512 * 3584 * 4
+    assert w4.gemm_workspace_size(4096, 37888, 3584, 128) == 0                   # 9472 tiles
+    # below 256 rows, 64 x 128 tiles split to reach 256 workgroups: 112 tiles, 3 splits
+    assert w4.gemm_workspace_size(200, 3584, 3584, 128) == 3 * 200 * 3584 * 4
     assert w4.gemm_workspace_size(1, 64, 64, 64) == 0  # one k step: nothing to split
 
 

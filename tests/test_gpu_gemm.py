@@ -61,7 +61,9 @@ def _logical(seed, m, n, k, group, s_lo=0.001, s_hi=0.02):
 
 # (m, n, k, group): several tiles in every direction and ragged tails in each:
 # m vs the 64/128-row tiles, n vs the 4-row packing tiles and the 64/128-column
-# tiles, k vs the 64-input k steps (k = 200: 25 blocks of 8, G = 8).
+# tiles, k vs the 64-input k steps (k = 200: 25 blocks of 8, G = 8); from 256
+# token rows on the tiles are 128 rows, split over k to fill 512 workgroups
+# (300 x 200 x 992: 6 tiles, 8 splits over 15.5 k steps).
 PLAIN_SHAPES = [
     (5, 512, 256, 64),
     (1, 37, 96, 32),
@@ -70,6 +72,7 @@ PLAIN_SHAPES = [
     (200, 130, 200, 8),
     (129, 260, 576, 64),
     (257, 1030, 320, 32),
+    (300, 200, 992, 32),
 ]
 
 
