@@ -80,25 +80,29 @@ __device__ __forceinline__ u32x4_t dequant_word(uint32_t d, uint32_t s2)
 //
 // Pipeline: the global loads of k step s+RING go out while step s is
 // computed (a ring of RING register slots, the loop unrolled by RING so every
-// slot index is a constant), and the LDS tiles are double-buffered, so one
-// barrier per k step separates a step's LDS writes from its MFMA reads.  With
-// 128-row tiles a 2-slot ring keeps a wave within 256 registers, so two
-// workgroups share a CU and hide each other's waits.  Loads are never
+// slot index is a constant).  With NBUF = 2 the LDS tiles are double-buffered,
+// so one barrier per k step separates a step's LDS writes from its MFMA reads,
+// and two 128-row workgroups share a CU.  With NBUF = 1 a second barrier per
+// step keeps the next step's writes behind the current step's reads; the
+// halved LDS and a 2-slot ring (within 168 registers) let three workgroups
+// share a CU, which the gate/up shape (1184 workgroups, 1.5 rounds of 768
+// instead of 2.3 rounds of 512) turns into a shorter kernel.  Loads are never
 // predicated: past-the-end addresses are clamped in bounds and the values
 // masked when stored to LDS (k tail: x and the scale zeroed, so the weight is
 // 0; rows past m are read from the last row and never written out).
-template <int BM, int BN, int EPI, int RING>
-__global__ void __launch_bounds__(kThreads, 2) gemm_w4_kernel(GemmArgs a)
+template <int BM, int BN, int EPI, int RING, int NBUF>
+__global__ void __launch_bounds__(kThreads, NBUF == 2 ? 2 : 3) gemm_w4_kernel(GemmArgs a)
 {
     constexpr int kRing = RING;
     static_assert(RING % 2 == 0, "consecutive k steps alternate LDS buffers by slot parity");
+    static_assert(NBUF == 1 || NBUF == 2, "one or two LDS buffers");
     constexpr int MB = BM / 64;
     constexpr int NB = BN / 64;
     constexpr int XCHUNKS = BM * 8 / kThreads;          // 16-B chunks of X per thread per step
     constexpr int WITEMS = BN / 4 * 8;                   // (tile, block) items of W per step
     static_assert(BN == 128 && WITEMS == kThreads, "one W item per thread");
-    __shared__ __attribute__((aligned(16))) _Float16 xs[2][BM * kRowHalves];
-    __shared__ __attribute__((aligned(16))) _Float16 wsm[2][BN * kRowHalves];
+    __shared__ __attribute__((aligned(16))) _Float16 xs[NBUF][BM * kRowHalves];
+    __shared__ __attribute__((aligned(16))) _Float16 wsm[NBUF][BN * kRowHalves];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -230,19 +234,21 @@ __global__ void __launch_bounds__(kThreads, 2) gemm_w4_kernel(GemmArgs a)
             // keep each step's work in place: hoisting a later slot's dequant
             // above this point would make it wait for that slot's loads
             __builtin_amdgcn_sched_barrier(0);
-            lstore(ring[u], s_begin + base + u, u & 1);
+            if constexpr (NBUF == 1) __syncthreads();  // the previous step's reads are done
+            lstore(ring[u], s_begin + base + u, (u & 1) % NBUF);
             issue(ring[u], s_begin + base + u + kRing);
             __syncthreads();
-            mfma_step(u & 1);
+            mfma_step((u & 1) % NBUF);
         }
     }
     // the last nsteps % kRing steps (their slots are the first ones of the ring)
 #pragma unroll
     for (int u = 0; u < kRing - 1; ++u) {
         if (whole + u < nsteps) {
-            lstore(ring[u], s_begin + whole + u, u & 1);
+            if constexpr (NBUF == 1) __syncthreads();
+            lstore(ring[u], s_begin + whole + u, (u & 1) % NBUF);
             __syncthreads();
-            mfma_step(u & 1);
+            mfma_step((u & 1) % NBUF);
         }
     }
 
@@ -320,11 +326,11 @@ GemmPlan make_gemm_plan(const GemmCall& c)
     p.grid = dim3((unsigned)((cols + per_tile - 1) / per_tile), (unsigned)((c.m + sh.bm - 1) / sh.bm),
                   (unsigned)a.splits);
     if (gateup)
-        p.fn = sh.bm == 128 ? reinterpret_cast<const void*>(&gemm_w4_kernel<128, 128, kEpiGateUp, 2>)
-                            : reinterpret_cast<const void*>(&gemm_w4_kernel<64, 128, kEpiGateUp, 4>);
+        p.fn = sh.bm == 128 ? reinterpret_cast<const void*>(&gemm_w4_kernel<128, 128, kEpiGateUp, 2, 1>)
+                            : reinterpret_cast<const void*>(&gemm_w4_kernel<64, 128, kEpiGateUp, 4, 2>);
     else
-        p.fn = sh.bm == 128 ? reinterpret_cast<const void*>(&gemm_w4_kernel<128, 128, kEpiPlain, 2>)
-                            : reinterpret_cast<const void*>(&gemm_w4_kernel<64, 128, kEpiPlain, 4>);
+        p.fn = sh.bm == 128 ? reinterpret_cast<const void*>(&gemm_w4_kernel<128, 128, kEpiPlain, 2, 2>)
+                            : reinterpret_cast<const void*>(&gemm_w4_kernel<64, 128, kEpiPlain, 4, 2>);
     return p;
 }
 
