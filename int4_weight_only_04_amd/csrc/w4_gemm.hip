@@ -205,22 +205,45 @@ __global__ void __launch_bounds__(kThreads, NBUF == 2 ? 2 : 3) gemm_w4_kernel(Ge
             brow[j] = wn * (BN / 2) + j * 32 + (lane & 31);
     }
     const int kofs = 8 * (lane >> 5);
+    // One k step of 64 inputs: four MFMA rounds of 16 inputs.  The operands of
+    // round kk + 1 are read from LDS into the second register set while round
+    // kk's MFMAs run (issued one read after each MFMA), and the wave raises its
+    // priority for the step so that a SIMD's waves issue their MFMAs ahead of
+    // the other waves' dequantization and LDS writes.
     auto mfma_step = [&](int b) {
+        constexpr int KK = kStepK / 16;
+        h8_t av[2][MB], bv[2][NB];
 #pragma unroll
-        for (int kk = 0; kk < kStepK / 16; ++kk) {
-            h8_t av[MB], bv[NB];
+        for (int i = 0; i < MB; ++i) av[0][i] = *reinterpret_cast<const h8_t*>(&xs[b][arow[i] * kRowHalves + kofs]);
 #pragma unroll
-            for (int i = 0; i < MB; ++i)
-                av[i] = *reinterpret_cast<const h8_t*>(&xs[b][arow[i] * kRowHalves + kk * 16 + kofs]);
+        for (int j = 0; j < NB; ++j) bv[0][j] = *reinterpret_cast<const h8_t*>(&wsm[b][brow[j] * kRowHalves + kofs]);
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-            for (int j = 0; j < NB; ++j)
-                bv[j] = *reinterpret_cast<const h8_t*>(&wsm[b][brow[j] * kRowHalves + kk * 16 + kofs]);
+        for (int kk = 0; kk < KK; ++kk) {
+            const int cur = kk & 1, nxt = cur ^ 1;
+            if (kk + 1 < KK) {
+#pragma unroll
+                for (int i = 0; i < MB; ++i)
+                    av[nxt][i] = *reinterpret_cast<const h8_t*>(&xs[b][arow[i] * kRowHalves + (kk + 1) * 16 + kofs]);
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+                    bv[nxt][j] = *reinterpret_cast<const h8_t*>(&wsm[b][brow[j] * kRowHalves + (kk + 1) * 16 + kofs]);
+            }
 #pragma unroll
             for (int i = 0; i < MB; ++i)
 #pragma unroll
                 for (int j = 0; j < NB; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[cur][i], bv[cur][j], acc[i][j], 0, 0, 0);
+            if (kk + 1 < KK) {
+                // alternate: one LDS read, one MFMA
+#pragma unroll
+                for (int q = 0; q < MB + NB; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                }
+            }
         }
+        __builtin_amdgcn_s_setprio(0);
     };
 
 #pragma unroll
