@@ -87,8 +87,11 @@ def test_gemm_plain_vs_oracle(m, n, k, group):
     assert np.all(err <= tol_plain(a_ref)), (float((err / tol_plain(a_ref)).max()), m, n, k, group)
 
 
+# From 256 token rows gate/up runs on 128-row tiles with one LDS buffer (three
+# workgroups per CU): 300 and 257 rows end in ragged tiles, 448 inputs are an
+# odd number of k steps (the ring's tail), and 200 inputs end inside a step.
 @pytest.mark.parametrize("m,half,k,group", [(70, 136, 256, 64), (33, 64, 128, 32), (130, 200, 384, 128),
-                                            (1, 9, 64, 64)])
+                                            (1, 9, 64, 64), (300, 200, 448, 64), (257, 70, 200, 8)])
 def test_gemm_gateup_vs_oracle(m, half, k, group):
     n = 2 * half
     q, s, xm = _logical(300 + m + half, m, n, k, group)
