@@ -69,6 +69,8 @@ KERNEL_SRC = os.path.join(ROOT, "int4_weight_only_04_amd", "csrc", "w4_kernels.h
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gateup_silu_37888x3584.json")
 GEMM_SRC = os.path.join(ROOT, "int4_weight_only_04_amd", "csrc", "w4_gemm.hip")
 GEMM_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_gateup_512x37888x3584.json")
+ATTN_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attn_4096.json")
+ATTN_SRC = os.path.join(ROOT, "int4_weight_only_04_amd", "csrc", "w4_attn.hip")
 A8_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gateup_silu_a8_37888x3584.json")
 
 
@@ -512,7 +514,7 @@ def run_attention(args) -> int:
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": read_traffic(path=ATTN_TRAFFIC_FILE, src=ATTN_SRC),
             "algorithmic_bytes_per_launch": nbytes,
             "avg_launch_us": round(per_call_ms * 1e3, 3),
             "launches_timed": args.steps * 2 * layers,
