@@ -208,8 +208,8 @@ __global__ void __launch_bounds__(kThreads, NBUF == 2 ? 2 : 3) gemm_w4_kernel(Ge
     // One k step of 64 inputs: four MFMA rounds of 16 inputs.  The operands of
     // round kk + 1 are read from LDS into the second register set while round
     // kk's MFMAs run (issued one read after each MFMA), and the wave raises its
-    // priority for the step so that a SIMD's waves issue their MFMAs ahead of
-    // the other waves' dequantization and LDS writes.
+    // priority for the step (to 1; its LDS stores and loads run at 2, the rest
+    // at 0) so that a SIMD issues MFMAs ahead of other waves' dequantization.
     auto mfma_step = [&](int b) {
         constexpr int KK = kStepK / 16;
         h8_t av[2][MB], bv[2][NB];
@@ -258,8 +258,13 @@ __global__ void __launch_bounds__(kThreads, NBUF == 2 ? 2 : 3) gemm_w4_kernel(Ge
             // above this point would make it wait for that slot's loads
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (NBUF == 1) __syncthreads();  // the previous step's reads are done
+            // the LDS stores and the next global loads run above the MFMA
+            // phase's priority: a workgroup reaches its barrier sooner and
+            // the loads go out early
+            __builtin_amdgcn_s_setprio(2);
             lstore(ring[u], s_begin + base + u, (u & 1) % NBUF);
             issue(ring[u], s_begin + base + u + kRing);
+            __builtin_amdgcn_s_setprio(0);
             __syncthreads();
             mfma_step((u & 1) % NBUF);
         }
@@ -269,7 +274,9 @@ __global__ void __launch_bounds__(kThreads, NBUF == 2 ? 2 : 3) gemm_w4_kernel(Ge
     for (int u = 0; u < kRing - 1; ++u) {
         if (whole + u < nsteps) {
             if constexpr (NBUF == 1) __syncthreads();
+            __builtin_amdgcn_s_setprio(2);
             lstore(ring[u], s_begin + whole + u, (u & 1) % NBUF);
+            __builtin_amdgcn_s_setprio(0);
             __syncthreads();
             mfma_step((u & 1) % NBUF);
         }
