@@ -73,6 +73,8 @@ PLAIN_SHAPES = [
     (129, 260, 576, 64),
     (257, 1030, 320, 32),
     (300, 200, 992, 32),
+    (256, 96, 128, 32),     # the tile policy's boundary: 128-row tiles, two of them
+    (255, 96, 128, 32),     # one row fewer: 64-row tiles, the last one ragged
 ]
 
 
