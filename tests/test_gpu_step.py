@@ -8,8 +8,9 @@ layer (oracle/step.py) takes the GPU's value of each stage as the input of the
 next one, and every GPU stage is held to the bar of its own operation:
 
   * RMSNorm (fp16 output): 2^-11 |x| (the fp16 rounding) plus
-    (t/2 + 8) 2^-24 |x| with t = n/64 + 32 bounding the additions a square
-    passes through in the fp32 sum of squares (either norm kernel), plus the
+    (t/2 + 8) 2^-24 |x| with t = max(ceil(n/1024) + 21, 25) bounding the
+    additions a square passes through in the fp32 sum of squares (the
+    one-workgroup norm kernel, or the norm folded into qkv), plus the
     sqrt, reciprocal and two products; plus 2^-25 below the fp16 normal range;
   * INT4 products: 1e-3 sum|w x| + 1e-5 (fused gate/up: its propagated form);
   * rotary embedding (fp16 output): 2^-11 |r| plus 5 2^-24 (|x_i| + |x_i+64|)
@@ -21,6 +22,8 @@ next one, and every GPU stage is held to the bar of its own operation:
     (bit-exact) and lies in the oracle's near-tie set.
 """
 from __future__ import annotations
+
+import math
 
 import numpy as np
 import pytest
@@ -65,7 +68,7 @@ def tol_rmsnorm(x_ref, n):
     # folded into the qkv projection has the square, 3 additions in the down
     # projection's part (up to 8 rows), 15 per-lane additions of the parts and
     # 6 shuffle levels, i.e. 25
-    t = n / 64 + 32
+    t = max(math.ceil(n / 1024) + 21, 25)
     return (2.0 ** -11 + (t / 2 + 8) * U) * np.abs(x_ref) + 2.0 ** -25
 
 
