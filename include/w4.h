@@ -134,6 +134,22 @@ w4_status w4_gemv(const void* packed_w, const void* packed_s, const uint16_t* x,
                   int32_t group, void* stream);
 
 /*
+ * w4_gemv with the argmax epilogue, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same outputs as w4_gemv(..., argmax, workspace, ...),
+ * but the per-workgroup partials live in a static device array of the
+ * library (256 KiB per GPU, held until the process ends), so no workspace is
+ * passed and nothing is allocated or freed.  Every call on one GPU shares that
+ * array: calls that may overlap on the same GPU (different streams, threads)
+ * race and must be serialized by the caller.  The array needs no initial
+ * contents.  Shapes whose launch needs more partials than the array holds
+ * (more than ~520K rows at k = 3584) return W4_ESHAPE; otherwise rules and
+ * errors as for w4_gemv.  Device, asynchronous on `stream`.
+ */
+w4_status w4_gemv_argmax_noalloc(const void* packed_w, const void* packed_s, const uint16_t* x, float* y,
+                                 int32_t* argmax, int64_t n, int64_t k, int32_t group, void* stream);
+
+/*
  * Fused gate/up + SiLU: with I = n_total / 2, g = rows [0, I) of W x and
  * u = rows [I, 2I), h[j] = silu(g[j]) * u[j] rounded to fp16 (nearest even),
  * silu(t) = t / (1 + e^-t).  Device, asynchronous on `stream`.

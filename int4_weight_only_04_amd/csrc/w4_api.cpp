@@ -268,6 +268,34 @@ w4_status w4_gemv(const void* packed_w, const void* packed_s, const uint16_t* x,
     }
 }
 
+w4_status w4_gemv_argmax_noalloc(const void* packed_w, const void* packed_s, const uint16_t* x, float* y,
+                                 int32_t* argmax, int64_t n, int64_t k, int32_t group, void* stream)
+{
+    try {
+        const char* who = "w4_gemv_argmax_noalloc";
+        if (!argmax) return fail(W4_EINVAL, "%s: null argmax", who);
+        // validated with a placeholder workspace address; the real one is the
+        // library's static scratch, looked up below
+        GemvCall c{packed_w, packed_s, x, y, argmax, reinterpret_cast<void*>(uintptr_t{256}), n, k, group,
+                   kEpiArgmax};
+        w4_status st = validate_gemv(c, who);
+        if (st != W4_OK) return st;
+        const size_t need = argmax_workspace_bytes(launch_grid(c));
+        if (need > kNoAllocScratchBytes)
+            return fail(W4_ESHAPE, "%s: n=%lld k=%lld needs %zu bytes of scratch, the static scratch holds %zu", who,
+                        (long long)n, (long long)k, need, kNoAllocScratchBytes);
+        void* ws = nullptr;
+        hipError_t err = noalloc_scratch(&ws);
+        if (err != hipSuccess) return hip_fail(err, "w4_gemv_argmax_noalloc scratch lookup");
+        c.ws = ws;
+        err = launch_gemv(c, static_cast<hipStream_t>(stream));
+        if (err != hipSuccess) return hip_fail(err, "w4_gemv_argmax_noalloc launch");
+        return ok();
+    } catch (...) {
+        return fail(W4_EINVAL, "w4_gemv_argmax_noalloc: internal exception");
+    }
+}
+
 w4_status w4_gemv_gateup_silu(const void* packed_w, const void* packed_s, const uint16_t* x,
                               uint16_t* h, int64_t n_total, int64_t k, int32_t group, void* stream)
 {

@@ -194,6 +194,15 @@ hipError_t launch_advance(int32_t* pos, hipStream_t stream);
 constexpr int kProbeSinkWords = 1024;
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
 
+// Size of the file-scope device array that backs the allocation-free argmax
+// entry point (the per-workgroup partials of one call; 8 bytes per workgroup
+// plus alignment, so up to 32736 workgroups, e.g. ~520K rows at k = 3584).
+constexpr size_t kNoAllocScratchBytes = 256 * 1024;
+
+// Device address of that array on the current device (looked up once per
+// device with hipGetSymbolAddress, then cached).
+hipError_t noalloc_scratch(void** ptr);
+
 // Launch one GEMV on `stream` (shape already validated by the caller); the
 // argmax epilogue adds a one-workgroup finalize kernel on the same stream.
 hipError_t launch_gemv(const GemvCall& call, hipStream_t stream);

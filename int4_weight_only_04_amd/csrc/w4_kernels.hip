@@ -53,6 +53,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "w4_internal.h"
 
 namespace w4i {
@@ -764,6 +766,35 @@ Plan make_plan(const GemvCall& c)
 }
 
 }  // namespace
+
+// Device memory of the allocation-free argmax entry point: the per-workgroup
+// (value, row) partials live in this file-scope array instead of a caller
+// workspace.  Each GPU the library runs on holds its own copy until the
+// process ends.  In host code the name is only a stand-in for the symbol, so
+// its device address is looked up once per device (hipGetSymbolAddress) and
+// only that address is ever passed to a kernel.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(void** ptr)
+{
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (err != hipSuccess) return err;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 int64_t launch_grid(const GemvCall& c)
 {

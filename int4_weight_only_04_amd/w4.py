@@ -22,7 +22,7 @@ PROJ_PLAIN, PROJ_GATEUP_SILU, PROJ_LMHEAD_ARGMAX = 0, 1, 2
 
 EXPORTED = (
     "w4_status_string", "w4_last_error", "w4_abi_version", "w4_packed_size", "w4_pack",
-    "w4_gemv_workspace_size", "w4_gemv", "w4_gemv_gateup_silu", "w4_gemm_workspace_size", "w4_gemm", "w4_gemm_gateup_silu",
+    "w4_gemv_workspace_size", "w4_gemv", "w4_gemv_argmax_noalloc", "w4_gemv_gateup_silu", "w4_gemm_workspace_size", "w4_gemm", "w4_gemm_gateup_silu",
     "w4_attn_decode_workspace_size", "w4_attn_decode",
     "w4_decode_linear_sweep_create", "w4_decode_linear_sweep", "w4_decode_linear_sweep_destroy",
     "w4_embed", "w4_add_rmsnorm", "w4_rope_kv_append",
@@ -119,6 +119,8 @@ def lib():
     L.w4_gemv.restype = i32
     L.w4_gemv.argtypes = [vp, vp, vp, vp, vp, vp, sz, i64, i64, i32, vp]
     L.w4_gemv_gateup_silu.restype = i32
+    L.w4_gemv_argmax_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, vp]
+    L.w4_gemv_argmax_noalloc.restype = i32
     L.w4_gemv_gateup_silu.argtypes = [vp, vp, vp, vp, i64, i64, i32, vp]
     L.w4_residual_parts.restype = i32
     L.w4_residual_parts.argtypes = [i64, i64, i32, ctypes.POINTER(i64)]
@@ -266,6 +268,19 @@ def gemv(packed_w, packed_s, x, y, n: int, k: int, group: int, argmax=None, work
                          _dev_ptr(argmax, "argmax", torch.int32, 1),
                          _dev_ptr(workspace, "workspace"), ws_bytes, n, k, group,
                          _stream(stream)), "w4_gemv")
+
+
+def gemv_argmax_noalloc(packed_w, packed_s, x, y, argmax, n: int, k: int, group: int, stream=None):
+    """y[n] (fp32) = W x and the lowest-index argmax of y, with the partials
+    in the library's static device scratch (no workspace argument)."""
+    import torch
+    wb, sb = packed_size(n, k, group, "plain")
+    _check(lib().w4_gemv_argmax_noalloc(_dev_ptr(packed_w, "packed_w", torch.uint8, wb),
+                                        _dev_ptr(packed_s, "packed_s", torch.uint8, sb),
+                                        _dev_ptr(x, "x", torch.float16, k),
+                                        _dev_ptr(y, "y", torch.float32, n),
+                                        _dev_ptr(argmax, "argmax", torch.int32, 1),
+                                        n, k, group, _stream(stream)), "w4_gemv_argmax_noalloc")
 
 
 def gemv_gateup_silu(packed_w, packed_s, x, h, n_total: int, k: int, group: int, stream=None):

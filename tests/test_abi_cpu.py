@@ -149,6 +149,20 @@ def test_gemv_validation_before_launch():
     assert L.w4_gemv_gateup_silu(A, None, A, A, 6, 64, 32, None) == w4.EINVAL
 
 
+def test_gemv_argmax_noalloc_validation_before_launch():
+    """The allocation-free argmax entry point rejects bad arguments, and shapes
+    whose partials exceed its static scratch, before any device call."""
+    L = w4.lib()
+    A = 1 << 20
+    assert L.w4_gemv_argmax_noalloc(A, A, A, A, None, 4, 64, 32, None) == w4.EINVAL    # no argmax
+    assert L.w4_gemv_argmax_noalloc(None, A, A, A, A, 4, 64, 32, None) == w4.EINVAL    # null weights
+    assert L.w4_gemv_argmax_noalloc(A + 4, A, A, A, A, 4, 64, 32, None) == w4.EALIGN
+    assert L.w4_gemv_argmax_noalloc(A, A, A, A, A, 4, 96, 64, None) == w4.ESHAPE       # k % group
+    # 600000 x 3584 needs 37500 workgroups of partials, past the 256 KiB scratch
+    assert L.w4_gemv_argmax_noalloc(A, A, A, A, A, 600000, 3584, 128, None) == w4.ESHAPE
+    assert "scratch" in w4.last_error()
+
+
 def test_gemm_validation_before_launch():
     """Prefill GEMM argument checks run before any device call."""
     L = w4.lib()
