@@ -117,10 +117,15 @@ w4_status w4_gemv_workspace_size(int64_t n, int64_t k, int32_t group, int32_t wi
                                  size_t* bytes);
 
 /*
- * y = W x for a plain-layout packed matrix, optionally with the lm_head argmax
- * epilogue (lowest index of the largest y; NaN never wins; -1 if every y is
- * NaN).  Device, asynchronous on `stream`; with argmax a second, one-workgroup
- * kernel on the same stream reduces the per-workgroup partials.
+ * y = W x for a plain-layout packed matrix: the run-time INT4 dequantization
+ * GEMV of "How To Build Your Own LLM Runtime From Scratch" (aitrending.vip),
+ * "Technical Details", first bullet, with fp16 activations (third page,
+ * "As tres licoes", lesson 3).  Optionally with the lm_head argmax epilogue,
+ * the greedy reading of the runtime's own sampling code (first page,
+ * "Industry Insight", first bullet): lowest index of the largest y; NaN never
+ * wins; -1 if every y is NaN.  Device, asynchronous on `stream`; with argmax a
+ * second, one-workgroup kernel on the same stream reduces the per-workgroup
+ * partials.
  *   packed_w, packed_s  device, from w4_pack(..., W4_LAYOUT_PLAIN, ...);
  *   x        device, fp16 [k];
  *   y        device, fp32 [n] (written for every row);
@@ -150,7 +155,10 @@ w4_status w4_gemv_argmax_noalloc(const void* packed_w, const void* packed_s, con
                                  int32_t* argmax, int64_t n, int64_t k, int32_t group, void* stream);
 
 /*
- * Fused gate/up + SiLU: with I = n_total / 2, g = rows [0, I) of W x and
+ * Fused gate/up + SiLU: the gate/up GEMV that the pages' instruction lesson is
+ * about (first page, section 技术解析, engineering-lessons bullet, item 2; third
+ * page, "As tres licoes", lesson 3), with the SiLU-gated MLP epilogue of the model family
+ * they name.  With I = n_total / 2, g = rows [0, I) of W x and
  * u = rows [I, 2I), h[j] = silu(g[j]) * u[j] rounded to fp16 (nearest even),
  * silu(t) = t / (1 + e^-t).  Device, asynchronous on `stream`.
  *   packed_w, packed_s  device, from w4_pack(..., W4_LAYOUT_GATEUP, ...);
@@ -306,19 +314,48 @@ typedef struct w4_proj_desc {
 
 typedef struct w4_sweep w4_sweep;
 
+/* How a sweep is issued (the `mode` of w4_decode_linear_sweep_create). */
+#define W4_SWEEP_EAGER 0            /* one GEMV kernel per projection, launched one by one        */
+#define W4_SWEEP_GRAPH 1            /* the same kernels captured into one HIP graph               */
+#define W4_SWEEP_PERSISTENT 2       /* one persistent cooperative kernel for all projections,     */
+                                    /* captured into one HIP graph                               */
+#define W4_SWEEP_PERSISTENT_EAGER 3 /* the persistent kernel's launches, not captured            */
+
 /*
  * Build the per-token sweep over `count` projections, run in array order
- * (the decode order: per layer QKV, o_proj, gate/up, down; then lm_head).
- * use_graph != 0 captures all launches into one HIP graph (one submission
+ * (the decode order: per layer QKV, o_proj, gate/up, down; then lm_head);
+ * each projection's math starts only after the previous one has finished.
+ * W4_SWEEP_GRAPH captures all launches into one HIP graph (one submission
  * per token, as the pages' "CUDA Graph Optimization" bullet describes);
- * use_graph == 0 keeps them as eager launches, for the eager-vs-graph
- * comparison.  Every descriptor is validated first.  The handle keeps a copy
- * of the descriptors and the graph, which bakes in every pointer: the buffers
- * must stay alive and in place until w4_decode_linear_sweep_destroy.
- * Capture uses a private stream of the library.
+ * W4_SWEEP_EAGER keeps them as eager launches, for the eager-vs-graph
+ * comparison.
+ *
+ * W4_SWEEP_PERSISTENT runs every projection inside one cooperative kernel
+ * with one workgroup per CU: while a projection finishes, each workgroup
+ * already has the next projection's first weights in flight, and the next
+ * projection's input reaches every workgroup as data written by the other
+ * workgroups after they finished (tagged words plus arrival counters in
+ * device memory), so the decode-order dependency is kept without a kernel
+ * boundary.  Its outputs are bit-identical to the one-kernel path's.  It
+ * covers sweeps of at most 256 projections whose every k is a multiple of
+ * 512 and at most 20480, with 64 <= G <= 512 (W4_ESHAPE otherwise); lm_head workspaces then need
+ * w4_gemv_workspace_size bytes for at most one workgroup per CU.  The handle
+ * allocates its device state at create (phase table, control block, two
+ * input buffers of k/2 8-byte words; ~160 KB for the 7B shapes).  Every wait
+ * in the kernel is bounded by a watchdog (200 ms by default): on a timeout
+ * the kernel ends normally, its outputs are undefined, and
+ * w4_decode_linear_sweep_status reports it.  Only one persistent sweep may
+ * run on a GPU at a time (it needs every CU).  On MI355X it is slower than
+ * W4_SWEEP_GRAPH for the 28-layer sweep (3.27 ms against 0.91 ms): it is
+ * kept as the dependency-checked single-kernel form, not as the fast path.
+ *
+ * Every descriptor is validated first.  The handle keeps a copy of the
+ * descriptors and the graph, which bakes in every pointer: the buffers must
+ * stay alive and in place until w4_decode_linear_sweep_destroy.  Capture uses
+ * a private stream of the library, so create takes no stream.
  */
 w4_status w4_decode_linear_sweep_create(const w4_proj_desc* projs, int32_t count,
-                                        int32_t use_graph, w4_sweep** out);
+                                        int32_t mode, w4_sweep** out);
 
 /* Run one token's sweep on `stream` (graph launch or eager launches).  The
  * lm_head projection contributes two kernels (GEMV + argmax finalize). */
@@ -326,6 +363,16 @@ w4_status w4_decode_linear_sweep(w4_sweep* sweep, void* stream);
 
 /* Release the handle (NULL is accepted). */
 w4_status w4_decode_linear_sweep_destroy(w4_sweep* sweep);
+
+/* Persistent modes: waits for the device, then sets *timed_out to 1 if a
+ * watchdog timeout happened in any run since the last call (and clears it),
+ * else 0.  Other modes: always 0.  Host, synchronizing. */
+w4_status w4_decode_linear_sweep_status(w4_sweep* sweep, int32_t* timed_out);
+
+/* Persistent modes: the watchdog bound of every wait in the kernel, in
+ * seconds (0 < seconds <= 60); takes effect from the next run.  Host,
+ * synchronizing.  W4_EINVAL for other modes. */
+w4_status w4_decode_linear_sweep_set_watchdog(w4_sweep* sweep, double seconds);
 
 /*
  * The glue of a full decode step.  The pages name the model (Qwen2.5-Coder-7B:

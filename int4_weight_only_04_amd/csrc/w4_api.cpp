@@ -565,9 +565,19 @@ w4_status w4_attn_decode(const uint16_t* q, const uint16_t* k_cache, const uint1
 
 struct w4_sweep {
     std::vector<GemvCall> calls;
-    bool use_graph = false;
+    int32_t mode = 0;             // W4_SWEEP_EAGER / _GRAPH / _PERSISTENT / _PERSISTENT_EAGER
+    bool use_graph = false;       // the launches are replayed from `exec`
     hipGraph_t graph = nullptr;
     hipGraphExec_t exec = nullptr;
+    // persistent modes
+    void* dev = nullptr;          // phase table + control block + tagged input words
+    PersistArgs pargs{};
+    struct Final {
+        const float* part_v;
+        const int32_t* part_i;
+        int32_t* out;
+    };
+    std::vector<Final> finals;    // argmax finalize per lm_head projection
 };
 
 namespace {
@@ -592,6 +602,111 @@ w4_status desc_to_call(const w4_proj_desc& d, int32_t idx, GemvCall* out)
     return W4_OK;
 }
 
+w4_status launch_persistent(const w4_sweep& sw, hipStream_t stream)
+{
+    hipError_t err = launch_persist(sw.pargs, stream);
+    if (err != hipSuccess) return hip_fail(err, "persistent sweep launch");
+    for (const auto& f : sw.finals) {
+        err = launch_argmax_finalize(f.part_v, f.part_i, sw.pargs.nwg, f.out, stream);
+        if (err != hipSuccess) return hip_fail(err, "persistent sweep argmax finalize");
+    }
+    return W4_OK;
+}
+
+// Build the persistent sweep's device state: the phase table (same unit and
+// split shape per projection as the launch table of the one-kernel path), the
+// control block and the tagged input words.  Fails with W4_ESHAPE for sweeps
+// the persistent kernel does not cover.
+w4_status persist_setup(w4_sweep* sw, const w4_proj_desc* projs)
+{
+    const char* who = "w4_decode_linear_sweep_create (persistent)";
+    const int32_t count = (int32_t)sw->calls.size();
+    if (count > kPMaxPhases) return fail(W4_ESHAPE, "%s: %d projections, at most %d", who, count, kPMaxPhases);
+    for (int32_t i = 0; i < count; ++i) {
+        const GemvCall& c = sw->calls[(size_t)i];
+        if (c.k % 512 != 0 || c.k / 8 > kPMaxKb)
+            return fail(W4_ESHAPE, "%s: projection %d: k=%lld must be a multiple of 512 and at most %d", who, i,
+                        (long long)c.k, kPMaxKb * 8);
+        if (c.group < 64 || c.group > 512)
+            return fail(W4_ESHAPE, "%s: projection %d: group=%d must be in [64, 512]", who, i, c.group);
+    }
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return hip_fail(err, "hipGetDevice");
+    int cus = 0, coop = 0;
+    err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (err == hipSuccess) err = hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev);
+    if (err != hipSuccess) return hip_fail(err, "hipDeviceGetAttribute");
+    if (!coop) return fail(W4_EINVAL, "%s: the device does not support cooperative launches", who);
+    int per_cu = 0;
+    err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, persist_kernel_fn(), persist_threads(), 0);
+    if (err != hipSuccess) return hip_fail(err, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+    if (per_cu < 1 || cus < 8) return fail(W4_EINVAL, "%s: the kernel does not fit on a CU (%d per CU, %d CUs)", who,
+                                           per_cu, cus);
+    const int32_t nwg = cus;
+    std::vector<PersistPhase> ph((size_t)count);
+    int32_t max_words = 1;
+    for (int32_t i = 0; i < count; ++i) {
+        const GemvCall& c = sw->calls[(size_t)i];
+        const int32_t words = (int32_t)(c.k / 2);
+        if ((words + nwg - 1) / nwg > kPStageWords)
+            return fail(W4_ESHAPE, "%s: projection %d: k=%lld too long for %d workgroups", who, i, (long long)c.k,
+                        nwg);
+        if (words > max_words) max_words = words;
+        const bool gateup = c.epi == kEpiGateUp;
+        PersistPhase& P = ph[(size_t)i];
+        P.pw = static_cast<const uint4*>(c.pw);
+        P.ps = static_cast<const uint2*>(c.ps);
+        P.x = static_cast<const uint16_t*>(c.x);
+        P.out = c.out;
+        P.n = c.n;
+        P.tiles = tiles_for(c.n, gateup);
+        P.tiles_half = gateup ? P.tiles / 2 : 0;
+        P.kb = (int32_t)(c.k / 8);
+        P.iters = (int32_t)(c.k / 512);
+        P.ng = (int32_t)(c.k / c.group);
+        int32_t gshift = 0;
+        while ((8 << gshift) < c.group) ++gshift;
+        P.gshift = gshift;
+        P.epi = c.epi;
+        const LaunchConfig cfg = choose_config(c.epi, gateup ? P.tiles / 2 : P.tiles, P.iters);
+        P.utiles = gateup ? 2 : cfg.tiles;
+        P.split = cfg.split;
+        const int64_t units = gateup ? P.tiles / 2 : (P.tiles + cfg.tiles - 1) / cfg.tiles;
+        if (units > INT32_MAX) return fail(W4_ESHAPE, "%s: projection %d too tall", who, i);
+        P.units = (int32_t)units;
+        P.sc_dwords = 2 * (512 / c.group);
+        if (c.epi == kEpiArgmax) {
+            const w4_proj_desc& d = projs[i];
+            if (d.workspace_bytes < argmax_workspace_bytes(nwg))
+                return fail(W4_EINVAL, "%s: projection %d: workspace of %zu bytes, need %zu", who, i,
+                            d.workspace_bytes, argmax_workspace_bytes(nwg));
+            uint8_t* ws = static_cast<uint8_t*>(c.ws);
+            P.part_v = reinterpret_cast<float*>(ws);
+            P.part_i = reinterpret_cast<int32_t*>(ws + argmax_index_offset(nwg));
+            sw->finals.push_back({P.part_v, P.part_i, c.argmax});
+        }
+    }
+    const size_t ph_bytes = ((sizeof(PersistPhase) * (size_t)count) + 255) & ~(size_t)255;
+    const size_t hand_bytes = 2 * (size_t)max_words * 8;
+    err = hipMalloc(&sw->dev, ph_bytes + kPersistCtrlBytes + hand_bytes);
+    if (err != hipSuccess) return hip_fail(err, "hipMalloc (persistent sweep state)");
+    uint8_t* base = static_cast<uint8_t*>(sw->dev);
+    err = hipMemset(base + ph_bytes, 0, kPersistCtrlBytes + hand_bytes);
+    if (err == hipSuccess) err = hipMemcpy(base, ph.data(), sizeof(PersistPhase) * (size_t)count, hipMemcpyHostToDevice);
+    const unsigned long long ticks = kPersistTicksPerSecond / 5;   // 200 ms watchdog
+    if (err == hipSuccess)
+        err = hipMemcpy(base + ph_bytes + kPersistCtrlWatchdogOffset, &ticks, sizeof ticks, hipMemcpyHostToDevice);
+    if (err != hipSuccess) return hip_fail(err, "persistent sweep state upload");
+    sw->pargs.ph = reinterpret_cast<const PersistPhase*>(base);
+    sw->pargs.nph = count;
+    sw->pargs.nwg = nwg;
+    sw->pargs.ctrl = reinterpret_cast<unsigned*>(base + ph_bytes);
+    sw->pargs.hand = reinterpret_cast<unsigned long long*>(base + ph_bytes + kPersistCtrlBytes);
+    sw->pargs.hand_words = max_words;
+    return W4_OK;
+}
+
 w4_status launch_all(const std::vector<GemvCall>& calls, hipStream_t stream)
 {
     for (size_t i = 0; i < calls.size(); ++i) {
@@ -609,7 +724,7 @@ w4_status launch_all(const std::vector<GemvCall>& calls, hipStream_t stream)
 
 extern "C" {
 
-w4_status w4_decode_linear_sweep_create(const w4_proj_desc* projs, int32_t count, int32_t use_graph,
+w4_status w4_decode_linear_sweep_create(const w4_proj_desc* projs, int32_t count, int32_t mode,
                                         w4_sweep** out)
 {
     try {
@@ -617,8 +732,11 @@ w4_status w4_decode_linear_sweep_create(const w4_proj_desc* projs, int32_t count
         *out = nullptr;
         if (!projs || count < 1)
             return fail(W4_EINVAL, "w4_decode_linear_sweep_create: need at least one projection");
+        if (mode < W4_SWEEP_EAGER || mode > W4_SWEEP_PERSISTENT_EAGER)
+            return fail(W4_EINVAL, "w4_decode_linear_sweep_create: unknown mode %d", mode);
         w4_sweep* sw = new w4_sweep();
-        sw->use_graph = use_graph != 0;
+        sw->mode = mode;
+        sw->use_graph = mode == W4_SWEEP_GRAPH || mode == W4_SWEEP_PERSISTENT;
         sw->calls.resize((size_t)count);
         for (int32_t i = 0; i < count; ++i) {
             w4_status st = desc_to_call(projs[i], i, &sw->calls[(size_t)i]);
@@ -627,25 +745,37 @@ w4_status w4_decode_linear_sweep_create(const w4_proj_desc* projs, int32_t count
                 return st;
             }
         }
+        const bool persistent = mode == W4_SWEEP_PERSISTENT || mode == W4_SWEEP_PERSISTENT_EAGER;
+        if (persistent) {
+            w4_status st = persist_setup(sw, projs);
+            if (st != W4_OK) {
+                if (sw->dev) hipFree(sw->dev);
+                delete sw;
+                return st;
+            }
+        }
         if (sw->use_graph) {
             hipStream_t cap = nullptr;
             hipError_t err = hipStreamCreateWithFlags(&cap, hipStreamNonBlocking);
             if (err != hipSuccess) {
+                if (sw->dev) hipFree(sw->dev);
                 delete sw;
                 return hip_fail(err, "hipStreamCreateWithFlags");
             }
             err = hipStreamBeginCapture(cap, hipStreamCaptureModeThreadLocal);
             if (err != hipSuccess) {
                 hipStreamDestroy(cap);
+                if (sw->dev) hipFree(sw->dev);
                 delete sw;
                 return fail(W4_ECAPTURE, "hipStreamBeginCapture failed: %s", hipGetErrorString(err));
             }
-            w4_status st = launch_all(sw->calls, cap);
+            w4_status st = persistent ? launch_persistent(*sw, cap) : launch_all(sw->calls, cap);
             hipGraph_t graph = nullptr;
             hipError_t end_err = hipStreamEndCapture(cap, &graph);
             hipStreamDestroy(cap);
             if (st != W4_OK || end_err != hipSuccess) {
                 if (graph) hipGraphDestroy(graph);
+                if (sw->dev) hipFree(sw->dev);
                 delete sw;
                 if (st != W4_OK) return st;
                 return fail(W4_ECAPTURE, "hipStreamEndCapture failed: %s", hipGetErrorString(end_err));
@@ -654,6 +784,7 @@ w4_status w4_decode_linear_sweep_create(const w4_proj_desc* projs, int32_t count
             err = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
             if (err != hipSuccess) {
                 hipGraphDestroy(graph);
+                if (sw->dev) hipFree(sw->dev);
                 delete sw;
                 return fail(W4_ECAPTURE, "hipGraphInstantiate failed: %s", hipGetErrorString(err));
             }
@@ -679,6 +810,7 @@ w4_status w4_decode_linear_sweep(w4_sweep* sweep, void* stream)
             if (err != hipSuccess) return hip_fail(err, "hipGraphLaunch");
             return ok();
         }
+        if (sweep->mode == W4_SWEEP_PERSISTENT_EAGER) return launch_persistent(*sweep, s);
         return launch_all(sweep->calls, s);
     } catch (...) {
         return fail(W4_EINVAL, "w4_decode_linear_sweep: internal exception");
@@ -691,10 +823,55 @@ w4_status w4_decode_linear_sweep_destroy(w4_sweep* sweep)
         if (!sweep) return ok();
         if (sweep->exec) hipGraphExecDestroy(sweep->exec);
         if (sweep->graph) hipGraphDestroy(sweep->graph);
+        if (sweep->dev) hipFree(sweep->dev);
         delete sweep;
         return ok();
     } catch (...) {
         return fail(W4_EINVAL, "w4_decode_linear_sweep_destroy: internal exception");
+    }
+}
+
+w4_status w4_decode_linear_sweep_status(w4_sweep* sweep, int32_t* timed_out)
+{
+    try {
+        if (!sweep || !timed_out) return fail(W4_EINVAL, "w4_decode_linear_sweep_status: null argument");
+        *timed_out = 0;
+        if (!sweep->dev) return ok();
+        hipError_t err = hipDeviceSynchronize();
+        if (err != hipSuccess) return hip_fail(err, "hipDeviceSynchronize");
+        uint32_t word = 0;
+        uint8_t* ctrl = reinterpret_cast<uint8_t*>(sweep->pargs.ctrl);
+        err = hipMemcpy(&word, ctrl + kPersistCtrlErrorOffset, sizeof word, hipMemcpyDeviceToHost);
+        if (err != hipSuccess) return hip_fail(err, "hipMemcpy (sweep status)");
+        if (word) {
+            const uint32_t zero = 0;
+            err = hipMemcpy(ctrl + kPersistCtrlErrorOffset, &zero, sizeof zero, hipMemcpyHostToDevice);
+            if (err != hipSuccess) return hip_fail(err, "hipMemcpy (sweep status clear)");
+        }
+        *timed_out = word ? 1 : 0;
+        return ok();
+    } catch (...) {
+        return fail(W4_EINVAL, "w4_decode_linear_sweep_status: internal exception");
+    }
+}
+
+w4_status w4_decode_linear_sweep_set_watchdog(w4_sweep* sweep, double seconds)
+{
+    try {
+        if (!sweep) return fail(W4_EINVAL, "w4_decode_linear_sweep_set_watchdog: null handle");
+        if (!(seconds > 0.0) || !(seconds <= 60.0))
+            return fail(W4_EINVAL, "w4_decode_linear_sweep_set_watchdog: seconds=%g must be in (0, 60]", seconds);
+        if (!sweep->dev) return fail(W4_EINVAL, "w4_decode_linear_sweep_set_watchdog: not a persistent sweep");
+        unsigned long long ticks = (unsigned long long)(seconds * (double)kPersistTicksPerSecond);
+        if (ticks < 1) ticks = 1;
+        hipError_t err = hipDeviceSynchronize();
+        if (err == hipSuccess)
+            err = hipMemcpy(reinterpret_cast<uint8_t*>(sweep->pargs.ctrl) + kPersistCtrlWatchdogOffset, &ticks,
+                            sizeof ticks, hipMemcpyHostToDevice);
+        if (err != hipSuccess) return hip_fail(err, "hipMemcpy (sweep watchdog)");
+        return ok();
+    } catch (...) {
+        return fail(W4_EINVAL, "w4_decode_linear_sweep_set_watchdog: internal exception");
     }
 }
 

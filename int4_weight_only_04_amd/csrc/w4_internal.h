@@ -203,6 +203,58 @@ constexpr size_t kNoAllocScratchBytes = 256 * 1024;
 // device with hipGetSymbolAddress, then cached).
 hipError_t noalloc_scratch(void** ptr);
 
+// Persistent sweep (one cooperative kernel for every projection of a sweep;
+// eligible sweeps: k a multiple of 512 and at most kPMaxKb * 8, 64 <= G <= 512,
+// at most kPStageWords input words per workgroup).
+constexpr int kPMaxKb = 2560;          // k / 8 bound (k <= 20480)
+constexpr int kPStageWords = 128;      // input words (2 fp16 each) a workgroup forwards
+constexpr int kPMaxPhases = 256;       // projections per sweep (the phase table is kept in LDS)
+
+struct PersistPhase {
+    const uint4* pw;        // packed weights
+    const uint2* ps;        // packed scales
+    const uint16_t* x;      // the projection's input x (fp16 [k])
+    void* out;              // y fp32 [n], or h fp16 [n/2] for gate/up
+    float* part_v;          // argmax: per-workgroup best value [nwg]
+    int32_t* part_i;        // argmax: per-workgroup best row [nwg]
+    int64_t n;              // logical rows (gate/up: 2I)
+    int64_t tiles;          // tiles in the packed matrix
+    int64_t tiles_half;     // gate/up: tiles per half
+    int32_t units;          // units (tiles, tile pairs, or gate/up tile pairs)
+    int32_t kb;             // k / 8
+    int32_t iters;          // k / 512
+    int32_t ng;             // k / G
+    int32_t gshift;         // log2(G / 8)
+    int32_t epi;            // kEpiPlain / kEpiGateUp / kEpiArgmax
+    int32_t utiles;         // tiles per unit (1 or 2)
+    int32_t split;          // waves per unit (same as the one-kernel path's launch table)
+    int32_t sc_dwords;      // scale dwords per 512-input chunk of a tile (2 * 512 / G)
+    int32_t pad[5];         // 128 bytes (the kernel copies the table to LDS in 16-byte words)
+};
+
+struct PersistArgs {
+    const PersistPhase* ph;     // device array [nph]
+    int32_t nph;
+    int32_t nwg;                // workgroups (one per CU)
+    unsigned long long* hand;   // tagged input words [2][hand_words]
+    int32_t hand_words;
+    unsigned* ctrl;             // control block (kPersistCtrlBytes)
+};
+
+constexpr size_t kPersistCtrlBytes = 12 * 128;
+constexpr size_t kPersistCtrlErrorOffset = 10 * 128;      // uint32: nonzero after a watchdog timeout
+constexpr size_t kPersistCtrlWatchdogOffset = 11 * 128;   // uint64: wait limit in 100 MHz ticks
+constexpr unsigned long long kPersistTicksPerSecond = 100000000ull;   // s_memrealtime rate
+
+const void* persist_kernel_fn();
+int persist_threads();
+// the launch sequence of one token: the advance kernel, then the cooperative
+// persistent kernel (the argmax finalize kernels are launched by the caller)
+hipError_t launch_persist(const PersistArgs& args, hipStream_t stream);
+// lowest-index maximum over `count` per-workgroup (value, row) partials
+hipError_t launch_argmax_finalize(const float* part_v, const int32_t* part_i, int32_t count, int32_t* out,
+                                  hipStream_t stream);
+
 // Launch one GEMV on `stream` (shape already validated by the caller); the
 // argmax epilogue adds a one-workgroup finalize kernel on the same stream.
 hipError_t launch_gemv(const GemvCall& call, hipStream_t stream);

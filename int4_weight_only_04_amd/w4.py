@@ -19,12 +19,14 @@ LIB_PATH = os.path.join(_PKG, "libw4.so")
 OK, EINVAL, ESHAPE, EALIGN, EHIP, ENOMEM, ECAPTURE = range(7)
 LAYOUT_PLAIN, LAYOUT_GATEUP = 0, 1
 PROJ_PLAIN, PROJ_GATEUP_SILU, PROJ_LMHEAD_ARGMAX = 0, 1, 2
+SWEEP_EAGER, SWEEP_GRAPH, SWEEP_PERSISTENT, SWEEP_PERSISTENT_EAGER = 0, 1, 2, 3
 
 EXPORTED = (
     "w4_status_string", "w4_last_error", "w4_abi_version", "w4_packed_size", "w4_pack",
     "w4_gemv_workspace_size", "w4_gemv", "w4_gemv_argmax_noalloc", "w4_gemv_gateup_silu", "w4_gemm_workspace_size", "w4_gemm", "w4_gemm_gateup_silu",
     "w4_attn_decode_workspace_size", "w4_attn_decode",
     "w4_decode_linear_sweep_create", "w4_decode_linear_sweep", "w4_decode_linear_sweep_destroy",
+    "w4_decode_linear_sweep_status", "w4_decode_linear_sweep_set_watchdog",
     "w4_embed", "w4_add_rmsnorm", "w4_rope_kv_append",
     "w4_decode_step_create", "w4_decode_step", "w4_decode_step_launches", "w4_decode_step_destroy",
     "w4_decode_step_trace_layout",
@@ -147,6 +149,10 @@ def lib():
     L.w4_decode_linear_sweep.argtypes = [vp, vp]
     L.w4_decode_linear_sweep_destroy.restype = i32
     L.w4_decode_linear_sweep_destroy.argtypes = [vp]
+    L.w4_decode_linear_sweep_status.argtypes = [vp, ctypes.POINTER(i32)]
+    L.w4_decode_linear_sweep_status.restype = i32
+    L.w4_decode_linear_sweep_set_watchdog.argtypes = [vp, ctypes.c_double]
+    L.w4_decode_linear_sweep_set_watchdog.restype = i32
     L.w4_embed.restype = i32
     L.w4_embed.argtypes = [vp, i64, i64, vp, vp, vp]
     L.w4_add_rmsnorm.restype = i32
@@ -473,9 +479,10 @@ class Proj:
 
 
 class Sweep:
-    """Per-token linear sweep: eager launches or one captured HIP graph."""
+    """Per-token linear sweep: eager launches, one captured HIP graph, or the
+    persistent kernel (mode SWEEP_PERSISTENT / SWEEP_PERSISTENT_EAGER)."""
 
-    def __init__(self, projs: Sequence[Proj], use_graph: bool = True):
+    def __init__(self, projs: Sequence[Proj], use_graph: bool = True, mode: Optional[int] = None):
         import torch
         self._projs = list(projs)  # keep device buffers alive while the graph exists
         arr = (ProjDesc * len(self._projs))()
@@ -498,12 +505,24 @@ class Sweep:
             d.workspace = _dev_ptr(p.workspace, "workspace")
             d.workspace_bytes = (p.workspace.numel() * p.workspace.element_size()
                                  if p.workspace is not None else 0)
+        if mode is None:
+            mode = SWEEP_GRAPH if use_graph else SWEEP_EAGER
         handle = ctypes.c_void_p()
-        _check(lib().w4_decode_linear_sweep_create(arr, len(self._projs), int(bool(use_graph)),
-                                                   ctypes.byref(handle)),
+        _check(lib().w4_decode_linear_sweep_create(arr, len(self._projs), int(mode), ctypes.byref(handle)),
                "w4_decode_linear_sweep_create")
         self._handle = handle
-        self.use_graph = use_graph
+        self.mode = int(mode)
+        self.use_graph = self.mode in (SWEEP_GRAPH, SWEEP_PERSISTENT)
+
+    def status(self) -> bool:
+        """True if a watchdog timeout happened since the last call (persistent modes)."""
+        out = ctypes.c_int32()
+        _check(lib().w4_decode_linear_sweep_status(self._handle, ctypes.byref(out)), "w4_decode_linear_sweep_status")
+        return bool(out.value)
+
+    def set_watchdog(self, seconds: float):
+        _check(lib().w4_decode_linear_sweep_set_watchdog(self._handle, float(seconds)),
+               "w4_decode_linear_sweep_set_watchdog")
 
     def run(self, stream=None):
         if not self._handle:

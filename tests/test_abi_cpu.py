@@ -251,6 +251,40 @@ def test_sweep_create_validation():
     assert L.w4_decode_linear_sweep(None, None) == w4.EINVAL
 
 
+def test_persistent_sweep_validation_before_launch():
+    """The persistent modes' shape limits (k a multiple of 512, 64 <= G <= 512,
+    at most 256 projections), the mode range and the status / watchdog calls'
+    argument checks all fail before any device call."""
+    L = w4.lib()
+    A = 1 << 20
+    handle = ctypes.c_void_p()
+    descs = (w4.ProjDesc * 2)()
+    for d in descs:
+        d.kind, d.group, d.n, d.k = w4.PROJ_PLAIN, 128, 64, 1024
+        d.packed_w = d.packed_s = d.x = d.out = A
+    assert L.w4_decode_linear_sweep_create(descs, 2, 4, ctypes.byref(handle)) == w4.EINVAL
+    assert "mode" in w4.last_error()
+    assert L.w4_decode_linear_sweep_create(descs, 2, -1, ctypes.byref(handle)) == w4.EINVAL
+    descs[1].k = 768  # a multiple of G = 128 and of 256, not of 512
+    for mode in (w4.SWEEP_PERSISTENT, w4.SWEEP_PERSISTENT_EAGER):
+        assert L.w4_decode_linear_sweep_create(descs, 2, mode, ctypes.byref(handle)) == w4.ESHAPE
+        assert "projection 1" in w4.last_error() and "512" in w4.last_error()
+    descs[1].k = 1024
+    descs[0].group = 32
+    assert L.w4_decode_linear_sweep_create(descs, 2, w4.SWEEP_PERSISTENT, ctypes.byref(handle)) == w4.ESHAPE
+    assert "projection 0" in w4.last_error() and "group" in w4.last_error()
+    many = (w4.ProjDesc * 257)()
+    for d in many:
+        d.kind, d.group, d.n, d.k = w4.PROJ_PLAIN, 128, 64, 1024
+        d.packed_w = d.packed_s = d.x = d.out = A
+    assert L.w4_decode_linear_sweep_create(many, 257, w4.SWEEP_PERSISTENT, ctypes.byref(handle)) == w4.ESHAPE
+    assert "257" in w4.last_error()
+    assert not handle.value
+    flag = ctypes.c_int32(5)
+    assert L.w4_decode_linear_sweep_status(None, ctypes.byref(flag)) == w4.EINVAL
+    assert L.w4_decode_linear_sweep_set_watchdog(None, ctypes.c_double(0.1)) == w4.EINVAL
+
+
 def test_step_glue_validation_before_launch():
     """Embedding, residual + RMSNorm and rotary/KV-append checks run before
     any device call."""
