@@ -8,10 +8,22 @@ outputs), all resident in HBM before timing starts.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 5]
 
-prints one JSON line: achieved GB/s over the whole sweep (value), ms per
-sweep, the eager-launch sweep for comparison, the dominant kernel's roofline
-(gate/up + SiLU, timed per launch with HIP events on the launch stream) and
-the CPU oracle timed on a bounded sample on the host.
+prints one JSON line: achieved GB/s over the whole sweep (value) and ms per
+sweep; the graph and the library's eager launches timed in alternating rounds
+(and a Python-driven eager loop); each config's GEMV (tiny, down, gate/up +
+SiLU, lm_head + argmax) on cold buffers, with its counter-calibrated HBM
+bytes when they were taken on this kernel source; the dominant kernel's
+roofline (gate/up + SiLU, timed per launch with HIP events on the launch
+stream) with the GPU clocks sampled around it and a sustained series; the
+pages' H100 figures as context; and the CPU oracle timed on the host's cores,
+single-threaded and on all available cores.
+
+    python bench.py --workload configs
+    python bench.py --traffic-from FETCH.csv WRITE.csv COPYF.csv COPYW.csv
+
+run only the per-config timings (the run the FETCH_SIZE / WRITE_SIZE
+counters are taken over), and turn those counters into
+profiles/traffic_configs.json (host only).
 
     python bench.py --workload attention
 
@@ -66,6 +78,16 @@ W4A8_METRIC = "W4A8 achieved HBM GB/s (% of peak) and ms per 28-layer+lm_head IN
 STEP_METRIC = "batch-1 decode tokens/s and ms per full 28-layer decode step (hipGraph), tokens 512..639"
 ATTN_HEADS, ATTN_KV_HEADS, ATTN_PAGE, ATTN_CTX = 28, 4, 16, 4096
 KERNEL_SRC = os.path.join(ROOT, "int4_weight_only_04_amd", "csrc", "w4_kernels.hip")
+# every file the decode GEMV kernel is compiled from (its math and its launch table)
+GEMV_SRCS = tuple(os.path.join(ROOT, "int4_weight_only_04_amd", "csrc", f)
+                  for f in ("w4_kernels.hip", "w4_gemv_math.h", "w4_internal.h"))
+CONFIG_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_configs.json")
+COLD_BYTES = 576 << 20      # per-config working set: past the 256 MB Infinity Cache
+# The pages' own figures (H100, whole decode step, INT4 weights, batch 1): context, not targets.
+PAGES_CONTEXT_H100 = {"runtime_ms_per_token": 16.7, "eager_ms_per_token": 119, "graph_ms_per_token": 17,
+                      "llama_cpp_q4km_ms_per_token": 4.95,
+                      "note": "whole decode step on an NVIDIA H100 as the pages report it; not this path's "
+                              "metric and not a target"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gateup_silu_37888x3584.json")
 GEMM_SRC = os.path.join(ROOT, "int4_weight_only_04_amd", "csrc", "w4_gemm.hip")
 GEMM_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_gateup_512x37888x3584.json")
@@ -121,12 +143,16 @@ def build_sweep(layers: int = synthetic.LAYERS, device: str = "cuda"):
     return specs, projs
 
 
-def kernel_source_hash(path: str = KERNEL_SRC) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def kernel_source_hash(path=KERNEL_SRC) -> str:
+    """sha256 prefix of a kernel's source file, or of several concatenated."""
+    h = hashlib.sha256()
+    for f in ((path,) if isinstance(path, str) else path):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
-def read_traffic(launch_bytes_alg: int = 0, path: str = TRAFFIC_FILE, src: str = KERNEL_SRC):
+def read_traffic(launch_bytes_alg: int = 0, path: str = TRAFFIC_FILE, src=GEMV_SRCS):
     """HBM bytes per launch of the dominant kernel from the committed counter
     summary, or None if absent or taken on another kernel source."""
     try:
@@ -158,17 +184,19 @@ def time_graph(sweep, stream, steps: int, warmup: int):
     return ev_ms, wall * 1e3 / steps
 
 
-def time_dominant_kernel(projs, stream, replays: int = 4):
+def time_dominant_kernel(projs, stream, replays: int = 4, sustained: int = 40):
     """Average duration of one gate/up + SiLU launch (the kernel that moves the
     most bytes in the sweep): the 28 layers' gate/up launches are captured in
     their own HIP graph (1.96 GB of weights, so nothing is served from the
     256 MB Infinity Cache), replayed once to warm up, then `replays` times
     between HIP events recorded on the launch stream.  The per-launch figure
     includes the time between graph nodes (about 1.4 us from the last wave of
-    one kernel to the first wave of the next).  The loop is kept short: after
-    a few milliseconds of back-to-back gate/up launches (about 5 TB/s
-    sustained) the kernel was seen to slow down in steps, which the sweep, at
-    a lower average bandwidth, does not show."""
+    one kernel to the first wave of the next).
+
+    Then `sustained` more replays back to back, each between its own events,
+    with the GPU's clocks, power and throttle status sampled throughout: that
+    series shows whether a longer run at this bandwidth slows down, and why.
+    Returns (ms per launch in the short window, launches, sustained summary)."""
     import torch
     from int4_weight_only_04_amd import w4
     gu = [p for p in projs if p.kind == w4.PROJ_GATEUP_SILU]
@@ -177,14 +205,30 @@ def time_dominant_kernel(projs, stream, replays: int = 4):
     stream.synchronize()
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for _ in range(replays):
-        g.run(stream)
-    b.record(stream)
-    stream.synchronize()
-    g.close()
+    with ClockSampler() as short_clk:
+        a.record(stream)
+        for _ in range(replays):
+            g.run(stream)
+        b.record(stream)
+        stream.synchronize()
     launches = replays * len(gu)
-    return a.elapsed_time(b) / launches, launches
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(sustained + 1)]
+    with ClockSampler() as long_clk:
+        ev[0].record(stream)
+        for i in range(sustained):
+            g.run(stream)
+            ev[i + 1].record(stream)
+        stream.synchronize()
+    g.close()
+    per = [ev[i].elapsed_time(ev[i + 1]) * 1e3 / len(gu) for i in range(sustained)]
+    q = max(1, sustained // 8)
+    sus = {"replays": sustained, "launches": sustained * len(gu),
+           "us_per_launch_first": round(sum(per[:q]) / q, 3),
+           "us_per_launch_last": round(sum(per[-q:]) / q, 3),
+           "us_per_launch_min": round(min(per), 3), "us_per_launch_max": round(max(per), 3),
+           "ms_total": round(ev[0].elapsed_time(ev[-1]), 3),
+           "clocks": long_clk.summary()}
+    return a.elapsed_time(b) / launches, launches, sus, short_clk.summary()
 
 
 def time_pure_read_sweep(specs, stream, steps: int, warmup: int):
@@ -218,32 +262,402 @@ def time_pure_read_sweep(specs, stream, steps: int, warmup: int):
     return ms, total, (1 << 30) / (big_ms * 1e-3) / 1e9
 
 
-def cpu_baseline():
-    """The oracle as it stands (single thread, fp64) on a bounded sample: all
-    rows of layer 0's four projections, inputs drawn exactly as in the sweep."""
-    import oracle
+CONFIGS = (synthetic.CONFIG_TINY, synthetic.CONFIG_DOWN, synthetic.CONFIG_GATEUP, synthetic.CONFIG_LMHEAD)
+
+
+def config_label(c) -> str:
+    extra = {"gateup": " + silu", "lmhead": " + argmax"}.get(c["kind"], "")
+    return f'{c["name"]} {c["n"]}x{c["k"]} g{c["group"]}{extra}'
+
+
+def config_inputs(c):
+    """A config's packed inputs, drawn in packed form from its seed (row counts
+    are multiples of 4, so no padding slots), with its scale range."""
     from int4_weight_only_04_amd import w4
-    specs = synthetic.sweep_projections(1)
-    total_bytes = 0
-    t_total = 0.0
-    for p in specs:
+    layout = "gateup" if c["kind"] == "gateup" else "plain"
+    wb, sb = w4.packed_size(c["n"], c["k"], c["group"], layout)
+    pw, ps, x = synthetic.packed_random(c["seed"], wb, sb // 2, c["k"], c["s_lo"], c["s_hi"])
+    return layout, wb, sb, pw, ps, x
+
+
+def time_configs(stream, replays: int = 5, max_calls=None):
+    """Per config (tiny, down, gate/up + SiLU, lm_head + argmax): microseconds
+    per GEMV call on cold buffers.  The packed matrix is replicated on the
+    device until the copies span COLD_BYTES (more than the 256 MB Infinity
+    Cache), a HIP graph of max(copies, 32) back-to-back calls cycles through
+    them, and the graph is replayed `replays` times after one warm-up; the
+    figure is the replay time over the calls, so it includes the gap between
+    consecutive kernels (and, for lm_head, the argmax finalize launch).
+    `max_calls` caps the calls per graph (the counter runs, where every
+    dispatch is serialized): the copies used are then the first ones written,
+    which the later copies have pushed out of the caches."""
+    import torch
+    from int4_weight_only_04_amd import w4
+    traffic = read_config_traffic()
+    out = []
+    for c in CONFIGS:
+        layout, wb, sb, pw, ps, x = config_inputs(c)
+        n, k, g = c["n"], c["k"], c["group"]
+        wpad, spad = (wb + 4095) // 4096 * 4096, (sb + 255) // 256 * 256
+        copies = max(2, -(-COLD_BYTES // (wpad + spad)))
+        big_w = torch.empty((copies, wpad), dtype=torch.uint8, device="cuda")
+        big_s = torch.empty((copies, spad), dtype=torch.uint8, device="cuda")
+        big_w[0, :wb].copy_(torch.from_numpy(pw))
+        big_s[0, :sb].copy_(torch.from_numpy(ps))
+        big_w[1:] = big_w[0]
+        big_s[1:] = big_s[0]
+        dx = torch.from_numpy(x.view(np.int16)).cuda().view(torch.float16)
+        if c["kind"] == "gateup":
+            y = torch.empty(n // 2, dtype=torch.float16, device="cuda")
+        else:
+            y = torch.empty(n, dtype=torch.float32, device="cuda")
+        am = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+        ws = torch.zeros(w4.gemv_workspace_size(n, k, g, True), dtype=torch.uint8, device="cuda")
+        calls = max(copies, 32) if max_calls is None else min(max(copies, 32), max_calls)
+        print(f"[configs] {config_label(c)}: {copies} copies, {calls} calls x {replays} replays",
+              file=sys.stderr, flush=True)
+
+        def launch(st, c=c):
+            for i in range(calls):
+                cw, cs = big_w[i % copies], big_s[i % copies]
+                if c["kind"] == "gateup":
+                    w4.gemv_gateup_silu(cw, cs, dx, y, n, k, g, stream=st)
+                elif c["kind"] == "lmhead":
+                    w4.gemv(cw, cs, dx, y, n, k, g, argmax=am, workspace=ws, stream=st)
+                else:
+                    w4.gemv(cw, cs, dx, y, n, k, g, stream=st)
+
+        graph = capture(launch, stream)
+        ms = replay_ms(graph, stream, replays, 1)
+        del graph
+        us = ms * 1e3 / calls
+        alg = algorithmic_bytes(c["kind"], n, k, g)
+        gbs = alg / (us * 1e-6) / 1e9
+        t = traffic.get(c["name"]) if traffic else None
+        hbm = t["hbm_bytes_per_launch"] if t else None
+        out.append({
+            "config": config_label(c),
+            "us_per_gemv": round(us, 3),
+            "algorithmic_bytes": alg,
+            "gbs": round(gbs, 1),
+            "pct_of_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+            "floor_us_at_8tbs": round(alg / (HBM_PEAK_GBS * 1e9) * 1e6, 3),
+            "hbm_bytes_per_launch_fetch_write": hbm,
+            "fetch_gbs": round(hbm / (us * 1e-6) / 1e9, 1) if hbm else None,
+            "calls_timed": calls * replays,
+            "cold_copies": copies,
+            "cold_working_set_bytes": copies * (wb + sb),
+        })
+        del big_w, big_s
+        torch.cuda.synchronize()
+    return out
+
+
+def read_config_traffic(path: str = CONFIG_TRAFFIC_FILE):
+    """Per-config HBM bytes per call from the committed counter summary, or
+    None if absent or taken on another kernel source."""
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != kernel_source_hash(GEMV_SRCS):
+        return None
+    return t.get("configs")
+
+
+def write_traffic(fetch_csv: str, write_csv: str, copyf_csv: str, copyw_csv: str) -> int:
+    """Turn four `rocprofv3 --pmc` CSVs (FETCH_SIZE and WRITE_SIZE over
+    `bench.py --workload configs`, then over `bench.py --copy-probe`) into the
+    per-config traffic summary and the dominant kernel's: HBM bytes per call =
+    mean FETCH_SIZE x f + mean WRITE_SIZE x w (KiB), with f and w the ratios of
+    a plain 1 GiB copy's known bytes to what the same counters read for it."""
+    import csv
+
+    def per_kernel(path, counter):
+        acc = {}
+        order = []
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                key = (r["Kernel_Name"], int(r["Grid_Size"]))
+                if key not in acc:
+                    acc[key] = []
+                    order.append(key)
+                acc[key].append(float(r["Counter_Value"]))
+        return order, {k: sum(v) / len(v) for k, v in acc.items()}, {k: len(v) for k, v in acc.items()}
+
+    _, cf, _ = per_kernel(copyf_csv, "FETCH_SIZE")
+    _, cw, _ = per_kernel(copyw_csv, "WRITE_SIZE")
+    copy_kib = float(1 << 20)
+    ff = copy_kib / max(v for k, v in cf.items() if "copyBuffer" in k[0])
+    wf = copy_kib / max(v for k, v in cw.items() if "copyBuffer" in k[0])
+    order, fetch, count = per_kernel(fetch_csv, "FETCH_SIZE")
+    _, write, _ = per_kernel(write_csv, "WRITE_SIZE")
+    ours = [k for k in order if "w4i::" in k[0]]
+    # --workload configs launches, in this order: tiny, down, gate/up, lm_head GEMV, argmax finalize
+    names = ["tiny", "down", "gateup", "lmhead", "lmhead_finalize"]
+    if len(ours) != len(names):
+        print(f"expected {len(names)} kernels of the library, found {len(ours)}: {ours}", file=sys.stderr)
+        return 1
+    per = {}
+    for name, key in zip(names, ours):
+        per[name] = {"kernel": key[0][:160], "grid": key[1], "dispatches": count[key],
+                     "fetch_kib": round(fetch[key], 1), "write_kib": round(write.get(key, 0.0), 1),
+                     "hbm_bytes": int(round((fetch[key] * ff + write.get(key, 0.0) * wf) * 1024))}
+    fin = per.pop("lmhead_finalize")
+    per["lmhead"]["hbm_bytes"] += fin["hbm_bytes"]
+    per["lmhead"]["finalize"] = fin
+    configs = {}
+    for c in CONFIGS:
+        alg = algorithmic_bytes(c["kind"], c["n"], c["k"], c["group"])
+        e = per[c["name"]]
+        configs[c["name"]] = {"hbm_bytes_per_launch": e["hbm_bytes"], "algorithmic_bytes": alg,
+                              "ratio": round(e["hbm_bytes"] / alg, 4), "counters": e}
+    src_hash = kernel_source_hash(GEMV_SRCS)
+    summary = {"what": "HBM bytes per call of each config's kernels on cold buffers "
+                       "(rocprofv3 FETCH_SIZE and WRITE_SIZE means, calibrated by a 1 GiB copy)",
+               "kernel_source_sha256_16": src_hash, "fetch_factor": round(ff, 6), "write_factor": round(wf, 6),
+               "configs": configs,
+               "source": "bench.py --traffic-from over the four CSVs of the commands in "
+                         "gemv_configs_traffic.md (same folder)"}
+    with open(CONFIG_TRAFFIC_FILE, "w") as f:
+        json.dump(summary, f, indent=1)
+        f.write("\n")
+    gu = configs["gateup"]
+    dom = {"kernel": "gemv_w4_kernel<2, gate/up, split 2, depth 4, full, fp16 x> 37888x3584 g128",
+           "kernel_source_sha256_16": src_hash, "hbm_bytes_per_launch": gu["hbm_bytes_per_launch"],
+           "fetch_factor": round(ff, 6), "write_factor": round(wf, 6),
+           "source": "the gate/up config of traffic_configs.json (same folder)"}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(dom, f, indent=1)
+        f.write("\n")
+    print(json.dumps(summary, indent=1))
+    return 0
+
+
+class ClockSampler:
+    """Samples the GPU's engine and memory clocks, power and throttle status
+    (amdsmi GPU metrics) from a background thread while a measured loop runs."""
+
+    KEYS = ("current_gfxclk", "average_gfxclk_frequency", "current_uclk", "average_uclk_frequency",
+            "current_socket_power", "average_socket_power", "temperature_hotspot", "temperature_mem",
+            "throttle_status", "indep_throttle_status")
+
+    def __init__(self, period_s: float = 0.0005):
+        self.period = period_s
+        self.samples = []
+        self.error = None
+        self._stop = None
+        self._thread = None
+        self._handle = None
+
+    def _read(self):
+        import amdsmi
+        m = amdsmi.amdsmi_get_gpu_metrics_info(self._handle)
+        row = {}
+        for key in self.KEYS:
+            v = m.get(key)
+            if isinstance(v, (int, float)) and v not in (0xFFFF, 0xFFFFFFFF, 0xFFFFFFFFFFFFFFFF):
+                row[key] = v
+        gfx = m.get("current_gfxclks")
+        if isinstance(gfx, (list, tuple)):
+            vals = [v for v in gfx if isinstance(v, (int, float)) and 0 < v < 0xFFFF]
+            if vals:
+                row["current_gfxclks_min"] = min(vals)
+                row["current_gfxclks_max"] = max(vals)
+        return row
+
+    def __enter__(self):
+        import threading
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._handle = amdsmi.amdsmi_get_processor_handles()[0]
+            self.samples.append(self._read())
+        except Exception as e:  # clocks are context; the measurement does not depend on them
+            self.error = f"{type(e).__name__}: {e}"
+            return self
+        self._stop = threading.Event()
+
+        def loop():
+            while not self._stop.is_set():
+                try:
+                    self.samples.append(self._read())
+                except Exception as e:
+                    self.error = f"{type(e).__name__}: {e}"
+                    return
+                self._stop.wait(self.period)
+
+        self._thread = threading.Thread(target=loop, daemon=True)
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+        if self._handle is not None:
+            try:
+                import amdsmi
+                self.samples.append(self._read())
+                amdsmi.amdsmi_shut_down()
+            except Exception:
+                pass
+        return False
+
+    def summary(self):
+        if not self.samples:
+            return {"error": self.error or "no samples"}
+        keys = sorted({k for r in self.samples for k in r})
+        out = {"samples": len(self.samples)}
+        for k in keys:
+            vals = [r[k] for r in self.samples if k in r]
+            if "throttle" in k:
+                out[k] = sorted({int(v) for v in vals})
+            else:
+                out[k] = {"min": min(vals), "max": max(vals), "first": vals[0], "last": vals[-1]}
+        if self.error:
+            out["error"] = self.error
+        return out
+
+
+def time_graph_vs_eager(projs, stream, steps: int, rounds: int = 3):
+    """The captured sweep and the same launches issued eagerly by the
+    library, timed the same way (HIP events around `steps` sweeps) in
+    alternating rounds after one shared warm-up; medians of the rounds."""
+    from int4_weight_only_04_amd import w4
+    graph = w4.Sweep(projs, mode=w4.SWEEP_GRAPH)
+    eager = w4.Sweep(projs, mode=w4.SWEEP_EAGER)
+    for sw in (graph, eager):
+        time_graph(sw, stream, 2, 2)
+    g_ms, e_ms = [], []
+    for _ in range(rounds):
+        g_ms.append(time_graph(graph, stream, steps, 0)[0])
+        e_ms.append(time_graph(eager, stream, steps, 0)[0])
+    graph.close()
+    eager.close()
+    med = lambda v: sorted(v)[len(v) // 2]
+    return med(g_ms), med(e_ms), g_ms, e_ms
+
+
+def py_eager_sweep(projs, stream):
+    """One sweep launched projection by projection from Python through the
+    binding (the host-driven eager loop the pages compare graph capture with)."""
+    from int4_weight_only_04_amd import w4
+    for p in projs:
+        if p.kind == w4.PROJ_GATEUP_SILU:
+            w4.gemv_gateup_silu(p.packed_w, p.packed_s, p.x, p.out, p.n, p.k, p.group, stream=stream)
+        elif p.kind == w4.PROJ_LMHEAD_ARGMAX:
+            w4.gemv(p.packed_w, p.packed_s, p.x, p.out, p.n, p.k, p.group, argmax=p.argmax, workspace=p.workspace,
+                    stream=stream)
+        else:
+            w4.gemv(p.packed_w, p.packed_s, p.x, p.out, p.n, p.k, p.group, stream=stream)
+
+
+def time_py_eager(projs, stream, steps: int, warmup: int = 2):
+    import torch
+    for _ in range(warmup):
+        py_eager_sweep(projs, stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        py_eager_sweep(projs, stream)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def host_info():
+    """Host cores and CPU model, as the process sees them."""
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    omp = os.environ.get("OMP_NUM_THREADS")
+    threads = min(avail, int(omp)) if omp and omp.isdigit() and int(omp) > 0 else avail
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "affinity_cpus": avail, "omp_num_threads": omp, "threads": threads,
+            "cpu_model": model}
+
+
+def oracle_gemv_timed(pw, ps, x, n, k, g, kind, threads: int):
+    """The oracle's GEMV (fp64 C, unchanged) over all rows, the rows split in
+    `threads` contiguous ranges run by a thread pool (the C call releases the
+    interpreter lock); gate/up adds the SiLU gate.  Seconds."""
+    import oracle
+    from concurrent.futures import ThreadPoolExecutor
+    gateup = kind == "gateup"
+    t0 = time.perf_counter()
+    if threads == 1:
+        y, _ = oracle.gemv_packed(pw, ps, x, n, k, g, gateup=gateup)
+    else:
+        cuts = np.linspace(0, n, threads + 1).astype(np.int64)
+        parts = [np.arange(cuts[i], cuts[i + 1], dtype=np.int64) for i in range(threads)]
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            ys = list(ex.map(lambda r: oracle.gemv_packed(pw, ps, x, n, k, g, gateup=gateup, rows=r)[0], parts))
+        y = np.concatenate(ys)
+    if gateup:
+        oracle.silu_gate(y)
+    if kind == "lmhead":
+        int(np.argmax(y))
+    return time.perf_counter() - t0
+
+
+def cpu_baseline():
+    """The oracle as it stands (fp64 C, never tuned), on the host's cores: once
+    single-threaded and once over all available cores (rows split across a
+    thread pool).  Per config one call each; the sweep figure is layer 0's
+    four projections, run in full, with the whole sweep estimated as
+    28 x layer 0 + lm_head."""
+    from int4_weight_only_04_amd import w4
+    host = host_info()
+    nt = host["threads"]
+    per_config = {}
+    lm_s = {}
+    for c in CONFIGS:
+        layout, wb, sb, pw, ps, x = config_inputs(c)
+        alg = algorithmic_bytes(c["kind"], c["n"], c["k"], c["group"])
+        t1 = oracle_gemv_timed(pw, ps, x, c["n"], c["k"], c["group"], c["kind"], 1)
+        tn = oracle_gemv_timed(pw, ps, x, c["n"], c["k"], c["group"], c["kind"], nt)
+        per_config[c["name"]] = {"ms_1_thread": round(t1 * 1e3, 3), f"ms_{nt}_threads": round(tn * 1e3, 3),
+                                 "gbs_1_thread": round(alg / t1 / 1e9, 4),
+                                 f"gbs_{nt}_threads": round(alg / tn / 1e9, 4)}
+        if c["name"] == "lmhead":
+            lm_s = {1: t1, nt: tn}
+    layer = synthetic.sweep_projections(1)
+    total = 0
+    t = {1: 0.0, nt: 0.0}
+    for p in layer:
         layout = "gateup" if p.kind == "gateup" else "plain"
         wb, sb = w4.packed_size(p.n, p.k, p.group, layout)
         pw, ps, x = synthetic.packed_random(p.seed, wb, sb // 2, p.k)
-        t0 = time.perf_counter()
-        y, _ = oracle.gemv_packed(pw, ps, x, p.n, p.k, p.group, gateup=(layout == "gateup"))
-        if p.kind == "gateup":
-            oracle.silu_gate(y)
-        t_total += time.perf_counter() - t0
-        total_bytes += algorithmic_bytes(p.kind, p.n, p.k, p.group)
+        for th in (1, nt):
+            t[th] += oracle_gemv_timed(pw, ps, x, p.n, p.k, p.group, p.kind, th)
+        total += algorithmic_bytes(p.kind, p.n, p.k, p.group)
+    layers = synthetic.LAYERS
+    est = {th: (layers * t[th] + lm_s[th]) * 1e3 for th in (1, nt)}
     return {
-        "value": total_bytes / t_total / 1e9,
+        "value": round(total / t[nt] / 1e9, 4),
         "unit": "GB/s",
-        "cores": 1,
+        "cores": nt,
         "kind": "oracle",
-        "sample": "layer 0 of the sweep (qkv, o_proj, gate/up+silu, down), all rows, "
-                  f"{total_bytes} algorithmic bytes in {t_total:.1f} s, single-threaded fp64 C",
-        "seconds": t_total,
+        "sample": f"layer 0 of the sweep (qkv, o_proj, gate/up+silu, down), all rows, {total} algorithmic "
+                  f"bytes in {t[nt]:.2f} s on {nt} threads (rows split across a thread pool; fp64 C oracle)",
+        "single_thread": {"value": round(total / t[1] / 1e9, 4), "unit": "GB/s", "cores": 1,
+                          "seconds": round(t[1], 3)},
+        "sweep_ms_estimate": {"1_thread": round(est[1], 1), f"{nt}_threads": round(est[nt], 1),
+                              "how": f"{layers} x layer 0 + lm_head, each timed in full"},
+        "per_config": per_config,
+        "host": host,
     }
 
 
@@ -741,7 +1155,7 @@ def run_step(args) -> int:
     hbuf = torch.empty(synthetic.MLP, dtype=torch.float16, device="cuda")
     gu = [w4.Proj(w4.PROJ_GATEUP_SILU, 2 * synthetic.MLP, synthetic.HIDDEN, synthetic.GROUP, L.gateup_w, L.gateup_s,
                   x, hbuf) for L in model["layers"]]
-    gu_mean_ms, gu_launches = time_dominant_kernel(gu, stream)
+    gu_mean_ms, gu_launches, _, _ = time_dominant_kernel(gu, stream)
     gu_bytes = algorithmic_bytes("gateup", 2 * synthetic.MLP, synthetic.HIDDEN, synthetic.GROUP)
     gu_gbs = gu_bytes / (gu_mean_ms * 1e-3) / 1e9
     graph.close()
@@ -966,14 +1380,22 @@ def main(argv=None):
     ap.add_argument("--layers", type=int, default=synthetic.LAYERS)
     ap.add_argument("--eager-steps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", choices=("decode", "prefill", "attention", "step", "w4a8"), default="decode",
+    ap.add_argument("--workload", choices=("decode", "prefill", "attention", "step", "w4a8", "configs"),
+                    default="decode",
                     help="decode: the per-token GEMV sweep (default); prefill: the 512-token GEMM sweep; "
                          "attention: 28 layers' paged-KV decode attention at a 4096-token context; "
                          "step: the full decode step (tokens 512.. after a 512-token prompt); "
-                         "w4a8: the sweep with int8 activations")
+                         "w4a8: the sweep with int8 activations; configs: only the per-config GEMV "
+                         "timings on cold buffers (the run the traffic counters are taken over)")
+    ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="write profiles/traffic_configs.json (and the dominant kernel's traffic file) from "
+                         "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE CSVs of --workload configs and --copy-probe; "
+                         "host only")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args(argv)
+    if args.traffic_from:
+        return write_traffic(*args.traffic_from)
     if args.steps is None:
         args.steps = 128 if args.workload == "step" else 50
 
@@ -1007,6 +1429,10 @@ def main(argv=None):
         return run_step(args)
     if args.workload == "w4a8":
         return run_w4a8(args)
+    if args.workload == "configs":
+        stream = torch.cuda.Stream()
+        print(json.dumps({"per_config": time_configs(stream, replays=1, max_calls=32)}), flush=True)
+        return 0
 
     print(f"[bench] building sweep ({args.layers} layers)", file=sys.stderr, flush=True)
     specs, projs = build_sweep(args.layers)
@@ -1016,20 +1442,25 @@ def main(argv=None):
     print("[bench] graph sweep", file=sys.stderr, flush=True)
     graph = w4.Sweep(projs, use_graph=True)
     ev_ms, wall_ms = time_graph(graph, stream, args.steps, args.warmup)
+    graph.close()
 
-    print("[bench] eager sweep", file=sys.stderr, flush=True)
-    eager = w4.Sweep(projs, use_graph=False)
-    eager_ms, eager_wall_ms = time_graph(eager, stream, args.eager_steps, 2)
-    eager.close()
+    print("[bench] graph vs eager (alternating rounds)", file=sys.stderr, flush=True)
+    g_med, e_med, g_rounds, e_rounds = time_graph_vs_eager(projs, stream, args.steps)
+    print("[bench] python-driven eager sweep", file=sys.stderr, flush=True)
+    py_ms = time_py_eager(projs, stream, args.eager_steps)
 
-    print("[bench] dominant kernel", file=sys.stderr, flush=True)
-    gu_mean_ms, gu_launches = time_dominant_kernel(projs, stream)
+    print("[bench] dominant kernel (+ clocks)", file=sys.stderr, flush=True)
+    gu_mean_ms, gu_launches, gu_sustained, gu_clocks = time_dominant_kernel(projs, stream)
     print("[bench] pure-read ceiling (113 read-only launches)", file=sys.stderr, flush=True)
     read_ms, read_bytes, stream_gbs = time_pure_read_sweep(specs, stream, args.steps, args.warmup)
     gp = next(p for p in specs if p.kind == "gateup")
     gu_bytes = algorithmic_bytes("gateup", gp.n, gp.k, gp.group)
     gu_gbs = gu_bytes / (gu_mean_ms * 1e-3) / 1e9
-    graph.close()
+    del projs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    print("[bench] per-config GEMVs on cold buffers", file=sys.stderr, flush=True)
+    per_config = time_configs(stream)
 
     value = alg_bytes / (ev_ms * 1e-3) / 1e9
     out = {
@@ -1054,12 +1485,19 @@ def main(argv=None):
             "algorithmic_bytes_per_step": alg_bytes,
             "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
             "wall_ms_per_step": round(wall_ms, 4),
-            "eager_ms_per_step": round(eager_ms, 4),
-            "graph_speedup_vs_eager": round(eager_ms / ev_ms, 3),
+            "graph_ms_per_step_alternating": round(g_med, 4),
+            "eager_ms_per_step": round(e_med, 4),
+            "graph_speedup_vs_eager": round(e_med / g_med, 3),
+            "graph_vs_eager_rounds_ms": {"graph": [round(v, 4) for v in g_rounds],
+                                         "eager": [round(v, 4) for v in e_rounds]},
+            "python_eager_ms_per_step": round(py_ms, 4),
+            "graph_speedup_vs_python_eager": round(py_ms / g_med, 3),
             "pure_read_sweep_ms": round(read_ms, 4),
             "pure_read_sweep_gbs": round(read_bytes / (read_ms * 1e-3) / 1e9, 1),
             "sweep_time_vs_pure_read": round(ev_ms / read_ms, 3),
             "stream_read_1gib_gbs": round(stream_gbs, 1),
+            "per_config": per_config,
+            "pages_context_h100": PAGES_CONTEXT_H100,
         },
         "roofline": {
             "kernel": "gemv_w4_kernel<2, gate/up+silu> 37888x3584 g128",
@@ -1072,6 +1510,8 @@ def main(argv=None):
             "algorithmic_bytes_per_launch": gu_bytes,
             "avg_launch_us": round(gu_mean_ms * 1e3, 3),
             "launches_timed": gu_launches,
+            "clocks": gu_clocks,
+            "sustained": gu_sustained,
         },
         "cpu_baseline": None,
     }
