@@ -871,19 +871,22 @@ def attn_cpu_baseline(layers: int = 12):
 def run_attention(args) -> int:
     """28 layers' decode attention at a 4096-token context: two sets of 28
     caches (470 MB, beyond the 256 MB Infinity Cache) alternate, each layer
-    with its own seeded cache and a permuted page table, in one HIP graph."""
+    with its own seeded cache, all of one sequence's permuted page table, in
+    one HIP graph."""
     import torch
     from int4_weight_only_04_amd import w4
     layers = args.layers
     npages = ATTN_CTX // ATTN_PAGE
     dev = "cuda"
     g = torch.Generator(device="cpu").manual_seed(4001)
+    # one sequence: its page table (a permutation of the pages) is shared by
+    # every layer, as a paged cache's block table belongs to the sequence
+    table = torch.randperm(npages, generator=g).to(torch.int32).to(dev)
     calls = []
     for i in range(2 * layers):
         kc = torch.randn((npages, ATTN_KV_HEADS, ATTN_PAGE, 128), generator=g).to(torch.float16).to(dev)
         vc = torch.randn((npages, ATTN_KV_HEADS, ATTN_PAGE, 128), generator=g).to(torch.float16).to(dev)
         q = torch.randn((ATTN_HEADS, 128), generator=g).to(torch.float16).to(dev)
-        table = torch.randperm(npages, generator=g).to(torch.int32).to(dev)
         out = torch.empty((ATTN_HEADS, 128), dtype=torch.float16, device=dev)
         calls.append((q, kc, vc, table, out))
     ctx = torch.full((1,), ATTN_CTX, dtype=torch.int32, device=dev)

@@ -97,18 +97,51 @@ __device__ __forceinline__ float row16_sum(float v)
     return v;
 }
 
-__device__ __forceinline__ float wave_max(float v)
+// Maximum over each row of 16 lanes (lane 15 of the row ends with it); a lane
+// whose source lies outside the row keeps its own value.
+__device__ __forceinline__ float row16_max(float v)
+{
+#define W4A_MAX_STEP(ctrl)                                                                             \
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v),      \
+                                                                     __builtin_bit_cast(int, v), ctrl, \
+                                                                     0xF, 0xF, false)))
+    W4A_MAX_STEP(0x111);
+    W4A_MAX_STEP(0x112);
+    W4A_MAX_STEP(0x114);
+    W4A_MAX_STEP(0x118);
+#undef W4A_MAX_STEP
+    return v;
+}
+
+// lane 15 + 16r of v, for the four rows r (uniform values)
+__device__ __forceinline__ void row_totals(float v, float (&r)[4])
 {
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-    return v;
+    for (int q = 0; q < 4; ++q)
+        r[q] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16 * q + 15));
+}
+
+// the value of this lane's row among four uniform row values
+__device__ __forceinline__ float of_row(const float (&r)[4], int lane)
+{
+    const int q = lane >> 4;
+    return q == 0 ? r[0] : (q == 1 ? r[1] : (q == 2 ? r[2] : r[3]));
+}
+
+// Whole-wave maximum and sum (uniform results), from the row reductions and
+// four lane reads: no LDS traffic.  The sum adds the rows in a fixed order.
+__device__ __forceinline__ float wave_max(float v)
+{
+    float r[4];
+    row_totals(row16_max(v), r);
+    return fmaxf(fmaxf(r[0], r[1]), fmaxf(r[2], r[3]));
 }
 
 __device__ __forceinline__ float wave_sum(float v)
 {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-    return v;
+    float r[4];
+    row_totals(row16_sum(v), r);
+    return ((r[0] + r[1]) + r[2]) + r[3];
 }
 
 __device__ __forceinline__ float round_half(float v) { return (float)(_Float16)v; }
@@ -129,18 +162,76 @@ __device__ __forceinline__ void rope_pair(const AttnArgs& a, int64_t base, int i
     r1 = x1 * t.x + x0 * t.y;
 }
 
-// GQ query heads per KV head (1..8).  ROPE: the query heads and the new
-// token's key are rotated here from the QKV projection (fp16-rounded, as the
-// stored q and cache are), and the new token's k and v are appended to the
-// cache by the workgroup whose chunk holds it; that workgroup uses them
-// directly, and no other workgroup reads that slot.
+typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ h4_t as_h4(uint32_t lo, uint32_t hi)
+{
+    typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
+    u2_t w;
+    w.x = lo;
+    w.y = hi;
+    return __builtin_bit_cast(h4_t, w);
+}
+
+// Sum and maximum over the four 16-lane rows, per column (lanes l, l ^ 16,
+// l ^ 32, l ^ 48): two lane-half swaps, every lane gets the result, and the
+// lanes of one column add the same operands in the same order.
+__device__ __forceinline__ float cols_sum(float v)
+{
+    const auto a = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v), __builtin_bit_cast(uint32_t, v),
+                                                    false, false);
+    const float p = __builtin_bit_cast(float, (uint32_t)a[0]) + __builtin_bit_cast(float, (uint32_t)a[1]);
+    const auto b = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, p), __builtin_bit_cast(uint32_t, p),
+                                                    false, false);
+    return __builtin_bit_cast(float, (uint32_t)b[0]) + __builtin_bit_cast(float, (uint32_t)b[1]);
+}
+
+__device__ __forceinline__ float cols_max(float v)
+{
+    const auto a = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v), __builtin_bit_cast(uint32_t, v),
+                                                    false, false);
+    const float p = fmaxf(__builtin_bit_cast(float, (uint32_t)a[0]), __builtin_bit_cast(float, (uint32_t)a[1]));
+    const auto b = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, p), __builtin_bit_cast(uint32_t, p),
+                                                    false, false);
+    return fmaxf(__builtin_bit_cast(float, (uint32_t)b[0]), __builtin_bit_cast(float, (uint32_t)b[1]));
+}
+
+__device__ __forceinline__ uint32_t pack_half2(float lo, float hi)
+{
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+}
+
+// GQ query heads per KV head (1..8).  Wave w of a workgroup takes the
+// chunk's tokens [16w, 16w + 16) and runs both products of its part on the
+// matrix cores (v_mfma_f32_16x16x16_f16: fp16 operands, exact products,
+// fp32 sums), the query heads padded to 16 with zeros:
+//   * scores S^T = K Q^T: the 128 dimensions are the reduction; lane
+//     (row r = lane / 16, column c = lane % 16) supplies token c's K and head
+//     c's q at dimensions 32 r + 4 s + (0..3) in step s, so each lane reads
+//     64 contiguous bytes of one K row, and the result leaves lane (r, c)
+//     with tokens 4r .. 4r + 3 of head c;
+//   * that is the operand layout of P in O = P V, so the softmax weights
+//     stay in registers (rounded to fp16 for the product; the sum of weights
+//     is taken over the same rounded values);
+//   * V is staged in LDS (each wave its own 16 rows, masked tokens as zeros,
+//     padded rows so the four row groups fall in different banks), and
+//     lane (r, c) reads tokens 4r .. 4r + 3 of dimension 16 n + c for tile n.
+// The four waves' parts are merged once, rescaled to the chunk maximum.
+// ROPE: the query heads and the new token's key are rotated here from the
+// QKV projection (fp16-rounded, as the stored q and cache are), and the new
+// token's k and v are appended to the cache by the workgroup whose chunk
+// holds it; that workgroup uses them directly, and no other workgroup reads
+// that slot.
 template <int GQ, bool ROPE>
 __global__ void __launch_bounds__(kAttnThreads) attn_partial_kernel(AttnArgs a)
 {
-    __shared__ float s_sc[GQ][kChunk];
+    constexpr int kVRow = kDim / 2 + 2;  // LDS words per staged V row (2 words of padding)
+    __shared__ uint32_t s_v[4][16][kVRow];
     __shared__ float s_o[4][GQ][kDim];
-    __shared__ float s_m[GQ];
-    __shared__ float s_l[GQ];
+    __shared__ float s_m[4][GQ];     // per wave: its 16 tokens' maximum and sum of weights, per head
+    __shared__ float s_l[4][GQ];
     __shared__ float s_q[ROPE ? GQ : 1][kDim];
     __shared__ float s_knew[ROPE ? kDim : 1];
     __shared__ uint32_t s_vnew[ROPE ? kDim / 2 : 1];
@@ -151,23 +242,20 @@ __global__ void __launch_bounds__(kAttnThreads) attn_partial_kernel(AttnArgs a)
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int t0 = chunk * kChunk;
+    const int col = lane & 15;   // MFMA column: this lane's K token, q head, V dimension within a tile
+    const int rg = lane >> 4;    // MFMA row group
     float* po = a.part_o + ((int64_t)chunk * a.n_heads + (int64_t)g * GQ) * kDim;
     float* pml = a.part_ml + ((int64_t)chunk * a.n_heads + (int64_t)g * GQ) * 2;
 
     // ---- first round: the context length (or position) and the page-table
-    // entries of this lane's K and V rows; a chunk past the context ends
-    // here, before any K/V traffic (the combine never reads its partial).
-    // Second round: q and the K row slices and V words, all issued before any
-    // math (rows of tokens past max_ctx are read from the last one; past the
-    // context they are masked below).
-    const int dpart = lane & 15;
-    const int tq = lane >> 4;
-    int64_t krow[4], vrow[16];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int t = t0 + wave * 16 + i * 4 + tq;
-        krow[i] = cache_row(a, t < a.max_ctx ? t : a.max_ctx - 1, g);
-    }
+    // entries of this lane's K row and of the wave's 16 V rows; a chunk past
+    // the context ends here, before any K/V traffic (the combine never reads
+    // its partial).  Second round: q and the K and V rows, all issued before
+    // any math (rows of tokens past max_ctx are read from the last one; past
+    // the context they are masked below).
+    const int tk = t0 + wave * 16 + col;
+    const int64_t krow = cache_row(a, tk < a.max_ctx ? tk : a.max_ctx - 1, g);
+    int64_t vrow[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
         const int t = t0 + wave * 16 + j;
@@ -182,14 +270,15 @@ __global__ void __launch_bounds__(kAttnThreads) attn_partial_kernel(AttnArgs a)
         ctx = clamp_ctx(a);
     }
     if (t0 >= ctx) return;  // whole workgroup, before any barrier
-    uint4 qv[ROPE ? 1 : GQ];
+    uint4 qv[4];
     if constexpr (!ROPE) {
+        const int hq = col < GQ ? col : 0;
 #pragma unroll
-        for (int h = 0; h < GQ; ++h) qv[h] = a.q[(int64_t)(g * GQ + h) * (kDim / 8) + dpart];
+        for (int m = 0; m < 4; ++m) qv[m] = a.q[(int64_t)(g * GQ + hq) * (kDim / 8) + rg * 4 + m];
     }
     uint4 kv[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) kv[i] = a.kc[krow[i] * (kDim / 8) + dpart];
+    for (int m = 0; m < 4; ++m) kv[m] = a.kc[krow * (kDim / 8) + rg * 4 + m];
     uint32_t vv[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) vv[j] = a.vc[vrow[j] * (kDim / 2) + lane];
@@ -240,8 +329,7 @@ __global__ void __launch_bounds__(kAttnThreads) attn_partial_kernel(AttnArgs a)
                         v0 += a.bias[vb];
                         v1 += a.bias[vb + 1];
                     }
-                    s_vnew[w] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v0) |
-                                ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v1) << 16);
+                    s_vnew[w] = pack_half2(v0, v1);
                 }
             }
         }
@@ -253,8 +341,7 @@ __global__ void __launch_bounds__(kAttnThreads) attn_partial_kernel(AttnArgs a)
             const int64_t row = cache_row(a, pos, g);
             if (tid < 64) {
                 reinterpret_cast<uint32_t*>(a.kc_w)[row * (kDim / 2) + tid] =
-                    (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)s_knew[2 * tid]) |
-                    ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)s_knew[2 * tid + 1]) << 16);
+                    pack_half2(s_knew[2 * tid], s_knew[2 * tid + 1]);
             } else if (tid < 128) {
                 a.vc_w[row * (kDim / 2) + (tid - 64)] = s_vnew[tid - 64];
             }
@@ -263,169 +350,184 @@ __global__ void __launch_bounds__(kAttnThreads) attn_partial_kernel(AttnArgs a)
             for (int i = tid; i < GQ * kDim; i += kAttnThreads)
                 a.q_out[(int64_t)g * GQ * kDim + i] = __builtin_bit_cast(uint16_t, (_Float16)s_q[i / kDim][i % kDim]);
         }
-    }
-    // ---- scores: 16 lanes per token, 8 dimensions per lane, 4 tokens per wave step
-    float qr[GQ][8];
+        const int hq = col < GQ ? col : 0;
 #pragma unroll
-    for (int h = 0; h < GQ; ++h) {
-        if constexpr (ROPE) {
+        for (int m = 0; m < 4; ++m) {
+            const float* qs = &s_q[hq][rg * 32 + m * 8];
+            qv[m] = make_uint4(pack_half2(qs[0], qs[1]), pack_half2(qs[2], qs[3]), pack_half2(qs[4], qs[5]),
+                               pack_half2(qs[6], qs[7]));
+        }
+        if (tk == pos) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) qr[h][j] = s_q[h][8 * dpart + j];
-        } else {
-            half8_to_float(qv[h], qr[h]);
+            for (int m = 0; m < 4; ++m) {
+                const float* ks = &s_knew[rg * 32 + m * 8];
+                kv[m] = make_uint4(pack_half2(ks[0], ks[1]), pack_half2(ks[2], ks[3]), pack_half2(ks[4], ks[5]),
+                                   pack_half2(ks[6], ks[7]));
+            }
         }
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int tl = wave * 16 + i * 4 + tq;
-        const bool valid = t0 + tl < ctx;
-        float kf[8];
-        half8_to_float(kv[i], kf);
-        if (ROPE && t0 + tl == pos) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) kf[j] = s_knew[8 * dpart + j];
-        }
-#pragma unroll
-        for (int h = 0; h < GQ; ++h) {
-            float d = 0.0f;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) d = __builtin_fmaf(qr[h][j], kf[j], d);
-            d = row16_sum(d);  // total in lane 15 of each 16-lane row
-            if (dpart == 15) s_sc[h][tl] = valid ? d * a.scale : -__builtin_inff();
-        }
-    }
-    __syncthreads();
 
-    // ---- chunk softmax: one wave per head, one lane per token
-    for (int h = wave; h < GQ; h += 4) {
-        const float v = s_sc[h][lane];
-        const float m = wave_max(v);
-        const float e = v == -__builtin_inff() ? 0.0f : __expf(v - m);
-        const float l = wave_sum(e);
-        s_sc[h][lane] = e;
-        if (lane == 0) {
-            s_m[h] = m;
-            s_l[h] = l;
-        }
-    }
-    __syncthreads();
-
-    // ---- unnormalised output: wave w takes tokens [16w, 16w+16), lane = 2 dimensions
-    float acc[GQ][2];
-#pragma unroll
-    for (int h = 0; h < GQ; ++h) acc[h][0] = acc[h][1] = 0.0f;
+    // ---- stage this wave's V rows (tokens past the context as zeros, so a
+    // row holding an infinity contributes exactly 0); only this wave reads
+    // them, and a wave's LDS accesses complete in order
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-        const int tl = wave * 16 + j;
-        // a token past the context (weight 0) contributes exactly 0, even if
-        // the row it was read from holds an infinity
-        const uint32_t keep = 0u - (uint32_t)(t0 + tl < ctx);
-        const uint32_t vw = (ROPE && t0 + tl == pos) ? s_vnew[lane] : vv[j];
-        const float v0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(vw & keep & 0xFFFFu));
-        const float v1 = (float)__builtin_bit_cast(_Float16, (uint16_t)((vw & keep) >> 16));
+        const int t = t0 + wave * 16 + j;
+        const uint32_t keep = 0u - (uint32_t)(t < ctx);
+        const uint32_t vw = (ROPE && t == pos) ? s_vnew[lane] : vv[j];
+        s_v[wave][j][lane] = vw & keep;
+    }
+
+    // ---- scores S^T = K Q^T (heads past GQ get q = 0)
+    const uint32_t qkeep = 0u - (uint32_t)(col < GQ);
+    f4_t sacc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int h = 0; h < GQ; ++h) {
-            const float w = s_sc[h][tl];  // 0 for tokens past the context
-            acc[h][0] = __builtin_fmaf(w, v0, acc[h][0]);
-            acc[h][1] = __builtin_fmaf(w, v1, acc[h][1]);
+    for (int st = 0; st < 8; ++st) {
+        const uint4& k4 = kv[st >> 1];
+        const uint4& q4 = qv[st >> 1];
+        const h4_t ka = (st & 1) ? as_h4(k4.z, k4.w) : as_h4(k4.x, k4.y);
+        const h4_t qb = (st & 1) ? as_h4(q4.z & qkeep, q4.w & qkeep) : as_h4(q4.x & qkeep, q4.y & qkeep);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x16f16(ka, qb, sacc, 0, 0, 0);
+    }
+
+    // ---- softmax over the wave's 16 tokens, per head (column): lane (r, c)
+    // holds tokens 4r .. 4r + 3 of head c
+    float sc[4];
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int t = t0 + wave * 16 + rg * 4 + i;
+        sc[i] = (t < ctx && col < GQ) ? sacc[i] * a.scale : -__builtin_inff();
+        mx = fmaxf(mx, sc[i]);
+    }
+    const float m = cols_max(mx);
+    float e[4], lsum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        // a token past the context, or a head past GQ, weighs exactly 0
+        e[i] = (float)(_Float16)(sc[i] == -__builtin_inff() ? 0.0f : __expf(sc[i] - m));
+        lsum += e[i];
+    }
+    const float l = cols_sum(lsum);
+    const h4_t pa = as_h4(pack_half2(e[0], e[1]), pack_half2(e[2], e[3]));
+
+    // ---- this wave's unnormalised output O = P V, 8 tiles of 16 dimensions
+    const _Float16* vrowp = reinterpret_cast<const _Float16*>(&s_v[wave][rg * 4][0]);
+    f4_t oacc[8];
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+        h4_t vb;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vb[i] = vrowp[i * (2 * kVRow) + n * 16 + col];
+        oacc[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, vb, f4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+    }
+    // lane (r, c) holds heads 4r .. 4r + 3 of dimensions 16 n + c
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int h = rg * 4 + i;
+        if (h < GQ) {
+#pragma unroll
+            for (int n = 0; n < 8; ++n) s_o[wave][h][n * 16 + col] = oacc[n][i];
         }
     }
-#pragma unroll
-    for (int h = 0; h < GQ; ++h) {
-        s_o[wave][h][2 * lane] = acc[h][0];
-        s_o[wave][h][2 * lane + 1] = acc[h][1];
+    if (rg == 0 && col < GQ) {
+        s_m[wave][col] = m;
+        s_l[wave][col] = l;
     }
     __syncthreads();
+
+    // ---- the chunk's partial: the four waves' parts rescaled to the chunk
+    // maximum (finite: the chunk's first token is inside the context) and
+    // added in wave order; a wave without a token in the context has maximum
+    // -inf, weight 0 and sum 0
     for (int i = tid; i < GQ * kDim; i += kAttnThreads) {
         const int h = i / kDim, d = i % kDim;
-        po[i] = ((s_o[0][h][d] + s_o[1][h][d]) + s_o[2][h][d]) + s_o[3][h][d];
+        const float mm = fmaxf(fmaxf(s_m[0][h], s_m[1][h]), fmaxf(s_m[2][h], s_m[3][h]));
+        float o = 0.0f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) o = __builtin_fmaf(__expf(s_m[w][h] - mm), s_o[w][h][d], o);
+        po[i] = o;
     }
     if (tid < GQ) {
-        pml[2 * tid] = s_m[tid];
-        pml[2 * tid + 1] = s_l[tid];
+        const float mm = fmaxf(fmaxf(s_m[0][tid], s_m[1][tid]), fmaxf(s_m[2][tid], s_m[3][tid]));
+        float ls = 0.0f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) ls = __builtin_fmaf(__expf(s_m[w][tid] - mm), s_l[w][tid], ls);
+        pml[2 * tid] = mm;
+        pml[2 * tid + 1] = ls;
     }
 }
 
-// One workgroup per query head: the chunk maxima and sums are reduced across
-// the workgroup, then thread (d, j) sums dimension d over the chunks j, j+8,
-// ... with independent loads, and the eight partial sums meet in LDS in a
-// fixed order.
-constexpr int kCombThreads = 1024;
-
-__device__ __forceinline__ float block_reduce(float v, float* red, bool is_max)
-{
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const float o = __shfl_xor(v, off);
-        v = is_max ? fmaxf(v, o) : v + o;
-    }
-    if (lane == 0) red[wave] = v;
-    __syncthreads();
-    float r = red[0];
-#pragma unroll
-    for (int w = 1; w < kCombThreads / 64; ++w) r = is_max ? fmaxf(r, red[w]) : r + red[w];
-    __syncthreads();
-    return r;
-}
+// One workgroup of eight waves per query head; thread (j, d) = (tid / 128,
+// tid % 128) adds dimension d over the chunks j, j + 4, ... in chunk order.
+// Every wave finds the chunks' global maximum and sum of weights itself
+// (lane c holds chunk c; row reductions and lane reads, uniform results), the
+// chunk weights come from lane c by a lane read, and the four chunk lanes'
+// sums meet once in LDS, added in a fixed order.
+constexpr int kCombThreads = 512;
 
 __global__ void __launch_bounds__(kCombThreads) attn_combine_kernel(AttnArgs a)
 {
-    constexpr int J = kCombThreads / kDim;  // 8 chunk lanes per dimension
-    constexpr int kMaxPer = 8;              // chunks per thread held in registers
-    __shared__ float red[kCombThreads / 64];
-    __shared__ float part[J][kDim];
+    __shared__ float part[4][kDim];
     const int h = blockIdx.x;
     const int tid = threadIdx.x;
+    const int lane = tid & 63;
     const int d = tid & (kDim - 1);
-    const int j = tid / kDim;
-    const int chunks = (a.max_ctx + kChunk - 1) / kChunk;
+    const int j = __builtin_amdgcn_readfirstlane(tid >> 7);  // uniform: a wave lies in one chunk lane
     const int ctx = clamp_ctx(a);
-    const int nch = (ctx + kChunk - 1) / kChunk;
-    // the first J * kMaxPer chunks: loads issued together, before the maxima
-    float mv[kMaxPer], lv[kMaxPer], ov[kMaxPer];
+    const int nch = (ctx + kChunk - 1) / kChunk;   // 1 .. chunks
+    const float2* ml = reinterpret_cast<const float2*>(a.part_ml);
+    const float* po = a.part_o + (int64_t)h * kDim + d;
+    const int64_t ostride = (int64_t)a.n_heads * kDim;
+    float o = 0.0f, l;
+    if (nch <= 64) {
+        // every load in one round: the lane's chunk (max, sum) and this
+        // thread's 16 partials (chunks past the context read the last one and
+        // are skipped below)
+        const int c = lane < nch ? lane : nch - 1;
+        const float2 mc = ml[(int64_t)c * a.n_heads + h];
+        float ov[16];
 #pragma unroll
-    for (int i = 0; i < kMaxPer; ++i) {
-        int c = j + J * i;
-        if (c >= chunks) c = chunks - 1;  // in bounds; masked below
-        const float* ml = a.part_ml + ((int64_t)c * a.n_heads + h) * 2;
-        mv[i] = ml[0];
-        lv[i] = ml[1];
-        ov[i] = a.part_o[((int64_t)c * a.n_heads + h) * kDim + d];
-    }
-    float mx = -__builtin_inff();
+        for (int i = 0; i < 16; ++i) {
+            const int cc = j + 4 * i;
+            ov[i] = po[(int64_t)(cc < nch ? cc : nch - 1) * ostride];
+        }
+        const float m = wave_max(lane < nch ? mc.x : -__builtin_inff());
+        const float f = lane < nch ? __expf(mc.x - m) : 0.0f;
+        l = wave_sum(f * (lane < nch ? mc.y : 0.0f));
 #pragma unroll
-    for (int i = 0; i < kMaxPer; ++i)
-        if (j + J * i < nch) mx = fmaxf(mx, mv[i]);
-    for (int c = j + J * kMaxPer; c < nch; c += J) mx = fmaxf(mx, a.part_ml[((int64_t)c * a.n_heads + h) * 2]);
-    mx = block_reduce(mx, red, true);
-    float l = 0.0f, o = 0.0f;
-#pragma unroll
-    for (int i = 0; i < kMaxPer; ++i) {
-        if (j + J * i < nch) {
-            const float f = __expf(mv[i] - mx);
-            l = __builtin_fmaf(f, lv[i], l);
-            o = __builtin_fmaf(f, ov[i], o);
+        for (int i = 0; i < 16; ++i) {
+            const int cc = j + 4 * i;
+            if (cc < nch) {
+                const float fi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), cc));
+                o = __builtin_fmaf(fi, ov[i], o);
+            }
+        }
+    } else {
+        // longer contexts: the maximum over all chunks first, then blocks of 64
+        float mx = -__builtin_inff();
+        for (int c0 = 0; c0 < nch; c0 += 64) {
+            const int c = c0 + lane;
+            mx = fmaxf(mx, c < nch ? ml[(int64_t)c * a.n_heads + h].x : -__builtin_inff());
+        }
+        const float m = wave_max(mx);
+        l = 0.0f;
+        for (int c0 = 0; c0 < nch; c0 += 64) {
+            const int c = c0 + lane;
+            const float2 mc = ml[(int64_t)(c < nch ? c : nch - 1) * a.n_heads + h];
+            const float f = c < nch ? __expf(mc.x - m) : 0.0f;
+            l += wave_sum(f * (c < nch ? mc.y : 0.0f));
+            for (int i = j; i < 64 && c0 + i < nch; i += 4) {
+                const float fi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), i));
+                o = __builtin_fmaf(fi, po[(int64_t)(c0 + i) * ostride], o);
+            }
         }
     }
-    for (int c = j + J * kMaxPer; c < nch; c += J) {
-        const float* ml = a.part_ml + ((int64_t)c * a.n_heads + h) * 2;
-        const float f = __expf(ml[0] - mx);
-        l = __builtin_fmaf(f, ml[1], l);
-        o = __builtin_fmaf(f, a.part_o[((int64_t)c * a.n_heads + h) * kDim + d], o);
-    }
-    // every dimension's thread group holds the same l partials: sum them over j only
     part[j][d] = o;
-    if (d == 0) red[j] = l;  // red is free again after block_reduce
     __syncthreads();
     if (j == 0) {
-        float t = part[0][d], ls = red[0];
-#pragma unroll
-        for (int q = 1; q < J; ++q) {
-            t += part[q][d];
-            ls += red[q];
-        }
-        a.out[(int64_t)h * kDim + d] = __builtin_bit_cast(uint16_t, (_Float16)(t / ls));
+        const float t = ((part[0][d] + part[1][d]) + part[2][d]) + part[3][d];
+        a.out[(int64_t)h * kDim + d] = __builtin_bit_cast(uint16_t, (_Float16)(t / l));
     }
 }
 
