@@ -484,7 +484,8 @@ w4_status w4_gemv_gateup_silu_rmsnorm(const void* packed_w, const void* packed_s
  *   qkv   device fp32 [(n_heads + 2 n_kv_heads) * 128];  bias likewise or NULL;
  *   q_out device fp16 [n_heads][128];
  *   k_cache, v_cache  device fp16 [num_pages][n_kv_heads][page_size][128]
- *   (the layout w4_attn_decode reads);  page_table  device int32.
+ *   (the layout w4_attn_decode reads), 16-byte aligned (W4_EALIGN
+ *   otherwise);  page_table  device int32.
  * Rules as for w4_attn_decode (head_dim 128, n_heads 1..8 x n_kv_heads,
  * power-of-two page_size <= 4096, 1 <= max_ctx <= 2^20); theta > 0.
  */
@@ -508,8 +509,8 @@ typedef struct w4_layer_desc {
     const void* gateup_s;
     const void* down_w;         /* hidden rows, inter inputs                       */
     const void* down_s;
-    uint16_t* k_cache;          /* fp16 [num_pages][n_kv][page_size][128]          */
-    uint16_t* v_cache;
+    uint16_t* k_cache;          /* fp16 [num_pages][n_kv][page_size][128],         */
+    uint16_t* v_cache;          /* both 16-byte aligned (read in 16-byte words)    */
 } w4_layer_desc;
 
 typedef struct w4_step_desc {

@@ -50,9 +50,11 @@ w4_status check_rope(const RopeCall& c, int32_t head_dim, const char* who)
     if (!c.qkv || !c.pos || !c.q_out || !c.k_cache || !c.v_cache || !c.page_table)
         return fail(W4_EINVAL, "%s: null pointer", who);
     if (!aligned_to(c.qkv, 4) || (c.bias && !aligned_to(c.bias, 4)) || !aligned_to(c.pos, 4) ||
-        !aligned_to(c.q_out, 2) || !aligned_to(c.k_cache, 2) || !aligned_to(c.v_cache, 2) ||
-        !aligned_to(c.page_table, 4) || (c.ctx_out && !aligned_to(c.ctx_out, 4)))
+        !aligned_to(c.q_out, 2) || !aligned_to(c.page_table, 4) || (c.ctx_out && !aligned_to(c.ctx_out, 4)))
         return fail(W4_EALIGN, "%s: pointers must be aligned to their element size", who);
+    // the caches are the attention's, which reads K rows in 16-byte words
+    if (!aligned_to(c.k_cache, 16) || !aligned_to(c.v_cache, 16))
+        return fail(W4_EALIGN, "%s: k_cache and v_cache must be 16-byte aligned", who);
     return W4_OK;
 }
 
@@ -216,8 +218,8 @@ w4_status validate_step(const w4_step_desc& d)
         const w4_layer_desc& L = d.layer[l];
         if (!L.attn_norm || !L.mlp_norm || !L.k_cache || !L.v_cache)
             return fail(W4_EINVAL, "%s: layer %d: null norm or cache pointer", who, l);
-        if (!aligned_to(L.attn_norm, 16) || !aligned_to(L.mlp_norm, 8) || !aligned_to(L.k_cache, 2) ||
-            !aligned_to(L.v_cache, 2) || (L.qkv_bias && !aligned_to(L.qkv_bias, 4)))
+        if (!aligned_to(L.attn_norm, 16) || !aligned_to(L.mlp_norm, 8) || !aligned_to(L.k_cache, 16) ||
+            !aligned_to(L.v_cache, 16) || (L.qkv_bias && !aligned_to(L.qkv_bias, 4)))
             return fail(W4_EALIGN, "%s: layer %d: pointers must be aligned to their element size", who, l);
         const GemvCall calls[4] = {
             {L.qkv_w, L.qkv_s, ph, ph, nullptr, nullptr, qkv_rows, d.hidden, d.group, kEpiPlain},

@@ -315,6 +315,10 @@ def test_step_glue_validation_before_launch():
     assert rope(kc=None) == w4.EINVAL
     assert rope(qkv=A + 2) == w4.EALIGN
     assert rope(bias=A + 1) == w4.EALIGN
+    # the caches are read by the attention in 16-byte words
+    assert rope(kc=A + 2) == w4.EALIGN
+    assert rope(vc=A + 8) == w4.EALIGN
+    assert "16-byte" in w4.last_error()
 
 
 def test_read_probe_validation_before_launch():
@@ -437,6 +441,11 @@ def test_decode_step_create_validation():
     bad = _layer_arr(2)
     bad[1].gateup_w = (1 << 20) + 8
     assert create(_step_desc(bad)) == w4.EALIGN
+    for field, off in (("k_cache", 2), ("v_cache", 8)):
+        bad = _layer_arr(2)
+        setattr(bad[0], field, (1 << 20) + off)  # element-aligned, not 16-byte aligned
+        assert create(_step_desc(bad)) == w4.EALIGN
+        assert "layer 0" in w4.last_error()
     bad = _layer_arr(2)
     bad[1].attn_norm = (1 << 20) + 8         # read 16 bytes at a time by the qkv norm prologue
     assert create(_step_desc(bad)) == w4.EALIGN
