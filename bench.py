@@ -184,7 +184,7 @@ def time_graph(sweep, stream, steps: int, warmup: int):
     return ev_ms, wall * 1e3 / steps
 
 
-def time_dominant_kernel(projs, stream, replays: int = 4, sustained: int = 40):
+def time_dominant_kernel(projs, stream, replays: int = 4, sustained: int = 200):
     """Average duration of one gate/up + SiLU launch (the kernel that moves the
     most bytes in the sweep): the 28 layers' gate/up launches are captured in
     their own HIP graph (1.96 GB of weights, so nothing is served from the
@@ -193,9 +193,11 @@ def time_dominant_kernel(projs, stream, replays: int = 4, sustained: int = 40):
     includes the time between graph nodes (about 1.4 us from the last wave of
     one kernel to the first wave of the next).
 
-    Then `sustained` more replays back to back, each between its own events,
-    with the GPU's clocks, power and throttle status sampled throughout: that
-    series shows whether a longer run at this bandwidth slows down, and why.
+    Then `sustained` more replays back to back (about 80 ms), each between its
+    own events, with the GPU's clocks, power and throttle status sampled
+    throughout (the metrics refresh more slowly than a few milliseconds, so
+    the series is long enough to span several refreshes): it shows whether a
+    longer run at this bandwidth slows down, and why.
     Returns (ms per launch in the short window, launches, sustained summary)."""
     import torch
     from int4_weight_only_04_amd import w4
