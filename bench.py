@@ -663,6 +663,60 @@ def cpu_baseline():
     }
 
 
+def run_persistent(args) -> int:
+    """The same 28-layer sweep in its persistent form (one cooperative kernel
+    for all 113 projections, graph-captured) against the graph of one kernel
+    per projection, timed alike (HIP events around `steps` sweeps after
+    `warmup`), in alternating rounds; the outputs of the two are bit-identical
+    (tests/test_gpu_persist.py)."""
+    import torch
+    from int4_weight_only_04_amd import w4
+    specs, projs = build_sweep(args.layers)
+    alg_bytes = sweep_bytes(specs)
+    stream = torch.cuda.Stream()
+    forms = {"graph": w4.Sweep(projs, mode=w4.SWEEP_GRAPH),
+             "persistent": w4.Sweep(projs, mode=w4.SWEEP_PERSISTENT)}
+    for sw in forms.values():
+        time_graph(sw, stream, 2, args.warmup)
+    rounds = {k: [] for k in forms}
+    for _ in range(3):
+        for k, sw in forms.items():
+            rounds[k].append(time_graph(sw, stream, args.steps, 0)[0])
+    timed_out = forms["persistent"].status()
+    for sw in forms.values():
+        sw.close()
+    med = {k: sorted(v)[len(v) // 2] for k, v in rounds.items()}
+    ms = med["persistent"]
+    value = alg_bytes / (ms * 1e-3) / 1e9
+    out = {
+        "metric": "persistent-kernel sweep: achieved HBM GB/s and ms per 28-layer+lm_head INT4 linear sweep",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"the decode-step INT4 linear sweep ({args.layers} layers + lm_head) as one persistent "
+                         "cooperative kernel (one workgroup per CU, hand-off through tagged words and arrival "
+                         "counters), graph-captured, against the graph of one kernel per projection"),
+            "graph_ms_per_step": round(med["graph"], 4),
+            "persistent_vs_graph_time": round(ms / med["graph"], 3),
+            "rounds_ms": {k: [round(x, 4) for x in v] for k, v in rounds.items()},
+            "watchdog_timeout": bool(timed_out),
+            "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        },
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def build_prefill(layers: int, device: str = "cuda"):
     """Device buffers of the prefill sweep: packed weights drawn like the decode
     sweep's, one seeded 512-row token block per projection, and lm_head as
@@ -1385,13 +1439,14 @@ def main(argv=None):
     ap.add_argument("--layers", type=int, default=synthetic.LAYERS)
     ap.add_argument("--eager-steps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", choices=("decode", "prefill", "attention", "step", "w4a8", "configs"),
+    ap.add_argument("--workload", choices=("decode", "prefill", "attention", "step", "w4a8", "configs", "persistent"),
                     default="decode",
                     help="decode: the per-token GEMV sweep (default); prefill: the 512-token GEMM sweep; "
                          "attention: 28 layers' paged-KV decode attention at a 4096-token context; "
                          "step: the full decode step (tokens 512.. after a 512-token prompt); "
                          "w4a8: the sweep with int8 activations; configs: only the per-config GEMV "
-                         "timings on cold buffers (the run the traffic counters are taken over)")
+                         "timings on cold buffers (the run the traffic counters are taken over); "
+                         "persistent: the sweep as one cooperative kernel against the graph")
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="write profiles/traffic_configs.json (and the dominant kernel's traffic file) from "
                          "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE CSVs of --workload configs and --copy-probe; "
@@ -1434,6 +1489,8 @@ def main(argv=None):
         return run_step(args)
     if args.workload == "w4a8":
         return run_w4a8(args)
+    if args.workload == "persistent":
+        return run_persistent(args)
     if args.workload == "configs":
         stream = torch.cuda.Stream()
         print(json.dumps({"per_config": time_configs(stream, replays=1, max_calls=32)}), flush=True)
