@@ -16,6 +16,7 @@
 #include <stdint.h>
 
 #include "w4_internal.h"
+#include "w4_wave.h"
 
 namespace w4i {
 namespace {
@@ -38,7 +39,8 @@ __global__ void __launch_bounds__(256) embed_kernel(const uint16_t* __restrict__
 
 // One workgroup: h += y (fp32, when y is given), then
 // x = fp16(h * g / sqrt(mean(h^2) + eps)).  The sum of squares is reduced in a
-// fixed order (per-thread strided sums, then a tree), so it is deterministic.
+// fixed order (per-thread strided sums, then a tree: DPP row sums and the four
+// row totals, then the waves in order), so it is deterministic.
 __global__ void __launch_bounds__(kNormThreads) add_rmsnorm_kernel(float* __restrict__ h, const float* __restrict__ y,
                                                                    const uint16_t* __restrict__ gamma, int64_t n,
                                                                    float eps, uint16_t* __restrict__ x)
@@ -54,8 +56,7 @@ __global__ void __launch_bounds__(kNormThreads) add_rmsnorm_kernel(float* __rest
         }
         ss = __builtin_fmaf(v, v, ss);
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+    ss = wave::wave_sum_tree(ss);
     if ((tid & 63) == 0) red[tid >> 6] = ss;
     __syncthreads();
     float tot = red[0];
@@ -85,8 +86,7 @@ __global__ void __launch_bounds__(kNormThreads) embed_rmsnorm_kernel(const uint1
         h[i] = v;
         ss = __builtin_fmaf(v, v, ss);
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+    ss = wave::wave_sum_tree(ss);
     if ((tid & 63) == 0) red[tid >> 6] = ss;
     __syncthreads();
     float tot = red[0];
@@ -106,8 +106,9 @@ constexpr int kNormVec = 4;
 
 __device__ __forceinline__ float block_sum(float v, float* red)
 {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    // each wave's total through DPP row sums and lane reads (depth 6, as a
+    // 6-level butterfly), without the LDS round trips of lane shuffles
+    v = wave::wave_sum_tree(v);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
     __syncthreads();
     float tot = red[0];
