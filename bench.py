@@ -757,17 +757,88 @@ def prefill_flops(items, lm_buf) -> int:
     return sum(2 * m * p.n * p.k for (p, *_rest) in items) + 2 * lm_buf[0].n * lm_buf[0].k
 
 
-def launch_prefill(items, lm_buf, workspace, stream, only_gateup: bool = False):
+PREFILL_PRODUCTS = ("qkv", "o", "gateup", "down")
+
+
+def product_of(p) -> str:
+    """The product a projection is, from its name (``L<layer>.<product>``)."""
+    return p.name.split(".", 1)[1]
+
+
+def launch_prefill(items, lm_buf, workspace, stream, only: str | None = None):
+    """The prefill sweep, or with `only` just that product's launches (no lm_head)."""
     from int4_weight_only_04_amd import w4
     m = synthetic.PROMPT
     for p, pw, ps, x, out in items:
+        if only is not None and product_of(p) != only:
+            continue
         if p.kind == "gateup":
             w4.gemm_gateup_silu(pw, ps, x, out, m, p.n, p.k, p.group, stream=stream)
-        elif not only_gateup:
+        else:
             w4.gemm(pw, ps, x, out, m, p.n, p.k, p.group, workspace=workspace, stream=stream)
-    if not only_gateup:
+    if only is None:
         lm, pw, ps, x, y, am, ws = lm_buf
         w4.gemv(pw, ps, x, y, lm.n, lm.k, lm.group, argmax=am, workspace=ws, stream=stream)
+
+
+def time_prefill_products(items, lm_buf, workspace, stream, reps: int = 3):
+    """Each product on its own: its launches over every layer (each layer's
+    weights are distinct, 0.2-1 GB per product, beyond the 256 MB Infinity
+    Cache) captured in one graph, replayed once to warm up and `reps` times
+    between events; microseconds per launch, the split-k reduction included."""
+    m = synthetic.PROMPT
+    rows = []
+    for prod in PREFILL_PRODUCTS:
+        sel = [it[0] for it in items if product_of(it[0]) == prod]
+        if not sel:
+            continue
+        g = capture(lambda s, prod=prod: launch_prefill(items, lm_buf, workspace, s, only=prod), stream)
+        us = replay_ms(g, stream, reps, 1) / len(sel) * 1e3
+        del g
+        p = sel[0]
+        flops = 2 * m * p.n * p.k
+        rows.append({"product": prod, "shape_m_n_k": [m, p.n, p.k], "launches": len(sel) * reps,
+                     "w4_us_per_launch": round(us, 2),
+                     "w4_tflops": round(flops / (us * 1e-6) / 1e12, 1),
+                     "w4_pct_of_mfma_f16_peak": round(100.0 * flops / (us * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS, 2)})
+    return rows
+
+
+def dense_f16_library_times(reps: int = 20) -> dict:
+    """Context, not the INT4 path: the same products as dense fp16 weight
+    matrices [n][k] through the vendor GEMM library (torch's F.linear, which
+    calls hipBLASLt), x of 512 token rows.  Each shape cycles through enough
+    weight copies to span >= 512 MiB, so every call reads its weights from
+    HBM; one warm-up call per copy, then `reps` timed calls between events.
+    The dense form reads 4x the INT4 weight bytes and dequantizes nothing;
+    gate/up is timed without the SiLU (37888 output columns)."""
+    import torch
+    m = synthetic.PROMPT
+    shapes = {"qkv": (synthetic.QKV, synthetic.HIDDEN), "o": (synthetic.HIDDEN, synthetic.HIDDEN),
+              "gateup": (2 * synthetic.MLP, synthetic.HIDDEN), "down": (synthetic.HIDDEN, synthetic.MLP)}
+    gen = torch.Generator(device="cuda").manual_seed(5150)
+    out = {}
+    for prod, (n, k) in shapes.items():
+        copies = max(2, -(-(512 << 20) // (2 * n * k)))
+        x = torch.randn((m, k), generator=gen, device="cuda", dtype=torch.float16)
+        ws = [torch.randn((n, k), generator=gen, device="cuda", dtype=torch.float16) for _ in range(copies)]
+        for w in ws:
+            torch.nn.functional.linear(x, w)
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(reps):
+            torch.nn.functional.linear(x, ws[i % copies])
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) / reps * 1e3
+        tflops = 2 * m * n * k / (us * 1e-6) / 1e12
+        out[prod] = {"dense_f16_library_us": round(us, 2), "dense_f16_library_tflops": round(tflops, 1),
+                     "dense_f16_library_pct_of_mfma_f16_peak": round(100.0 * tflops / MFMA_F16_PEAK_TFLOPS, 2)}
+        del ws, x
+        torch.cuda.empty_cache()
+    return out
 
 
 def capture(fn, stream):
@@ -836,11 +907,19 @@ def run_prefill(args) -> int:
     print("[bench] prefill graph", file=sys.stderr, flush=True)
     g = capture(lambda s: launch_prefill(items, lm_buf, workspace, s), stream)
     ms = replay_ms(g, stream, args.steps, args.warmup)
-    print("[bench] dominant kernel (gate/up GEMM)", file=sys.stderr, flush=True)
-    gg = capture(lambda s: launch_prefill(items, lm_buf, workspace, s, only_gateup=True), stream)
-    n_gu = sum(1 for it in items if it[0].kind == "gateup")
+    print("[bench] each product alone, and the dense fp16 library GEMM at the same shapes",
+          file=sys.stderr, flush=True)
     reps = 3
-    gu_ms = replay_ms(gg, stream, reps, 1) / n_gu
+    per_product = time_prefill_products(items, lm_buf, workspace, stream, reps)
+    del g
+    dense = dense_f16_library_times()
+    for row in per_product:
+        d = dense.get(row["product"])
+        if d:
+            row.update(d)
+            row["w4_time_vs_dense_f16_library"] = round(row["w4_us_per_launch"] / d["dense_f16_library_us"], 3)
+    gu_row = next(r for r in per_product if r["product"] == "gateup")
+    gu_ms = gu_row["w4_us_per_launch"] / 1e3
     gp = next(it[0] for it in items if it[0].kind == "gateup")
     gu_flops = 2 * synthetic.PROMPT * gp.n * gp.k
     gu_tflops = gu_flops / (gu_ms * 1e-3) / 1e12
@@ -868,6 +947,7 @@ def run_prefill(args) -> int:
             "gemms_per_step": len(items),
             "flops_per_step": flops,
             "pct_of_mfma_f16_peak": round(100.0 * value / MFMA_F16_PEAK_TFLOPS, 2),
+            "per_product": per_product,
         },
         "roofline": {
             "kernel": "gemm_w4_kernel<gate/up+silu> 512x37888x3584 g128",
@@ -881,7 +961,7 @@ def run_prefill(args) -> int:
             "algorithmic_bytes_per_launch": (gp.n * gp.k // 2 + 2 * gp.n * (gp.k // gp.group)
                                              + 2 * synthetic.PROMPT * gp.k + synthetic.PROMPT * gp.n),
             "avg_launch_us": round(gu_ms * 1e3, 3),
-            "launches_timed": reps * n_gu,
+            "launches_timed": gu_row["launches"],
         },
         "cpu_baseline": None,
     }
