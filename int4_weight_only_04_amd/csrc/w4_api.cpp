@@ -749,7 +749,7 @@ w4_status w4_decode_linear_sweep_create(const w4_proj_desc* projs, int32_t count
         if (persistent) {
             w4_status st = persist_setup(sw, projs);
             if (st != W4_OK) {
-                if (sw->dev) hipFree(sw->dev);
+                if (sw->dev) (void)hipFree(sw->dev);
                 delete sw;
                 return st;
             }
@@ -758,24 +758,24 @@ w4_status w4_decode_linear_sweep_create(const w4_proj_desc* projs, int32_t count
             hipStream_t cap = nullptr;
             hipError_t err = hipStreamCreateWithFlags(&cap, hipStreamNonBlocking);
             if (err != hipSuccess) {
-                if (sw->dev) hipFree(sw->dev);
+                if (sw->dev) (void)hipFree(sw->dev);
                 delete sw;
                 return hip_fail(err, "hipStreamCreateWithFlags");
             }
             err = hipStreamBeginCapture(cap, hipStreamCaptureModeThreadLocal);
             if (err != hipSuccess) {
-                hipStreamDestroy(cap);
-                if (sw->dev) hipFree(sw->dev);
+                (void)hipStreamDestroy(cap);
+                if (sw->dev) (void)hipFree(sw->dev);
                 delete sw;
                 return fail(W4_ECAPTURE, "hipStreamBeginCapture failed: %s", hipGetErrorString(err));
             }
             w4_status st = persistent ? launch_persistent(*sw, cap) : launch_all(sw->calls, cap);
             hipGraph_t graph = nullptr;
             hipError_t end_err = hipStreamEndCapture(cap, &graph);
-            hipStreamDestroy(cap);
+            (void)hipStreamDestroy(cap);
             if (st != W4_OK || end_err != hipSuccess) {
-                if (graph) hipGraphDestroy(graph);
-                if (sw->dev) hipFree(sw->dev);
+                if (graph) (void)hipGraphDestroy(graph);
+                if (sw->dev) (void)hipFree(sw->dev);
                 delete sw;
                 if (st != W4_OK) return st;
                 return fail(W4_ECAPTURE, "hipStreamEndCapture failed: %s", hipGetErrorString(end_err));
@@ -783,8 +783,8 @@ w4_status w4_decode_linear_sweep_create(const w4_proj_desc* projs, int32_t count
             hipGraphExec_t exec = nullptr;
             err = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
             if (err != hipSuccess) {
-                hipGraphDestroy(graph);
-                if (sw->dev) hipFree(sw->dev);
+                (void)hipGraphDestroy(graph);
+                if (sw->dev) (void)hipFree(sw->dev);
                 delete sw;
                 return fail(W4_ECAPTURE, "hipGraphInstantiate failed: %s", hipGetErrorString(err));
             }
@@ -821,9 +821,9 @@ w4_status w4_decode_linear_sweep_destroy(w4_sweep* sweep)
 {
     try {
         if (!sweep) return ok();
-        if (sweep->exec) hipGraphExecDestroy(sweep->exec);
-        if (sweep->graph) hipGraphDestroy(sweep->graph);
-        if (sweep->dev) hipFree(sweep->dev);
+        if (sweep->exec) (void)hipGraphExecDestroy(sweep->exec);
+        if (sweep->graph) (void)hipGraphDestroy(sweep->graph);
+        if (sweep->dev) (void)hipFree(sweep->dev);
         delete sweep;
         return ok();
     } catch (...) {
