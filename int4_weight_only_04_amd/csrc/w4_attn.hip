@@ -15,7 +15,7 @@
 // (deterministic).  The context length is read from device memory, so a
 // captured graph replays unchanged from token to token; the grid is sized for
 // max_ctx, and a chunk past the context exits before reading the cache (the
-// combine reads only the chunks below the context).  A chunk's
+// combine uses only the chunks below the context).  A chunk's
 // softmax covers every token in it, the page's tail included: all waves reach
 // every barrier, and tokens past the context are masked, never skipped with
 // an early exit (the barrier-in-a-branch mistake the pages describe corrupted
@@ -68,12 +68,17 @@ __device__ __forceinline__ int clamp_ctx(const AttnArgs& a)
     return c;
 }
 
-// cache row index (in token rows) of token t of KV head g
-__device__ __forceinline__ int64_t cache_row(const AttnArgs& a, int t, int g)
+// cache row index (in token rows) of token t of KV head g, from the raw
+// page-table entry pg of t's page
+__device__ __forceinline__ int64_t cache_row_of(const AttnArgs& a, int pg, int t, int g)
 {
-    int pg = a.table[t >> a.page_shift];
     pg = pg < 0 ? 0 : (pg >= a.num_pages ? a.num_pages - 1 : pg);  // never read outside the cache
     return ((int64_t)pg * a.n_kv + g) * (1 << a.page_shift) + (t & ((1 << a.page_shift) - 1));
+}
+
+__device__ __forceinline__ int64_t cache_row(const AttnArgs& a, int t, int g)
+{
+    return cache_row_of(a, a.table[t >> a.page_shift], t, g);
 }
 
 __device__ __forceinline__ void half8_to_float(uint4 v, float (&f)[8])
@@ -247,34 +252,50 @@ __global__ void __launch_bounds__(kAttnThreads) attn_partial_kernel(AttnArgs a)
     float* po = a.part_o + ((int64_t)chunk * a.n_heads + (int64_t)g * GQ) * kDim;
     float* pml = a.part_ml + ((int64_t)chunk * a.n_heads + (int64_t)g * GQ) * 2;
 
-    // ---- first round: the context length (or position) and the page-table
-    // entries of this lane's K row and of the wave's 16 V rows; a chunk past
-    // the context ends here, before any K/V traffic (the combine never reads
-    // its partial).  Second round: q and the K and V rows, all issued before
-    // any math (rows of tokens past max_ctx are read from the last one; past
-    // the context they are masked below).
+    // ---- first round, issued together: the context length (or position),
+    // the page-table entries of this lane's K row and of the wave's 16 V rows
+    // (tokens past max_ctx use the last one; the table holds an entry for
+    // every token below max_ctx, so these reads are in bounds whatever the
+    // context) and q.  Only then is the context length waited for: a chunk
+    // past the context ends here, before any K/V traffic (the combine never
+    // uses its partial).  Second round: the K and V rows, all issued before
+    // any math (past the context they are masked below).
+    // read as a vector load through an index the compiler cannot fold, so
+    // that it goes out first and the exit test waits for it alone (vector
+    // loads are counted in issue order), not for the loads issued after it
+    int zero;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
+    const int raw_len = (ROPE ? a.pos : a.ctx_ptr)[zero];
     const int tk = t0 + wave * 16 + col;
-    const int64_t krow = cache_row(a, tk < a.max_ctx ? tk : a.max_ctx - 1, g);
-    int64_t vrow[16];
+    const int tkc = tk < a.max_ctx ? tk : a.max_ctx - 1;
+    const int kpg = a.table[tkc >> a.page_shift];
+    int vpg[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
         const int t = t0 + wave * 16 + j;
-        vrow[j] = cache_row(a, t < a.max_ctx ? t : a.max_ctx - 1, g);
+        vpg[j] = a.table[(t < a.max_ctx ? t : a.max_ctx - 1) >> a.page_shift];
     }
-    int ctx, pos = -1;
-    if constexpr (ROPE) {
-        pos = *a.pos;
-        pos = pos < 0 ? 0 : (pos >= a.max_ctx ? a.max_ctx - 1 : pos);
-        ctx = pos + 1;
-    } else {
-        ctx = clamp_ctx(a);
-    }
-    if (t0 >= ctx) return;  // whole workgroup, before any barrier
     uint4 qv[4];
     if constexpr (!ROPE) {
         const int hq = col < GQ ? col : 0;
 #pragma unroll
         for (int m = 0; m < 4; ++m) qv[m] = a.q[(int64_t)(g * GQ + hq) * (kDim / 8) + rg * 4 + m];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    int ctx, pos = -1;
+    if constexpr (ROPE) {
+        pos = raw_len < 0 ? 0 : (raw_len >= a.max_ctx ? a.max_ctx - 1 : raw_len);
+        ctx = pos + 1;
+    } else {
+        ctx = raw_len < 1 ? 1 : (raw_len > a.max_ctx ? a.max_ctx : raw_len);
+    }
+    if (t0 >= __builtin_amdgcn_readfirstlane(ctx)) return;  // whole workgroup, before any barrier
+    const int64_t krow = cache_row_of(a, kpg, tkc, g);
+    int64_t vrow[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int t = t0 + wave * 16 + j;
+        vrow[j] = cache_row_of(a, vpg[j], t < a.max_ctx ? t : a.max_ctx - 1, g);
     }
     uint4 kv[4];
 #pragma unroll
@@ -474,24 +495,28 @@ __global__ void __launch_bounds__(kCombThreads) attn_combine_kernel(AttnArgs a)
     const int lane = tid & 63;
     const int d = tid & (kDim - 1);
     const int j = __builtin_amdgcn_readfirstlane(tid >> 7);  // uniform: a wave lies in one chunk lane
-    const int ctx = clamp_ctx(a);
-    const int nch = (ctx + kChunk - 1) / kChunk;   // 1 .. chunks
+    const int cap = (a.max_ctx + kChunk - 1) / kChunk;  // chunks the workspace holds
     const float2* ml = reinterpret_cast<const float2*>(a.part_ml);
     const float* po = a.part_o + (int64_t)h * kDim + d;
     const int64_t ostride = (int64_t)a.n_heads * kDim;
     float o = 0.0f, l;
-    if (nch <= 64) {
-        // every load in one round: the lane's chunk (max, sum) and this
-        // thread's 16 partials (chunks past the context read the last one and
-        // are skipped below)
-        const int c = lane < nch ? lane : nch - 1;
+    if (cap <= 64) {
+        // every load in one round, with addresses that do not depend on the
+        // context length, so they travel together with its load: the lane's
+        // chunk (max, sum) and this thread's 16 partials.  Chunks past the
+        // context hold whatever an earlier call left there; they are only
+        // ever selected away below, never multiplied.
+        const int c = lane < cap ? lane : cap - 1;
         const float2 mc = ml[(int64_t)c * a.n_heads + h];
         float ov[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int cc = j + 4 * i;
-            ov[i] = po[(int64_t)(cc < nch ? cc : nch - 1) * ostride];
+            ov[i] = po[(int64_t)(cc < cap ? cc : cap - 1) * ostride];
         }
+        // only now wait for the context length
+        __builtin_amdgcn_sched_barrier(0);
+        const int nch = (clamp_ctx(a) + kChunk - 1) / kChunk;   // 1 .. cap
         const float m = wave_max(lane < nch ? mc.x : -__builtin_inff());
         const float f = lane < nch ? __expf(mc.x - m) : 0.0f;
         l = wave_sum(f * (lane < nch ? mc.y : 0.0f));
@@ -505,6 +530,7 @@ __global__ void __launch_bounds__(kCombThreads) attn_combine_kernel(AttnArgs a)
         }
     } else {
         // longer contexts: the maximum over all chunks first, then blocks of 64
+        const int nch = (clamp_ctx(a) + kChunk - 1) / kChunk;
         float mx = -__builtin_inff();
         for (int c0 = 0; c0 < nch; c0 += 64) {
             const int c = c0 + lane;
