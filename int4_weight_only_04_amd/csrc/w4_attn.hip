@@ -259,10 +259,10 @@ __global__ void __launch_bounds__(kAttnThreads) attn_partial_kernel(AttnArgs a)
     // context) and q.  Only then is the context length waited for: a chunk
     // past the context ends here, before any K/V traffic (the combine never
     // uses its partial).  Second round: the K and V rows, all issued before
-    // any math (past the context they are masked below).
-    // read as a vector load through an index the compiler cannot fold, so
+    // any math (past the context they are masked below).  The length is
+    // read as a vector load, through an index the compiler cannot fold, so
     // that it goes out first and the exit test waits for it alone (vector
-    // loads are counted in issue order), not for the loads issued after it
+    // loads are counted in issue order), not for the loads issued after it.
     int zero;
     asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
     const int raw_len = (ROPE ? a.pos : a.ctx_ptr)[zero];
@@ -282,14 +282,15 @@ __global__ void __launch_bounds__(kAttnThreads) attn_partial_kernel(AttnArgs a)
         for (int m = 0; m < 4; ++m) qv[m] = a.q[(int64_t)(g * GQ + hq) * (kDim / 8) + rg * 4 + m];
     }
     __builtin_amdgcn_sched_barrier(0);
+    const int len = __builtin_amdgcn_readfirstlane(raw_len);  // the same in every lane
     int ctx, pos = -1;
     if constexpr (ROPE) {
-        pos = raw_len < 0 ? 0 : (raw_len >= a.max_ctx ? a.max_ctx - 1 : raw_len);
+        pos = len < 0 ? 0 : (len >= a.max_ctx ? a.max_ctx - 1 : len);
         ctx = pos + 1;
     } else {
-        ctx = raw_len < 1 ? 1 : (raw_len > a.max_ctx ? a.max_ctx : raw_len);
+        ctx = len < 1 ? 1 : (len > a.max_ctx ? a.max_ctx : len);
     }
-    if (t0 >= __builtin_amdgcn_readfirstlane(ctx)) return;  // whole workgroup, before any barrier
+    if (t0 >= ctx) return;  // whole workgroup, before any barrier
     const int64_t krow = cache_row_of(a, kpg, tkc, g);
     int64_t vrow[16];
 #pragma unroll
