@@ -149,19 +149,49 @@ __device__ __forceinline__ uint4 normed_block(const float4& h0, const float4& h1
                       half_pair(h1.z * r * half_lo(g.w), h1.w * r * half_hi(g.w)));
 }
 
+// Lane N of each 16-lane row, broadcast to every lane of that row (DPP
+// row_newbcast:N).
+template <int N>
+__device__ __forceinline__ uint32_t row_bcast(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x150 + N, 0xF, 0xF, false);
+}
+
+// the same for n = 0..7, a constant once the caller's loop is unrolled
+__device__ __forceinline__ uint32_t row_bcast(uint32_t v, int n)
+{
+    switch (n) {
+        case 0: return row_bcast<0>(v);
+        case 1: return row_bcast<1>(v);
+        case 2: return row_bcast<2>(v);
+        case 3: return row_bcast<3>(v);
+        case 4: return row_bcast<4>(v);
+        case 5: return row_bcast<5>(v);
+        case 6: return row_bcast<6>(v);
+        default: return row_bcast<7>(v);
+    }
+}
+
 // Straight-line body for exactly C k iterations of one wave: all loads first
 // (weights and scales non-temporal, x through L1), then the math for each
 // iteration in order.  With no branches between the loads the compiler's
-// wait counters are exact, so iteration d waits only for its own three
-// loads and its math overlaps the loads still in flight (with branches it
-// falls back to waiting for every load before any math).
-template <int C, int U, int XM>
+// wait counters are exact, so iteration d waits only for its own loads and
+// its math overlaps the loads still in flight (with branches it falls back to
+// waiting for every load before any math).
+// RS (groups of 128 inputs or more, C <= 8): a 16-lane row's 16 blocks of an
+// iteration then share one scale word per tile, so one load per tile brings
+// every iteration's words: lane 16 q + d loads row q's word of iteration d
+// (lanes past C repeat iteration C - 1's), and the math broadcasts it to the
+// row.  That is one scale load per tile instead of one per iteration.
+template <int C, int U, int XM, bool RS>
 __device__ __forceinline__ void accumulate_exact(float (&acc)[U][4], const uint4* const (&wp)[U],
                                                  const uint2* const (&sp)[U], const bool (&tile_ok)[U],
                                                  const KernelArgs& a, int i0, int lane, uint32_t magic, bool write_x)
 {
+    static_assert(!RS || C <= 8, "row_bcast covers 8 iterations");
     uint4 w[C][U];
-    uint2 s[C][U];
+    uint2 s[C][U];      // per iteration (without RS)
+    uint2 srow[U];      // every iteration's, one word per lane (RS)
     uint4 xr[C];
     uint2 cr[C];
     float sx[C];
@@ -173,17 +203,22 @@ __device__ __forceinline__ void accumulate_exact(float (&acc)[U][4], const uint4
     // (keeping them live across it and reordering the waits).  An assembler
     // comment that differs per C makes the bodies differ from the first
     // instruction on.
-    asm volatile("; accumulate_exact %0 iterations" ::"n"(C));
+    asm volatile("; accumulate_exact %0 iterations, row scales %1" ::"n"(C), "n"(RS ? 1 : 0));
     // the norm's partial sums go first, so waiting for them does not wait
     // for the weight stream issued after them
     if constexpr (XM == kXNorm) load_parts(pv, a.nss, a.nparts, lane);
+    if constexpr (RS) {
+        const int dl = (lane & 15) < C ? (lane & 15) : C - 1;
+#pragma unroll
+        for (int u = 0; u < U; ++u) srow[u] = ld_stream(sp[u] + (((i0 + dl) * 64 + (lane & 48)) >> a.gshift));
+    }
 #pragma unroll
     for (int d = 0; d < C; ++d) {
         const int j = (i0 + d) * 64 + lane;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             w[d][u] = ld_stream(wp[u] + j);
-            s[d][u] = ld_stream(sp[u] + (j >> a.gshift));
+            if constexpr (!RS) s[d][u] = ld_stream(sp[u] + (j >> a.gshift));
         }
         if constexpr (XM == kXCodes) {
             cr[d] = reinterpret_cast<const uint2*>(a.x)[j];
@@ -215,7 +250,8 @@ __device__ __forceinline__ void accumulate_exact(float (&acc)[U][4], const uint4
             // scales masked to zero (a mask, not a select, so the scale load
             // stays unconditional and in issue order)
             const uint32_t keep = 0u - (uint32_t)tile_ok[u];
-            const uint2 sc = make_uint2(s[d][u].x & keep, s[d][u].y & keep);
+            const uint2 sr = RS ? make_uint2(row_bcast(srow[u].x, d), row_bcast(srow[u].y, d)) : s[d][u];
+            const uint2 sc = make_uint2(sr.x & keep, sr.y & keep);
             if constexpr (XM == kXCodes) {
                 acc[u][0] = __builtin_fmaf((float)idot8(w[d][u].x, cr[d], n8), half_lo(sc.x) * sx[d], acc[u][0]);
                 acc[u][1] = __builtin_fmaf((float)idot8(w[d][u].y, cr[d], n8), half_hi(sc.x) * sx[d], acc[u][1]);
@@ -308,10 +344,17 @@ __global__ void __launch_bounds__(waves_for(SPLIT) * 64) gemv_w4_kernel(KernelAr
             wp[u] = a.pw + t * a.kb;
             sp[u] = a.ps + t * a.ng;
         }
-        if (count == D)
-            accumulate_exact<D, U, XM>(acc, wp, sp, tile_ok, a, it0, lane, magic, write_x);
-        else if constexpr (D > 1)
-            accumulate_exact<D - 1, U, XM>(acc, wp, sp, tile_ok, a, it0, lane, magic, write_x);
+        if (a.gshift >= 4) {  // G >= 128: a 16-lane row lies in one group
+            if (count == D)
+                accumulate_exact<D, U, XM, true>(acc, wp, sp, tile_ok, a, it0, lane, magic, write_x);
+            else if constexpr (D > 1)
+                accumulate_exact<D - 1, U, XM, true>(acc, wp, sp, tile_ok, a, it0, lane, magic, write_x);
+        } else {
+            if (count == D)
+                accumulate_exact<D, U, XM, false>(acc, wp, sp, tile_ok, a, it0, lane, magic, write_x);
+            else if constexpr (D > 1)
+                accumulate_exact<D - 1, U, XM, false>(acc, wp, sp, tile_ok, a, it0, lane, magic, write_x);
+        }
     } else if (live) {
         const uint4* wp[U];
         const uint2* sp[U];
