@@ -866,34 +866,60 @@ def replay_ms(g, stream, steps: int, warmup: int) -> float:
     return a.elapsed_time(b) / steps
 
 
+def _pool_map(fn, items, threads: int):
+    """fn over items on a thread pool of `threads` (the oracle's C calls release
+    the interpreter lock), results in order."""
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        return list(ex.map(fn, items))
+
+
+def _row_ranges(n: int, parts: int):
+    cuts = np.linspace(0, n, parts + 1).astype(np.int64)
+    return [np.arange(cuts[i], cuts[i + 1], dtype=np.int64) for i in range(parts)]
+
+
 def prefill_cpu_baseline(tokens: int = 4):
-    """The oracle's prefill product (single thread, fp64) on a bounded sample:
+    """The oracle's prefill product (fp64 C, unchanged) on a bounded sample:
     layer 0's four projections, all weight rows, for the first `tokens` rows
-    of their token blocks."""
+    of their token blocks; once single-threaded and once with the weight rows
+    split over all available cores."""
     import oracle
     from int4_weight_only_04_amd import w4
+    host = host_info()
+    nt = host["threads"]
     flops = 0
-    t_total = 0.0
+    t = {1: 0.0, nt: 0.0}
     for p in synthetic.prefill_projections(1):
-        layout = "gateup" if p.kind == "gateup" else "plain"
+        gateup = p.kind == "gateup"
+        layout = "gateup" if gateup else "plain"
         wb, sb = w4.packed_size(p.n, p.k, p.group, layout)
         pw, ps, _ = synthetic.packed_random(p.seed, wb, sb // 2, p.k)
         xm = synthetic.prompt_acts(p.seed + 5, tokens, p.k)
-        t0 = time.perf_counter()
-        y, _ = oracle.gemm_packed(pw, ps, xm, p.n, p.k, p.group, gateup=(layout == "gateup"))
-        if p.kind == "gateup":
-            for row in y:
-                oracle.silu_gate(row)
-        t_total += time.perf_counter() - t0
+        for th in (1, nt):
+            t0 = time.perf_counter()
+            if th == 1:
+                y, _ = oracle.gemm_packed(pw, ps, xm, p.n, p.k, p.group, gateup=gateup)
+            else:
+                ys = _pool_map(lambda r: oracle.gemm_packed(pw, ps, xm, p.n, p.k, p.group, gateup=gateup,
+                                                            ncols=r)[0], _row_ranges(p.n, th), th)
+                y = np.concatenate(ys, axis=1)
+            if gateup:
+                for row in y:
+                    oracle.silu_gate(row)
+            t[th] += time.perf_counter() - t0
         flops += 2 * tokens * p.n * p.k
     return {
-        "value": flops / t_total / 1e12,
+        "value": flops / t[nt] / 1e12,
         "unit": "TFLOP/s",
-        "cores": 1,
+        "cores": nt,
         "kind": "oracle",
         "sample": f"layer 0 of the prefill sweep (qkv, o_proj, gate/up+silu, down), all rows, first "
-                  f"{tokens} prompt tokens: {flops} flops in {t_total:.1f} s, single-threaded fp64 C",
-        "seconds": t_total,
+                  f"{tokens} prompt tokens: {flops} flops in {t[nt]:.2f} s on {nt} threads (weight rows split "
+                  f"across a thread pool; fp64 C oracle)",
+        "seconds": t[nt],
+        "single_thread": {"value": flops / t[1] / 1e12, "unit": "TFLOP/s", "cores": 1, "seconds": round(t[1], 3)},
+        "host": host,
     }
 
 
@@ -978,29 +1004,48 @@ def attn_bytes(ctx: int) -> int:
 
 
 def attn_cpu_baseline(layers: int = 12):
-    """The oracle's attention (single thread, fp64) on `layers` layers' caches
-    at the full context."""
+    """The oracle's attention (fp64 C, unchanged) on `layers` layers' caches at
+    the full context: once single-threaded, one layer after another, and once
+    with the layers spread over all available cores (a thread pool of
+    min(cores, layers) threads; the oracle computes one call's heads in
+    order)."""
     import oracle
+    host = host_info()
+    nt = host["threads"]
     rng = np.random.default_rng(4000)
     npages = ATTN_CTX // ATTN_PAGE
-    total = 0.0
+    calls = []
     for _ in range(layers):
         q = rng.standard_normal((ATTN_HEADS, 128)).astype(np.float16).view(np.uint16)
         kc = rng.standard_normal((npages, ATTN_KV_HEADS, ATTN_PAGE, 128)).astype(np.float16).view(np.uint16)
         vc = rng.standard_normal((npages, ATTN_KV_HEADS, ATTN_PAGE, 128)).astype(np.float16).view(np.uint16)
         table = rng.permutation(npages).astype(np.int32)
-        t0 = time.perf_counter()
-        oracle.attn_decode(q, kc, vc, table, ATTN_CTX, ATTN_KV_HEADS, ATTN_PAGE, 1.0 / np.sqrt(128.0))
-        total += time.perf_counter() - t0
+        calls.append((q, kc, vc, table))
+
+    def one(c):
+        q, kc, vc, table = c
+        return oracle.attn_decode(q, kc, vc, table, ATTN_CTX, ATTN_KV_HEADS, ATTN_PAGE, 1.0 / np.sqrt(128.0))
+
+    t0 = time.perf_counter()
+    for c in calls:
+        one(c)
+    t1 = time.perf_counter() - t0
+    th = min(nt, layers)
+    t0 = time.perf_counter()
+    _pool_map(one, calls, th)
+    tn = time.perf_counter() - t0
     nbytes = layers * attn_bytes(ATTN_CTX)
     return {
-        "value": nbytes / total / 1e9,
+        "value": nbytes / tn / 1e9,
         "unit": "GB/s",
-        "cores": 1,
+        "cores": th,
         "kind": "oracle",
         "sample": f"{layers} layers' attention at context {ATTN_CTX} (28 query heads, 4 KV heads, pages of "
-                  f"{ATTN_PAGE}): {nbytes} algorithmic bytes in {total:.1f} s, single-threaded fp64 C",
-        "seconds": total,
+                  f"{ATTN_PAGE}): {nbytes} algorithmic bytes in {tn:.2f} s on {th} threads (one layer per "
+                  f"task; fp64 C oracle)",
+        "seconds": tn,
+        "single_thread": {"value": nbytes / t1 / 1e9, "unit": "GB/s", "cores": 1, "seconds": round(t1, 3)},
+        "host": host,
     }
 
 
@@ -1371,30 +1416,45 @@ def quant_bytes(k: int, group: int) -> int:
 
 
 def w4a8_cpu_baseline():
-    """The oracle's W4A8 product (single thread, fp64) on layer 0's four
-    projections, all rows, plus the oracle's quantization of their inputs."""
+    """The oracle's W4A8 product (fp64 C, unchanged) on layer 0's four
+    projections, all rows, plus the oracle's quantization of their inputs:
+    once single-threaded and once with the rows split over all available
+    cores (the quantization runs once, on one thread, in both)."""
     import oracle
     from int4_weight_only_04_amd import w4
-    total, t_total = 0, 0.0
+    host = host_info()
+    nt = host["threads"]
+    total = 0
+    t = {1: 0.0, nt: 0.0}
     for p in synthetic.sweep_projections(1):
-        layout = "gateup" if p.kind == "gateup" else "plain"
+        gateup = p.kind == "gateup"
+        layout = "gateup" if gateup else "plain"
         wb, sb = w4.packed_size(p.n, p.k, p.group, layout)
         pw, ps, x = synthetic.packed_random(p.seed, wb, sb // 2, p.k)
-        t0 = time.perf_counter()
-        c, sc = oracle.quantize_act8(x, p.group)
-        y, _ = oracle.gemv_a8_packed(pw, ps, c, sc, p.n, p.k, p.group, gateup=(layout == "gateup"))
-        if p.kind == "gateup":
-            oracle.silu_gate(y)
-        t_total += time.perf_counter() - t0
+        for th in (1, nt):
+            t0 = time.perf_counter()
+            c, sc = oracle.quantize_act8(x, p.group)
+            if th == 1:
+                y, _ = oracle.gemv_a8_packed(pw, ps, c, sc, p.n, p.k, p.group, gateup=gateup)
+            else:
+                ys = _pool_map(lambda r: oracle.gemv_a8_packed(pw, ps, c, sc, p.n, p.k, p.group, gateup=gateup,
+                                                               rows=r)[0], _row_ranges(p.n, th), th)
+                y = np.concatenate(ys)
+            if gateup:
+                oracle.silu_gate(y)
+            t[th] += time.perf_counter() - t0
         total += a8_bytes(p.kind, p.n, p.k, p.group) + quant_bytes(p.k, p.group)
     return {
-        "value": total / t_total / 1e9,
+        "value": total / t[nt] / 1e9,
         "unit": "GB/s",
-        "cores": 1,
+        "cores": nt,
         "kind": "oracle",
         "sample": f"layer 0 of the W4A8 sweep (quantize + qkv, o_proj, gate/up+silu, down), all rows, {total} "
-                  f"algorithmic bytes in {t_total:.1f} s, single-threaded fp64 C",
-        "seconds": t_total,
+                  f"algorithmic bytes in {t[nt]:.2f} s on {nt} threads (rows split across a thread pool; fp64 C "
+                  f"oracle)",
+        "seconds": t[nt],
+        "single_thread": {"value": total / t[1] / 1e9, "unit": "GB/s", "cores": 1, "seconds": round(t[1], 3)},
+        "host": host,
     }
 
 
