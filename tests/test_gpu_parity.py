@@ -121,7 +121,12 @@ def test_onehot_nibbles_exact_tiny():
     assert np.array_equal(rec, q.astype(np.float64))
 
 
-@pytest.mark.parametrize("n,k,group", [(3584, 18944, 128), (4608, 3584, 128)])
+# the down and QKV shapes (5 and 2 k iterations per wave), and shapes whose
+# waves take 8 iterations at G = 256 and 1 iteration at G = 512: with groups
+# of 128 inputs or more a wave loads each tile's scale words once and hands
+# each 16-lane row its word, which random scales and one-hot x pin exactly
+@pytest.mark.parametrize("n,k,group", [(3584, 18944, 128), (4608, 3584, 128), (40, 32768, 256),
+                                       (48, 2048, 512)])
 def test_onehot_nibbles_exact_big(n, k, group):
     w4 = _w4()
     q, s_rand, _ = synthetic.logical(31, n, k, group)
