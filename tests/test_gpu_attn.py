@@ -118,11 +118,13 @@ def test_attn_shapes(n_heads, n_kv, page, max_ctx, ctx):
     check(d.run(ctx), q, kc, vc, table, ctx, n_kv, page)
 
 
-@pytest.mark.parametrize("ctx", [4097, 4160, 4161, 5000])
+@pytest.mark.parametrize("ctx", [1, 100, 4097, 4160, 4161, 5000])
 def test_attn_long_context_combine(ctx):
-    """Contexts past 64 chunks of 64 tokens take the combine's blocked path
-    (the chunk maxima in blocks of 64 lanes): 4097 tokens end one token into
-    the 65th chunk, 4160 and 4161 straddle the 66th, 5000 needs 79 chunks."""
+    """A workspace of more than 64 chunks of 64 tokens (max_ctx 5000) takes the
+    combine's blocked path (the chunk maxima in blocks of 64 lanes), whatever
+    the context: 1 and 100 tokens use one and two chunks of it, 4097 tokens
+    end one token into the 65th chunk, 4160 and 4161 straddle the 66th, 5000
+    needs 79 chunks."""
     q, kc, vc, table = make_cache(11, 8, 2, 16, 5000)
     d = Dev(q, kc, vc, table, 2, 16, 5000)
     check(d.run(ctx), q, kc, vc, table, ctx, 2, 16)
