@@ -78,9 +78,10 @@ W4A8_METRIC = "W4A8 achieved HBM GB/s (% of peak) and ms per 28-layer+lm_head IN
 STEP_METRIC = "batch-1 decode tokens/s and ms per full 28-layer decode step (hipGraph), tokens 512..639"
 ATTN_HEADS, ATTN_KV_HEADS, ATTN_PAGE, ATTN_CTX = 28, 4, 16, 4096
 KERNEL_SRC = os.path.join(ROOT, "int4_weight_only_04_amd", "csrc", "w4_kernels.hip")
-# every file the decode GEMV kernel is compiled from (its math and its launch table)
+# every file the decode GEMV kernels are compiled from (the GEMV's math and its
+# launch table, and lm_head's argmax finalize, whose bytes the lm_head config counts)
 GEMV_SRCS = tuple(os.path.join(ROOT, "int4_weight_only_04_amd", "csrc", f)
-                  for f in ("w4_kernels.hip", "w4_gemv_math.h", "w4_internal.h"))
+                  for f in ("w4_kernels.hip", "w4_argmax.hip", "w4_gemv_math.h", "w4_internal.h"))
 CONFIG_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_configs.json")
 COLD_BYTES = 576 << 20      # per-config working set: past the 256 MB Infinity Cache
 # The pages' own figures (H100, whole decode step, INT4 weights, batch 1): context, not targets.

@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libw4.so")
 
-SOURCES = ["w4_kernels.hip", "w4_persist.hip", "w4_gemm.hip", "w4_attn.hip", "w4_step.hip", "w4_act8.hip", "w4_probe.hip", "w4_api.cpp",
+SOURCES = ["w4_kernels.hip", "w4_argmax.hip", "w4_persist.hip", "w4_gemm.hip", "w4_attn.hip", "w4_step.hip", "w4_act8.hip", "w4_probe.hip", "w4_api.cpp",
            "w4_step_api.cpp", "w4_pack.cpp"]
 ARCH = "gfx950"
 

@@ -187,7 +187,6 @@ hipError_t launch_rope_append(const RopeCall& call, hipStream_t stream);
 // table[p * 64 + i] = (cos, sin) of p * theta^(-2i/128) for p < max_ctx,
 // evaluated in double and rounded to fp32 (the rotary kernels' arithmetic).
 hipError_t launch_rope_table(double theta, int32_t max_ctx, float2* table, hipStream_t stream);
-hipError_t launch_advance(int32_t* pos, hipStream_t stream);
 
 // Read-only bandwidth probe: streams `bytes` (a multiple of 16, 16-byte
 // aligned) with 16-byte non-temporal loads; sink holds kProbeSinkWords words.
@@ -251,13 +250,15 @@ int persist_threads();
 // the launch sequence of one token: the advance kernel, then the cooperative
 // persistent kernel (the argmax finalize kernels are launched by the caller)
 hipError_t launch_persist(const PersistArgs& args, hipStream_t stream);
-// lowest-index maximum over `count` per-workgroup (value, row) partials
+// lowest-index maximum over `count` per-workgroup (value, row) partials into
+// out[0]; a non-null advance_pos is incremented once the token is written
 hipError_t launch_argmax_finalize(const float* part_v, const int32_t* part_i, int32_t count, int32_t* out,
-                                  hipStream_t stream);
+                                  hipStream_t stream, int32_t* advance_pos = nullptr);
 
 // Launch one GEMV on `stream` (shape already validated by the caller); the
-// argmax epilogue adds a one-workgroup finalize kernel on the same stream.
-hipError_t launch_gemv(const GemvCall& call, hipStream_t stream);
+// argmax epilogue adds a one-workgroup finalize kernel on the same stream,
+// which also advances `advance_pos` when it is not null.
+hipError_t launch_gemv(const GemvCall& call, hipStream_t stream, int32_t* advance_pos = nullptr);
 
 // Workgroups of the main kernel for this call (only n, k, group, epi used).
 int64_t launch_grid(const GemvCall& call);

@@ -39,9 +39,9 @@
 //     warp-specialisation bug, "Technical Details" bullet 4, was a barrier
 //     inside a divergent branch).
 //   * lm_head argmax: each workgroup writes its best (value, row) to the
-//     workspace with plain stores and a one-workgroup second kernel reduces
-//     them in index order.  The kernel boundary orders the two, so there are
-//     no device-scope fences or atomics on the hot path.
+//     workspace with plain stores and a one-workgroup second kernel
+//     (w4_argmax.hip) reduces them.  The kernel boundary orders the two, so
+//     there are no device-scope fences or atomics on the hot path.
 //   * Decode-step forms: the residual epilogue adds y into the fp32 residual
 //     stream and writes one sum of squares of the new rows per unit; the
 //     RMSNorm prologue (x mode kXNorm) takes h, gamma and those sums instead
@@ -529,62 +529,6 @@ __global__ void __launch_bounds__(waves_for(SPLIT) * 64) gemv_w4_kernel(KernelAr
     }
 }
 
-constexpr int kFinalThreads = 1024;
-constexpr int kFinalUnroll = 24;  // partials per thread per load round
-
-// Lowest-index maximum over the per-workgroup partials.  Every thread issues
-// its loads for a round before comparing (one memory round trip for up to
-// 24576 partials); the comparison is order-independent because ties go to
-// the lower row.
-__global__ void __launch_bounds__(kFinalThreads)
-argmax_finalize_kernel(const float* __restrict__ part_v, const int32_t* __restrict__ part_i, int32_t count,
-                       int32_t* __restrict__ out)
-{
-    __shared__ float sv[kFinalThreads / 64];
-    __shared__ int32_t si[kFinalThreads / 64];
-    const int tid = threadIdx.x;
-    float bv = -__builtin_inff();
-    int32_t bi = INT32_MAX;
-    for (int b0 = tid; b0 < count; b0 += kFinalThreads * kFinalUnroll) {
-        float v[kFinalUnroll];
-        int32_t ix[kFinalUnroll];
-#pragma unroll
-        for (int u = 0; u < kFinalUnroll; ++u) {
-            const int b = b0 + u * kFinalThreads;
-            v[u] = b < count ? part_v[b] : -__builtin_inff();
-            ix[u] = b < count ? part_i[b] : INT32_MAX;
-        }
-#pragma unroll
-        for (int u = 0; u < kFinalUnroll; ++u)
-            if (better(v[u], ix[u], bv, bi)) {
-                bv = v[u];
-                bi = ix[u];
-            }
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        const float ov = __shfl_xor(bv, off);
-        const int32_t oi = __shfl_xor(bi, off);
-        if (better(ov, oi, bv, bi)) {
-            bv = ov;
-            bi = oi;
-        }
-    }
-    if ((tid & 63) == 0) {
-        sv[tid >> 6] = bv;
-        si[tid >> 6] = bi;
-    }
-    __syncthreads();
-    if (tid == 0) {
-        for (int w = 1; w < kFinalThreads / 64; ++w)
-            if (better(sv[w], si[w], bv, bi)) {
-                bv = sv[w];
-                bi = si[w];
-            }
-        out[0] = (bi == INT32_MAX) ? -1 : bi;
-    }
-}
-
 // ----------------------------------------------------------------- launch table
 
 // Instantiated (split, depth) pairs: depth is the number of k iterations a
@@ -720,14 +664,6 @@ int64_t launch_grid(const GemvCall& c)
     return make_plan(c).grid;
 }
 
-hipError_t launch_argmax_finalize(const float* part_v, const int32_t* part_i, int32_t count, int32_t* out,
-                                  hipStream_t stream)
-{
-    void* fargs[] = {&part_v, &part_i, &count, &out};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&argmax_finalize_kernel), dim3(1), dim3(kFinalThreads),
-                           fargs, 0, stream);
-}
-
 int64_t residual_parts(int64_t n, int64_t k, int32_t group)
 {
     GemvCall c{};
@@ -738,7 +674,7 @@ int64_t residual_parts(int64_t n, int64_t k, int32_t group)
     return make_plan(c).args.units;
 }
 
-hipError_t launch_gemv(const GemvCall& c, hipStream_t stream)
+hipError_t launch_gemv(const GemvCall& c, hipStream_t stream, int32_t* advance_pos)
 {
     Plan p = make_plan(c);
     if (!p.fn) return hipErrorInvalidValue;
@@ -746,13 +682,7 @@ hipError_t launch_gemv(const GemvCall& c, hipStream_t stream)
     void* args[] = {&p.args};
     hipError_t err = hipLaunchKernel(p.fn, dim3((unsigned)p.grid), dim3(p.threads), args, 0, stream);
     if (err != hipSuccess || c.epi != kEpiArgmax) return err;
-    const float* pv = p.args.part_v;
-    const int32_t* pi = p.args.part_i;
-    int32_t count = (int32_t)p.grid;
-    int32_t* out = c.argmax;
-    void* fargs[] = {&pv, &pi, &count, &out};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&argmax_finalize_kernel), dim3(1), dim3(kFinalThreads),
-                           fargs, 0, stream);
+    return launch_argmax_finalize(p.args.part_v, p.args.part_i, (int32_t)p.grid, c.argmax, stream, advance_pos);
 }
 
 }  // namespace w4i

@@ -1,6 +1,7 @@
 // Glue kernels of a full decode step around the INT4 projections and the
-// paged attention: embedding lookup, residual add + RMSNorm, rotary embedding
-// with the KV-cache append, and the position advance.  The pages' runtime is
+// paged attention: embedding lookup, residual add + RMSNorm, and the rotary
+// embedding with the KV-cache append (the position advance runs in the
+// lm_head argmax's finalize kernel).  The pages' runtime is
 // a Qwen2.5-Coder-7B decoding stack ("How To Build Your Own LLM Runtime From
 // Scratch", aitrending.vip, TL;DR and "Technical Details"); its glue is read
 // as the Qwen2-family pre-norm decoder:
@@ -10,7 +11,7 @@
 //   then x = rmsnorm(h) g_f and the next token is argmax(x Wlm).
 //
 // The token id, the position and the attention's context length live in
-// device memory and are advanced by these kernels, so one captured graph of
+// device memory and are advanced on the device, so one captured graph of
 // the whole step replays token after token with no host work in between.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -279,11 +280,6 @@ __global__ void __launch_bounds__(256) rope_table_kernel(double theta, int32_t m
     table[k] = make_float2((float)cs, (float)sn);
 }
 
-__global__ void __launch_bounds__(64) advance_kernel(int32_t* pos)
-{
-    if (threadIdx.x == 0) *pos = *pos + 1;
-}
-
 }  // namespace
 
 hipError_t launch_embed(const uint16_t* table, int64_t vocab, int64_t hidden, const int32_t* token, float* h,
@@ -333,12 +329,6 @@ hipError_t launch_rope_table(double theta, int32_t max_ctx, float2* table, hipSt
 {
     const int64_t n = (int64_t)max_ctx * 64;
     hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, theta, max_ctx, table);
-    return hipGetLastError();
-}
-
-hipError_t launch_advance(int32_t* pos, hipStream_t stream)
-{
-    hipLaunchKernelGGL(advance_kernel, dim3(1), dim3(64), 0, stream, pos);
     return hipGetLastError();
 }
 

@@ -389,9 +389,9 @@ w4_status w4_decode_step_create(const w4_step_desc* desc, int32_t use_graph, w4_
             copy(l + 1, W4_TRACE_H_IN, h, "trace h");
             if (!next_normed) copy(l + 1, W4_TRACE_X1, x, "trace x1");
         }
-        s.ops.push_back({[=](hipStream_t st_) { return launch_gemv(lm, st_); }, 2, "lm_head + argmax"});
+        // the argmax finalize also advances the position
         int32_t* pos = d.pos;
-        s.ops.push_back({[=](hipStream_t st_) { return launch_advance(pos, st_); }, 1, "advance"});
+        s.ops.push_back({[=](hipStream_t st_) { return launch_gemv(lm, st_, pos); }, 2, "lm_head + argmax + advance"});
 
         if (s.use_graph) {
             hipStream_t cap = nullptr;

@@ -284,6 +284,44 @@ def test_argmax_planted_and_ties():
     assert idx == 0 and np.all(y == y[0])
 
 
+def _argmax_grid(n, k, group):
+    """Number of per-workgroup partials the finalize reduces, recovered from the
+    workspace size (partial values, a 256-byte aligned offset, partial rows)."""
+    wsb = _w4().gemv_workspace_size(n, k, group, True)
+    for g in range(max(1, wsb // 8 - 64), wsb // 8 + 64):
+        if ((4 * g + 255) // 256) * 256 + 4 * g == wsb:
+            return g
+    raise AssertionError(f"no grid gives a workspace of {wsb} bytes")
+
+
+# (n rows at k = 64): partial counts of every residue mod 4, so the finalize's
+# scalar tail loads and its 16-byte loads both carry the winner, and 1.05M rows
+# for more partials than one load round of the finalize covers
+@pytest.mark.parametrize("n", [4112, 4128, 4144, 4160, 1_050_000])
+def test_argmax_finalize_tails_and_rounds(n):
+    k, group = 64, 64
+    grid = _argmax_grid(n, k, group)
+    print(f"[argmax] n={n} partials={grid}", flush=True)
+    q, s, x = synthetic.logical(900 + n % 97, n, k, group)
+    xs = half_bits(np.abs(x.view(np.float16)))
+    top = s.max()
+    cases = []
+    for rows in ([n - 1], [1], [n // 2], [n - 1, n - 2], [n - 3, 7]):
+        qq, ss = q.copy(), s.copy()
+        for r in rows:
+            qq[r] = 15
+            ss[r] = top
+        cases.append((rows, qq, ss))
+    for rows, qq, ss in cases:
+        y, idx, _ = run_plain(qq, ss, xs, group, argmax=True)
+        # the setup makes the planted rows the maxima of the GPU's own logits
+        # (identical rows give bit-identical sums), so the lowest one must win
+        assert np.all(y[rows] == y.max()), rows
+        assert idx == min(rows) == oracle.argmax(y), (rows, idx)
+    if n > 1_000_000:
+        assert grid > 24576
+
+
 def test_argmax_workspace_reuse():
     """The workspace needs no initial contents: starting from garbage, repeated
     calls agree bit for bit."""

@@ -337,9 +337,10 @@ def test_step_teacher_forced_small(use_graph):
     # 7 kernels per layer (qkv with the attention norm folded in from layer 1
     # on, rotary + append + attention x2, o_proj, residual add + MLP norm,
     # gate/up, down with the residual add) + embedding with the first norm, the
-    # last down's residual add + final norm, lm_head (2) and advance; the trace
-    # adds 10 copies per layer and 2 for the first record
-    assert st.launches() == 7 * 3 + 5 + 10 * 3 + 2
+    # last down's residual add + final norm, and lm_head (2: the GEMV, then
+    # the argmax finalize, which also advances the position); the trace adds
+    # 10 copies per layer and 2 for the first record
+    assert st.launches() == 7 * 3 + 4 + 10 * 3 + 2
     model.token.fill_(5)
     model.pos.fill_(37)
     torch.cuda.synchronize()
@@ -421,7 +422,7 @@ def test_step_separate_norms_above_4096():
     cfg = dict(hidden=4224, n_heads=33, n_kv=11, inter=256, vocab=500, group=64, layers=2, page=16, max_ctx=64)
     model = Model(88, bias=True, **cfg)
     st = model.step(True)
-    assert st.launches() == 8 * 2 + 4 + 10 * 2 + 2
+    assert st.launches() == 8 * 2 + 3 + 10 * 2 + 2
     model.token.fill_(7)
     model.pos.fill_(30)
     torch.cuda.synchronize()
