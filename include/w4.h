@@ -258,7 +258,7 @@ w4_status w4_gemv_gateup_silu_a8(const void* packed_w, const void* packed_s, con
 
 /*
  * Workspace bytes w4_attn_decode needs: (130 x 4) bytes per query head per
- * 64-token chunk of max_ctx (about 0.9 MB for 28 heads at 4096).  Host only.
+ * 128-token chunk of max_ctx (about 0.47 MB for 28 heads at 4096).  Host only.
  */
 w4_status w4_attn_decode_workspace_size(int32_t n_heads, int32_t max_ctx, size_t* bytes);
 

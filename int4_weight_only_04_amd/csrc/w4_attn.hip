@@ -8,10 +8,10 @@
 // Token t sits in physical page page_table[t / page] at slot t % page; the
 // caches are fp16 [num_pages][n_kv][page][128].
 //
-// Two kernels.  The first splits the context into chunks of 64 tokens; a
-// workgroup takes one chunk of one KV head, so K and V are read once for all
-// the query heads that share them, and writes the chunk's softmax max, sum
-// and unnormalised fp32 output.  The second merges the chunks in chunk order
+// Two kernels.  The first splits the context into chunks of 128 tokens; a
+// workgroup of 8 waves takes one chunk of one KV head, so K and V are read
+// once for all the query heads that share them, and writes the chunk's
+// softmax max, sum and unnormalised fp32 output.  The second merges the chunks in chunk order
 // (deterministic).  The context length is read from device memory, so a
 // captured graph replays unchanged from token to token; the grid is sized for
 // max_ctx, and a chunk past the context exits before reading the cache (the
@@ -29,8 +29,9 @@ namespace w4i {
 namespace {
 
 constexpr int kDim = 128;          // head dimension
-constexpr int kChunk = 64;         // tokens per workgroup
-constexpr int kAttnThreads = 256;  // 4 waves
+constexpr int kChunk = 128;        // tokens per workgroup
+constexpr int kAttnThreads = 512;  // 8 waves
+constexpr int kWaves = kAttnThreads / 64;
 
 struct AttnArgs {
     const uint4* q;          // fp16 [n_heads][128], 16 per head (not used with the fused rotary embedding)
@@ -223,7 +224,7 @@ __device__ __forceinline__ uint32_t pack_half2(float lo, float hi)
 //   * V is staged in LDS (each wave its own 16 rows, masked tokens as zeros,
 //     padded rows so the four row groups fall in different banks), and
 //     lane (r, c) reads tokens 4r .. 4r + 3 of dimension 16 n + c for tile n.
-// The four waves' parts are merged once, rescaled to the chunk maximum.
+// The eight waves' parts are merged once, rescaled to the chunk maximum.
 // ROPE: the query heads and the new token's key are rotated here from the
 // QKV projection (fp16-rounded, as the stored q and cache are), and the new
 // token's k and v are appended to the cache by the workgroup whose chunk
@@ -233,10 +234,10 @@ template <int GQ, bool ROPE>
 __global__ void __launch_bounds__(kAttnThreads) attn_partial_kernel(AttnArgs a)
 {
     constexpr int kVRow = kDim / 2 + 2;  // LDS words per staged V row (2 words of padding)
-    __shared__ uint32_t s_v[4][16][kVRow];
-    __shared__ float s_o[4][GQ][kDim];
-    __shared__ float s_m[4][GQ];     // per wave: its 16 tokens' maximum and sum of weights, per head
-    __shared__ float s_l[4][GQ];
+    __shared__ uint32_t s_v[kWaves][16][kVRow];
+    __shared__ float s_o[kWaves][GQ][kDim];
+    __shared__ float s_m[kWaves][GQ];     // per wave: its 16 tokens' maximum and sum of weights, per head
+    __shared__ float s_l[kWaves][GQ];
     __shared__ float s_q[ROPE ? GQ : 1][kDim];
     __shared__ float s_knew[ROPE ? kDim : 1];
     __shared__ uint32_t s_vnew[ROPE ? kDim / 2 : 1];
@@ -306,10 +307,10 @@ __global__ void __launch_bounds__(kAttnThreads) attn_partial_kernel(AttnArgs a)
     for (int j = 0; j < 16; ++j) vv[j] = a.vc[vrow[j] * (kDim / 2) + lane];
     const bool has_new = ROPE && pos >= t0 && pos < t0 + kChunk;  // uniform per workgroup
     if constexpr (ROPE) {
-        // rotate this workgroup's query heads (GQ x 64 pairs over 256
+        // rotate this workgroup's query heads (GQ x 64 pairs over 512
         // threads) and, in the workgroup holding the new token, its k and v
         if (t0 < ctx) {
-            // at most two pairs per thread (GQ <= 8): every load first, then the math
+            // at most one pair per thread (GQ <= 8): every load first, then the math
             constexpr int kPairs = (GQ * 64 + kAttnThreads - 1) / kAttnThreads;
             float x0[kPairs], x1[kPairs];
             float2 cs[kPairs];
@@ -458,23 +459,27 @@ __global__ void __launch_bounds__(kAttnThreads) attn_partial_kernel(AttnArgs a)
     }
     __syncthreads();
 
-    // ---- the chunk's partial: the four waves' parts rescaled to the chunk
+    // ---- the chunk's partial: the eight waves' parts rescaled to the chunk
     // maximum (finite: the chunk's first token is inside the context) and
     // added in wave order; a wave without a token in the context has maximum
     // -inf, weight 0 and sum 0
     for (int i = tid; i < GQ * kDim; i += kAttnThreads) {
         const int h = i / kDim, d = i % kDim;
-        const float mm = fmaxf(fmaxf(s_m[0][h], s_m[1][h]), fmaxf(s_m[2][h], s_m[3][h]));
+        float mm = s_m[0][h];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) mm = fmaxf(mm, s_m[w][h]);
         float o = 0.0f;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) o = __builtin_fmaf(__expf(s_m[w][h] - mm), s_o[w][h][d], o);
+        for (int w = 0; w < kWaves; ++w) o = __builtin_fmaf(__expf(s_m[w][h] - mm), s_o[w][h][d], o);
         po[i] = o;
     }
     if (tid < GQ) {
-        const float mm = fmaxf(fmaxf(s_m[0][tid], s_m[1][tid]), fmaxf(s_m[2][tid], s_m[3][tid]));
+        float mm = s_m[0][tid];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) mm = fmaxf(mm, s_m[w][tid]);
         float ls = 0.0f;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) ls = __builtin_fmaf(__expf(s_m[w][tid] - mm), s_l[w][tid], ls);
+        for (int w = 0; w < kWaves; ++w) ls = __builtin_fmaf(__expf(s_m[w][tid] - mm), s_l[w][tid], ls);
         pml[2 * tid] = mm;
         pml[2 * tid + 1] = ls;
     }
@@ -487,6 +492,40 @@ __global__ void __launch_bounds__(kAttnThreads) attn_partial_kernel(AttnArgs a)
 // chunk weights come from lane c by a lane read, and the four chunk lanes'
 // sums meet once in LDS, added in a fixed order.
 constexpr int kCombThreads = 512;
+
+// The combine for workspaces of at most 4 NL chunks: every load in one
+// round, with addresses that do not depend on the context length, so they
+// travel together with its load: the lane's chunk (max, sum) and this
+// thread's NL partials (chunks j, j + 4, ...).  Chunks past the context hold
+// whatever an earlier call left there; they are only ever selected away,
+// never multiplied.
+template <int NL>
+__device__ __forceinline__ void one_round(const AttnArgs& a, int h, int lane, int j, int cap, const float2* ml,
+                                          const float* po, int64_t ostride, float& o, float& l)
+{
+    const int c = lane < cap ? lane : cap - 1;
+    const float2 mc = ml[(int64_t)c * a.n_heads + h];
+    float ov[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+        const int cc = j + 4 * i;
+        ov[i] = po[(int64_t)(cc < cap ? cc : cap - 1) * ostride];
+    }
+    // only now wait for the context length
+    __builtin_amdgcn_sched_barrier(0);
+    const int nch = (clamp_ctx(a) + kChunk - 1) / kChunk;   // 1 .. cap
+    const float m = wave_max(lane < nch ? mc.x : -__builtin_inff());
+    const float f = lane < nch ? __expf(mc.x - m) : 0.0f;
+    l = wave_sum(f * (lane < nch ? mc.y : 0.0f));
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+        const int cc = j + 4 * i;
+        if (cc < nch) {
+            const float fi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), cc));
+            o = __builtin_fmaf(fi, ov[i], o);
+        }
+    }
+}
 
 __global__ void __launch_bounds__(kCombThreads) attn_combine_kernel(AttnArgs a)
 {
@@ -501,34 +540,10 @@ __global__ void __launch_bounds__(kCombThreads) attn_combine_kernel(AttnArgs a)
     const float* po = a.part_o + (int64_t)h * kDim + d;
     const int64_t ostride = (int64_t)a.n_heads * kDim;
     float o = 0.0f, l;
-    if (cap <= 64) {
-        // every load in one round, with addresses that do not depend on the
-        // context length, so they travel together with its load: the lane's
-        // chunk (max, sum) and this thread's 16 partials.  Chunks past the
-        // context hold whatever an earlier call left there; they are only
-        // ever selected away below, never multiplied.
-        const int c = lane < cap ? lane : cap - 1;
-        const float2 mc = ml[(int64_t)c * a.n_heads + h];
-        float ov[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int cc = j + 4 * i;
-            ov[i] = po[(int64_t)(cc < cap ? cc : cap - 1) * ostride];
-        }
-        // only now wait for the context length
-        __builtin_amdgcn_sched_barrier(0);
-        const int nch = (clamp_ctx(a) + kChunk - 1) / kChunk;   // 1 .. cap
-        const float m = wave_max(lane < nch ? mc.x : -__builtin_inff());
-        const float f = lane < nch ? __expf(mc.x - m) : 0.0f;
-        l = wave_sum(f * (lane < nch ? mc.y : 0.0f));
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int cc = j + 4 * i;
-            if (cc < nch) {
-                const float fi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), cc));
-                o = __builtin_fmaf(fi, ov[i], o);
-            }
-        }
+    if (cap <= 32) {
+        one_round<8>(a, h, lane, j, cap, ml, po, ostride, o, l);
+    } else if (cap <= 64) {
+        one_round<16>(a, h, lane, j, cap, ml, po, ostride, o, l);
     } else {
         // longer contexts: the maximum over all chunks first, then blocks of 64
         const int nch = (clamp_ctx(a) + kChunk - 1) / kChunk;

@@ -226,7 +226,10 @@ def test_attn_validation_before_launch():
     need = w4.attn_decode_workspace_size(28, 64)
     assert need == 28 * 130 * 4
     assert call(wsb=need - 1) == w4.EINVAL
-    assert w4.attn_decode_workspace_size(28, 4096) == 64 * 28 * 130 * 4
+    # one (128 partial outputs, max, sum) record per query head and 128-token chunk
+    assert w4.attn_decode_workspace_size(28, 128) == 28 * 130 * 4
+    assert w4.attn_decode_workspace_size(28, 129) == 2 * 28 * 130 * 4
+    assert w4.attn_decode_workspace_size(28, 4096) == 32 * 28 * 130 * 4
 
 
 def test_sweep_create_validation():

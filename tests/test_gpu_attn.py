@@ -91,7 +91,7 @@ def check(o, q, kc, vc, table, ctx, n_kv, page):
     assert np.all(err <= tol), (ctx, float((err / tol).max()))
 
 
-CTXS = [1, 2, 15, 16, 17, 63, 64, 65, 100, 255, 256, 257, 1000, 4095, 4096]
+CTXS = [1, 2, 15, 16, 17, 63, 64, 65, 100, 127, 128, 129, 255, 256, 257, 1000, 4095, 4096]
 
 
 def test_attn_qwen_shape_page_tails():
@@ -118,16 +118,30 @@ def test_attn_shapes(n_heads, n_kv, page, max_ctx, ctx):
     check(d.run(ctx), q, kc, vc, table, ctx, n_kv, page)
 
 
-@pytest.mark.parametrize("ctx", [1, 100, 4097, 4160, 4161, 5000])
+@pytest.mark.parametrize("ctx", [1, 200, 8193, 8320, 8321, 9000])
 def test_attn_long_context_combine(ctx):
-    """A workspace of more than 64 chunks of 64 tokens (max_ctx 5000) takes the
+    """A workspace of more than 64 chunks of 128 tokens (max_ctx 9000) takes the
     combine's blocked path (the chunk maxima in blocks of 64 lanes), whatever
-    the context: 1 and 100 tokens use one and two chunks of it, 4097 tokens
-    end one token into the 65th chunk, 4160 and 4161 straddle the 66th, 5000
-    needs 79 chunks."""
-    q, kc, vc, table = make_cache(11, 8, 2, 16, 5000)
-    d = Dev(q, kc, vc, table, 2, 16, 5000)
+    the context: 1 and 200 tokens use one and two chunks of it, 8193 tokens
+    end one token into the 65th chunk, 8320 and 8321 straddle the 66th, 9000
+    needs 71 chunks."""
+    q, kc, vc, table = make_cache(11, 8, 2, 16, 9000)
+    d = Dev(q, kc, vc, table, 2, 16, 9000)
     check(d.run(ctx), q, kc, vc, table, ctx, 2, 16)
+
+
+@pytest.mark.parametrize("max_ctx,ctx", [(4096, 4096), (4096, 2049), (2000, 1999)])
+def test_attn_combine_one_round_widths(max_ctx, ctx):
+    """The combine's one-round path loads 8 partials per thread for at most 32
+    chunks (max_ctx <= 4096) and 16 for 33..64 chunks (max_ctx 8192, the same
+    contexts); 1999 tokens use 16 chunks, the last one ragged."""
+    q, kc, vc, table = make_cache(12 + ctx, 8, 2, 16, max_ctx)
+    d = Dev(q, kc, vc, table, 2, 16, max_ctx)
+    check(d.run(ctx), q, kc, vc, table, ctx, 2, 16)
+    if max_ctx == 4096:
+        q2, kc2, vc2, table2 = make_cache(13, 8, 2, 16, 8192)
+        d2 = Dev(q2, kc2, vc2, table2, 2, 16, 8192)
+        check(d2.run(ctx), q2, kc2, vc2, table2, ctx, 2, 16)
 
 
 def test_attn_context_clamped():

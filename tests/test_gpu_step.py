@@ -393,8 +393,9 @@ def test_step_first_position():
 @pytest.mark.parametrize("n_heads,n_kv,page,max_ctx,start", [
     (2, 2, 1, 40, 37),      # one query head per KV head, one token per page
     (8, 2, 64, 100, 97),    # the last chunk's reads past max_ctx are clamped onto the slot being appended
-    (6, 3, 16, 70, 63),     # steps across a chunk boundary (63 -> 64) into the ragged last chunk
-    (4, 1, 8, 129, 126),    # four query heads on one KV head; the new token ends at max_ctx - 1 = 128
+    (6, 3, 16, 70, 63),     # steps across a wave boundary inside the chunk (63 -> 64)
+    (4, 1, 8, 129, 126),    # four query heads on one KV head; steps across the chunk boundary (127 -> 128)
+                            # into a last chunk of one token, ending at max_ctx - 1 = 128
 ])
 def test_step_fused_attention_edges(n_heads, n_kv, page, max_ctx, start):
     """The rotary + KV append fused into attention at the cache's edges:
