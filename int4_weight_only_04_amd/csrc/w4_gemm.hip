@@ -311,16 +311,44 @@ __global__ void __launch_bounds__(kThreads, NBUF == 2 ? 2 : 3) gemm_w4_kernel(Ge
     }
 }
 
-// y = sum of the split partials, in split order (deterministic).
-__global__ void __launch_bounds__(256) gemm_reduce_kernel(const float* __restrict__ part, float* __restrict__ y,
-                                                          int64_t count, int32_t splits)
+// y = sum of the split partials, in split order (deterministic).  A thread
+// owns E elements, 256 apart so that every load instruction of a wave reads
+// 256 consecutive floats, and issues all E x S loads before adding: one
+// memory round trip per thread instead of one per element and split.
+constexpr int kReduceThreads = 256;
+
+template <int S, int E>
+__global__ void __launch_bounds__(kReduceThreads) gemm_reduce_kernel(const float* __restrict__ part,
+                                                                     float* __restrict__ y, int64_t count)
 {
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride) {
-        float t = part[i];
-        for (int s = 1; s < splits; ++s) t += part[(int64_t)s * count + i];
-        y[i] = t;
+    const int64_t base = (int64_t)blockIdx.x * (kReduceThreads * E) + threadIdx.x;
+    float v[E][S];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int64_t i = base + e * kReduceThreads;
+        const int64_t ic = i < count ? i : count - 1;   // in bounds; the sum is not stored
+#pragma unroll
+        for (int sp = 0; sp < S; ++sp) v[e][sp] = part[(int64_t)sp * count + ic];
     }
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int64_t i = base + e * kReduceThreads;
+        float t = v[e][0];
+#pragma unroll
+        for (int sp = 1; sp < S; ++sp) t += v[e][sp];
+        if (i < count) y[i] = t;
+    }
+}
+
+template <int S>
+hipError_t launch_reduce(const float* part, float* y, int64_t count, hipStream_t stream)
+{
+    constexpr int E = S <= 4 ? 8 : 4;   // at most 32 loads in flight per thread
+    const int64_t blocks = (count + kReduceThreads * E - 1) / (kReduceThreads * E);
+    if (blocks < 1 || blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    void* rargs[] = {&part, &y, &count};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_reduce_kernel<S, E>), dim3((unsigned)blocks),
+                           dim3(kReduceThreads), rargs, 0, stream);
 }
 
 struct GemmPlan {
@@ -375,13 +403,17 @@ hipError_t launch_gemm(const GemmCall& c, hipStream_t stream)
     if (err != hipSuccess || p.args.splits == 1) return err;
     const float* part = static_cast<const float*>(c.ws);
     float* y = static_cast<float*>(c.out);
-    int64_t count = c.m * c.n;
-    int32_t splits = p.args.splits;
-    void* rargs[] = {&part, &y, &count, &splits};
-    int64_t blocks = (count + 255) / 256;
-    if (blocks > 2048) blocks = 2048;
-    return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_reduce_kernel), dim3((unsigned)blocks), dim3(256),
-                           rargs, 0, stream);
+    const int64_t count = c.m * c.n;
+    switch (p.args.splits) {
+        case 2: return launch_reduce<2>(part, y, count, stream);
+        case 3: return launch_reduce<3>(part, y, count, stream);
+        case 4: return launch_reduce<4>(part, y, count, stream);
+        case 5: return launch_reduce<5>(part, y, count, stream);
+        case 6: return launch_reduce<6>(part, y, count, stream);
+        case 7: return launch_reduce<7>(part, y, count, stream);
+        case 8: return launch_reduce<8>(part, y, count, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace w4i
